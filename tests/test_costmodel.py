@@ -1,0 +1,87 @@
+"""The cost model reproduces every cache/work figure the concept page prints."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from sparse_attention_12_amd import costmodel as cm
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_arithmetic.json")))
+FIG = {f["name"]: f for f in GOLD["figures"]}
+
+
+def _value(name):
+    L = 1 << 20
+    return {
+        "layers": cm.LAYERS,
+        "indexer_layers": cm.indexer_layers(),
+        "owning_rope_layers": sum(cm.kv_source(l) == l and cm.is_rope_layer(l) for l in range(cm.LAYERS)),
+        "owning_nope_layers": sum(cm.kv_source(l) == l and not cm.is_rope_layer(l) for l in range(cm.LAYERS)),
+        "cached_values_per_position": cm.cached_values_per_position(),
+        "values_saved_by_cache_sharing": cm.values_saved_by_cache_sharing(),
+        "full_kv_values_per_position": cm.full_kv_values_per_position(),
+        "full_over_latent": cm.full_kv_values_per_position() / cm.cached_values_per_position(),
+        "latent_cache_GB_bf16_at_2^20": cm.latent_cache_bytes(L) / 1e9,
+        "score_macs_one_layer": cm.SCORE_MACS,
+        "attend_macs_one_rope_layer": cm.ATTEND_MACS,
+        "attend_macs_model": cm.attend_macs_per_position(),
+        "score_macs_model": cm.score_macs_per_position(),
+        "indexer_crossover_tokens": cm.indexer_crossover_tokens(),
+        "sparse_gain_at_2^20": cm.sparse_gain(L),
+        "sparse_gain_at_8K": cm.sparse_gain(8192),
+        "sparse_gain_at_128K": cm.sparse_gain(131072),
+        "short_prompt_overhead_percent": 100 * cm.short_prompt_overhead(),
+        "selection_reuse_saving_percent": 100 * cm.selection_reuse_saving(),
+        "fp8_indexer_keys_GB_at_2^20": cm.fp8_indexer_key_bytes(L) / 1e9,
+        "indexer_share_percent_at_2^20": 100 * cm.indexer_share(L),
+        "prefill_scoring_macs_at_2^20": cm.prefill_scoring_macs(L),
+    }[name]
+
+
+@pytest.mark.parametrize("name", sorted(FIG))
+def test_printed_figure(name):
+    f = FIG[name]
+    got, want, r = _value(name), f["value"], f["rounding"]
+    if r == "exact":
+        assert got == want
+    elif r == "nearest integer" or r == "nearest integer percent":
+        assert round(got) == want, got
+    elif r == "0.1":
+        assert round(got, 1) == want, got
+    elif r == "3 significant digits":
+        assert float(f"{got:.3g}") == want, got
+    elif r == "nearest thousand":
+        assert round(got, -3) == want, got
+    elif r == "order of magnitude":
+        assert round(math.log10(got)) == math.log10(want), got
+    else:
+        raise AssertionError(r)
+
+
+def test_schedule_shape():
+    # sharing runs are three layers long and start at 16, 20, ..., 68; reusers are RoPE layers
+    reusers = [l for l in range(cm.LAYERS) if not cm.runs_indexer(l)]
+    assert len(reusers) == 28 and reusers[:4] == [17, 18, 21, 22]
+    assert all(cm.is_rope_layer(l) for l in reusers)
+    # every cache-sharing layer and its source are NoPE layers
+    sharers = [l for l in range(cm.LAYERS) if cm.kv_source(l) != l]
+    assert len(sharers) == 9 and not cm.is_rope_layer(35)
+    assert all(not cm.is_rope_layer(l) for l in sharers)
+
+
+def test_path_traffic_units():
+    # one decode query at L = 32,768, bf16: 32,768 x 256 B of keys, 2,048 x 1,152 B of rows
+    t = cm.path_traffic([32768], [0], [32767], "bf16")
+    assert t["indexer"]["key_bytes"] == 32768 * 256
+    assert t["mla_layer"]["row_bytes_unique"] == 2048 * 1152
+    assert t["indexer"]["flop"] == 2 * 4096 * 32768
+    assert t["mla_layer"]["flop"] == 2 * 69632 * 2048
+    # causal prefill: query at position p has p+1 candidates
+    t = cm.path_traffic([65536], np.zeros(2048, int), 63488 + np.arange(2048), "bf16")
+    assert t["indexer"]["positions"] == 132121600
+    assert abs(t["indexer"]["flop"] / 1.082e12 - 1) < 1e-3
+    # short context: every position selected
+    t = cm.path_traffic([1000], [0], [999], "f32")
+    assert t["mla_layer"]["positions"] == 1000

@@ -1,0 +1,294 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle.
+
+Each test ties one oracle function to mathematics or to a figure of the
+"Mistral Large 4" concept page, chosen so that a plausible slip (a dropped
+ReLU, a head/weight index mismatch, a transposed operand, a wrong tie-break,
+a softmax normalised over the wrong set) fails at least one of them.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+HI, DI, H, DC, DR, D = oracle.HI, oracle.DI, oracle.H, oracle.DC, oracle.DR, oracle.D
+TAU = 1.0 / math.sqrt(192.0)
+
+
+def _ints(rng, shape, lo=-3, hi=3):
+    return rng.integers(lo, hi + 1, size=shape).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# indexer score
+# ----------------------------------------------------------------------------
+
+
+def test_dims_match_pages():
+    # 32 indexer heads x 128; 64 MLA heads; 512 latent + 64 rotary = 576 values
+    assert oracle.dims() == (32, 128, 64, 512, 64, 576)
+
+
+def test_indexer_relu_sign_identity():
+    """I(q) - I(-q) = (sum_h w_h q_h) . k  because max(0,x) - max(0,-x) = x.
+
+    The right side is one plain matrix-vector product (numpy), so this pins
+    the weights, the head indexing and the operand orientation; the ReLU is
+    pinned separately below.
+    """
+    rng = np.random.default_rng(1)
+    qI = rng.standard_normal((HI, DI)).astype(np.float32)
+    w = rng.uniform(0.5, 4, HI).astype(np.float32)
+    kI = rng.standard_normal((300, DI)).astype(np.float32)
+    diff = oracle.index_score(qI, w, kI) - oracle.index_score(-qI, w, kI)
+    lin = kI.astype(np.float64) @ (w.astype(np.float64) @ qI.astype(np.float64))
+    np.testing.assert_allclose(diff, lin, rtol=1e-12, atol=1e-9)
+
+
+def test_indexer_rank_one_closed_form():
+    """q_h = a_h e_j, k_s = b_s e_j  =>  I_s = b_s * sum_{h: a_h b_s > 0} w_h a_h."""
+    rng = np.random.default_rng(2)
+    a = rng.integers(-3, 4, HI).astype(np.float64)
+    w = rng.integers(1, 5, HI).astype(np.float64)
+    b = np.arange(-6, 7, dtype=np.float64)
+    j = 17
+    qI = np.zeros((HI, DI), np.float32)
+    qI[:, j] = a
+    kI = np.zeros((b.size, DI), np.float32)
+    kI[:, j] = b
+    got = oracle.index_score(qI, w.astype(np.float32), kI)
+    pos = (w * a)[a > 0].sum()
+    neg = (w * a)[a < 0].sum()
+    expect = np.where(b > 0, b * pos, np.where(b < 0, b * neg, 0.0))
+    np.testing.assert_array_equal(got, expect)
+
+
+def test_indexer_head_permutation_and_homogeneity():
+    rng = np.random.default_rng(3)
+    qI, kI = _ints(rng, (HI, DI)), _ints(rng, (257, DI))
+    w = rng.integers(1, 5, HI).astype(np.float32)
+    base = oracle.index_score(qI, w, kI)
+    perm = rng.permutation(HI)
+    np.testing.assert_array_equal(oracle.index_score(qI[perm], w[perm], kI), base)
+    np.testing.assert_array_equal(oracle.index_score(qI, 2 * w, kI), 2 * base)
+    np.testing.assert_array_equal(oracle.index_score(qI, w, 3 * kI), 3 * base)
+    # a head whose weight is zero contributes nothing
+    w0 = w.copy()
+    w0[5] = 0
+    q5 = qI.copy()
+    q5[5] = rng.integers(-3, 4, DI)
+    np.testing.assert_array_equal(oracle.index_score(q5, w0, kI), oracle.index_score(qI, w0, kI))
+
+
+def test_indexer_integer_inputs_are_exact_and_bounded():
+    rng = np.random.default_rng(4)
+    qI, kI = _ints(rng, (HI, DI)), _ints(rng, (512, DI))
+    w = rng.integers(1, 5, HI).astype(np.float32)
+    s = oracle.index_score(qI, w, kI)
+    assert np.all(s == np.round(s)) and np.all(s >= 0)
+    assert s.max() <= 32 * 4 * 128 * 9 < 2 ** 24
+    # extreme case reaches the bound exactly
+    q3 = np.full((HI, DI), 3, np.float32)
+    k3 = np.full((1, DI), 3, np.float32)
+    assert oracle.index_score(q3, np.full(HI, 4, np.float32), k3)[0] == 147456
+
+
+# ----------------------------------------------------------------------------
+# top-k selection
+# ----------------------------------------------------------------------------
+
+
+def _brute_force_selection(scores, k):
+    """s is kept iff fewer than k positions beat it: (score, -index) larger."""
+    n = len(scores)
+    kept = []
+    for s in range(n):
+        better = 0
+        for t in range(n):
+            if scores[t] > scores[s] or (scores[t] == scores[s] and t < s):
+                better += 1
+        if better < k:
+            kept.append(s)
+    return kept
+
+
+@pytest.mark.parametrize("k", [1, 4, 8, 2048])
+@pytest.mark.parametrize("case", ["random", "ties", "all_equal", "two_levels", "negative_zero"])
+def test_topk_matches_rank_count(k, case):
+    rng = np.random.default_rng(hash((k, case)) % 2 ** 32)
+    n = 64
+    if case == "random":
+        sc = rng.standard_normal(n)
+    elif case == "ties":
+        sc = rng.integers(0, 5, n).astype(np.float64)
+    elif case == "all_equal":
+        sc = np.full(n, 7.0)
+    elif case == "two_levels":
+        sc = np.where(rng.random(n) < 0.1, 3.0, 1.0)
+    else:
+        sc = np.where(rng.random(n) < 0.5, 0.0, -0.0) * 1.0
+        sc[::7] = -1.0
+    idx, m = oracle.topk(sc, k)
+    expect = _brute_force_selection(list(sc), k)
+    assert m == len(expect) == min(k, n)
+    assert list(idx[:m]) == expect
+    assert np.all(idx[m:] == -1) and idx.shape == (k,)
+
+
+def test_topk_all_equal_keeps_lowest_positions():
+    idx, m = oracle.topk(np.zeros(5000), 2048)
+    assert m == 2048 and np.array_equal(idx, np.arange(2048))
+
+
+def test_topk_short_context_keeps_everything():
+    rng = np.random.default_rng(5)
+    idx, m = oracle.topk(rng.standard_normal(100), 2048)
+    assert m == 100 and np.array_equal(idx[:100], np.arange(100)) and np.all(idx[100:] == -1)
+
+
+def test_topk_empty_and_nonfinite():
+    idx, m = oracle.topk(np.zeros(0), 4)
+    assert m == 0 and np.all(idx == -1)
+    with pytest.raises(ValueError):
+        oracle.topk(np.array([1.0, np.nan]), 1)
+
+
+# ----------------------------------------------------------------------------
+# sparse MLA
+# ----------------------------------------------------------------------------
+
+
+def _sdpa(q, kv, tau, mask=None):
+    """torch's library attention on the CPU in float64 (dense, optionally masked)."""
+    Q = torch.from_numpy(q.astype(np.float64))[None]            # [1,64,576] as [B, L=64, E]
+    K = torch.from_numpy(kv.astype(np.float64))[None]
+    V = torch.from_numpy(kv[:, :DC].astype(np.float64))[None]
+    Q = Q.unsqueeze(1)
+    K = K.unsqueeze(1)
+    V = V.unsqueeze(1)
+    am = None if mask is None else torch.from_numpy(mask)[None, None, None, :].expand(1, 1, H, -1)
+    o = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=am, scale=tau)
+    return o[0, 0].numpy()
+
+
+def test_mla_dense_case_equals_library_attention():
+    """A context of at most 2,048 positions is attended in full, so the sparse
+    read equals ordinary dense softmax attention (concept page, When does
+    sparse attention pay?)."""
+    rng = np.random.default_rng(6)
+    n = 700
+    q = rng.standard_normal((H, D)).astype(np.float32)
+    kv = rng.standard_normal((n, D)).astype(np.float32)
+    o, lse = oracle.mla_attend(q, kv, np.arange(n, dtype=np.int32), TAU)
+    np.testing.assert_allclose(o, _sdpa(q, kv, TAU), rtol=1e-10, atol=1e-12)
+    logits = TAU * (q.astype(np.float64) @ kv.astype(np.float64).T)
+    from scipy.special import logsumexp
+    np.testing.assert_allclose(lse, logsumexp(logits, axis=1), rtol=1e-12)
+
+
+def test_mla_normalises_over_selected_set_only():
+    rng = np.random.default_rng(7)
+    n = 500
+    q = rng.standard_normal((H, D)).astype(np.float32)
+    kv = rng.standard_normal((n, D)).astype(np.float32)
+    sel = np.sort(rng.choice(n, 123, replace=False)).astype(np.int32)
+    mask = np.zeros(n, bool)
+    mask[sel] = True
+    o, _ = oracle.mla_attend(q, kv, sel, TAU)
+    np.testing.assert_allclose(o, _sdpa(q, kv, TAU, mask), rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("n,gap", [(2, 0.0), (10, 1.5), (2048, 3.0), (2048, 9.0)])
+def test_mla_single_leader_closed_form(n, gap):
+    """One key ahead of n-1 equal competitors by logit gap D gets weight
+    1/(1+(n-1)e^-D) (concept page, Query scaling)."""
+    rng = np.random.default_rng(8)
+    kv = rng.standard_normal((n, D)).astype(np.float32)
+    kv[:, 0] = 0.0
+    kv[:, DC:] = 0.0
+    lead = n // 3
+    kv[lead, 0] = 1.0
+    q = np.zeros((H, D), np.float32)
+    q[:, 0] = np.float32(gap / TAU)
+    gap_eff = float(np.float32(gap / TAU)) * TAU
+    o, lse = oracle.mla_attend(q, kv, np.arange(n, dtype=np.int32), TAU)
+    p = 1.0 / (1.0 + (n - 1) * math.exp(-gap_eff))
+    others = np.delete(kv[:, :DC].astype(np.float64), lead, axis=0).mean(axis=0)
+    expect = p * kv[lead, :DC].astype(np.float64) + (1 - p) * others
+    np.testing.assert_allclose(o, np.broadcast_to(expect, (H, DC)), rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(lse, math.log(math.exp(gap_eff) + n - 1), rtol=1e-12)
+
+
+def test_mla_zero_query_is_mean_and_order_free():
+    rng = np.random.default_rng(9)
+    kv = rng.standard_normal((300, D)).astype(np.float32)
+    sel = rng.choice(300, 77, replace=False).astype(np.int32)
+    o, lse = oracle.mla_attend(np.zeros((H, D), np.float32), kv, sel, TAU)
+    np.testing.assert_allclose(o, np.broadcast_to(kv[sel, :DC].astype(np.float64).mean(0), (H, DC)),
+                               rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, math.log(77), rtol=1e-13)
+    q = rng.standard_normal((H, D)).astype(np.float32)
+    o1, l1 = oracle.mla_attend(q, kv, sel, TAU)
+    padded = np.concatenate([sel[::-1], np.full(9, -1, np.int32)])
+    o2, l2 = oracle.mla_attend(q, kv, padded, TAU)
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(l1, l2, rtol=1e-14)
+
+
+def test_mla_empty_selection():
+    o, lse = oracle.mla_attend(np.ones((H, D), np.float32), np.ones((4, D), np.float32),
+                               np.full(3, -1, np.int32), TAU)
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+
+
+def test_rotary_part_enters_logit_but_not_value():
+    """Changing only the 64 rotary values of a row changes the weights, never
+    the value vectors (value = 512-wide latent)."""
+    rng = np.random.default_rng(10)
+    kv = rng.standard_normal((50, D)).astype(np.float32)
+    q = np.zeros((H, D), np.float32)
+    q[:, DC:] = rng.standard_normal((H, DR))          # logits come from the rotary part only
+    o1, _ = oracle.mla_attend(q, kv, np.arange(50, dtype=np.int32), TAU)
+    kv2 = kv.copy()
+    kv2[:, DC:] = 0
+    o2, lse2 = oracle.mla_attend(q, kv2, np.arange(50, dtype=np.int32), TAU)
+    np.testing.assert_allclose(o2, np.broadcast_to(kv[:, :DC].astype(np.float64).mean(0), (H, DC)),
+                               rtol=1e-12, atol=1e-13)
+    assert np.abs(o1 - o2).max() > 1e-3
+
+
+# ----------------------------------------------------------------------------
+# the composed read
+# ----------------------------------------------------------------------------
+
+
+def test_decode_short_context_equals_dense_attention():
+    """L <= 2,048: the selection is every position, so the whole read equals
+    dense attention, whatever the indexer says."""
+    from sparse_attention_12_amd import workloads as wl
+    w = wl.make_decode([1500], "bf16", 2, seed=11)
+    kI = w.widen(w.kI)
+    qs = [w.widen(x)[0] for x in w.q]
+    kvs = [w.widen(x) for x in w.kv]
+    idx, m, outs, lses = oracle.decode_query(w.widen(w.qI)[0], w.w[0], kI, qs, kvs,
+                                             1500, 2048, w.tau)
+    assert m == 1500 and np.array_equal(idx[:1500], np.arange(1500))
+    for q, kv, o in zip(qs, kvs, outs):
+        np.testing.assert_allclose(o, _sdpa(q, kv, w.tau), rtol=1e-10, atol=1e-12)
+
+
+def test_decode_selection_shared_across_layers():
+    from sparse_attention_12_amd import workloads as wl
+    w = wl.make_decode([3000], "f32", 3, seed=12)
+    idx, m, outs, _ = oracle.decode_query(w.qI[0], w.w[0], w.kI, [x[0] for x in w.q], w.kv,
+                                          3000, 2048, w.tau)
+    assert m == 2048
+    for l in range(3):
+        o, _ = oracle.mla_attend(w.q[l][0], w.kv[l], idx, w.tau)
+        np.testing.assert_array_equal(o, outs[l])
+    # the kept set is exactly the brute-force top-2,048 of the scores
+    sc = oracle.index_score(w.qI[0], w.w[0], w.kI)
+    order = np.lexsort((np.arange(3000), -sc))[:2048]
+    assert np.array_equal(np.sort(order), idx)
