@@ -1,0 +1,188 @@
+/*
+ * dsa_mla.h -- C ABI of the MI355X (gfx950) library for one attention read
+ * of Mistral Large 4: DeepSeek-Sparse-Attention indexer -> top-2,048
+ * selection -> 64-head Multi-head Latent Attention over the selected
+ * positions only.
+ *
+ * The operations are defined on the "Mistral Large 4" concept page
+ * (liminalml.com/concepts/mistral-large-4):
+ *   - "What to keep": each cached position holds a 512-value latent plus a
+ *     64-value rotary key shared by all 64 heads, 576 values per row;
+ *   - "Where to look": an indexer with 32 small heads rates every earlier
+ *     position and keeps the best 2,048; all 64 heads attend to those only;
+ *     the change list adds that a layer may reuse the selection of the most
+ *     recent layer that ran its indexer;
+ *   - "Sparse attention": the score of every earlier position, the top
+ *     2,048, and a softmax normalised over the kept positions alone; its cost
+ *     figures (32 x 128 multiply-adds per scored position, 64 x (512 + 64 +
+ *     512) per attended one) fix the shapes below.
+ * The page's display formula for the score was lost; this library computes
+ *   I[q][s] = sum_{h<32} w[q][h] * max(0, sum_{d<128} qI[q][h][d] * kI[s][d])
+ * and the absorbed-form MLA read
+ *   l[h][j] = scale * (q[h][0:576] . kv[S_j][0:576]),  p = softmax_j(l) over S,
+ *   o[h][:] = sum_j p[h][j] * kv[S_j][0:512],  lse[h] = log sum_j exp(l[h][j]).
+ *
+ * Conventions shared by every entry point
+ *   - Every array argument is a DEVICE pointer owned by the caller, except
+ *     the dsa_batch_t struct itself and the per-layer pointer tables of the
+ *     fused call, which are HOST memory read during the call only.
+ *   - The library never allocates, frees or synchronises.  Work is enqueued
+ *     on `stream` (a hipStream_t; NULL = the default stream) and the call
+ *     returns at once; results are ready when the stream reaches them.
+ *   - Return value: DSA_OK (0) or a negative dsa_status_t.  Arguments are
+ *     validated on the host before anything is enqueued; a validation error
+ *     enqueues nothing.  A failed launch returns DSA_ERR_HIP.  The message of
+ *     the last error on the calling thread is in dsa_last_error().
+ *   - Dtypes: DSA_BF16 (bf16 storage, fp32 accumulation) or DSA_F32.  One
+ *     `dtype` covers the indexer query/keys and the MLA query/cache rows;
+ *     indexer weights, scores and log-sum-exp are always float32.
+ *   - Alignment: every pointer 16-byte aligned.  Row strides are fixed:
+ *     indexer keys 128 elements, cache rows 576 (512 latent then 64 rotary).
+ *   - Entries are re-entrant; calls that share a workspace race unless they
+ *     are ordered on one stream.
+ */
+#ifndef DSA_MLA_H
+#define DSA_MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_ABI_VERSION 1
+
+#define DSA_INDEX_HEADS 32  /* indexer heads                          */
+#define DSA_INDEX_DIM 128   /* indexer head width                     */
+#define DSA_MLA_HEADS 64    /* attention heads                        */
+#define DSA_LATENT 512      /* latent width = value width             */
+#define DSA_ROPE 64         /* rotary key width                       */
+#define DSA_ROW 576         /* cache row = latent + rotary key        */
+#define DSA_TOPK_MAX 2048   /* largest supported k (the pages' 2,048) */
+#define DSA_MAX_LAYERS 16   /* largest n_layers of the fused call     */
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_NULL = -1,        /* a required pointer is NULL                         */
+  DSA_ERR_SHAPE = -2,       /* a size is out of range                             */
+  DSA_ERR_DTYPE = -3,       /* unknown dtype                                      */
+  DSA_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned                   */
+  DSA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than the size query says */
+  DSA_ERR_UNSUPPORTED = -6, /* valid but not supported (k > 2,048, too many layers) */
+  DSA_ERR_HIP = -7          /* the HIP runtime reported an error                  */
+} dsa_status_t;
+
+typedef enum { DSA_F32 = 0, DSA_BF16 = 1 } dsa_dtype_t;
+
+/*
+ * A batch of queries over one or more sequences.
+ *   nq, nseq, max_len : host integers.  nq >= 0 (0 is a no-op), nseq >= 1,
+ *                       max_len >= 1 bounds every sequence length and sizes
+ *                       the launch grids.
+ *   q_seq  [nq]   (device) sequence of each query, in [0, nseq).
+ *   q_pos  [nq]   (device) absolute position of each query.
+ *   seq_len[nseq] (device) cached positions of each sequence, <= max_len.
+ *   seq_row0[nseq](device) first row of the sequence in every cache array
+ *                  (indexer keys and each layer's cache rows), so sequences
+ *                  may be packed, padded or ragged.
+ * The candidates of query q are positions s in [0, n_cand(q)) with
+ *   n_cand(q) = min(q_pos[q] + 1, seq_len[q_seq[q]], max_len)
+ * (its own position and every earlier one; "Sparse attention" section).
+ * Decode is nq = nseq with q_pos = seq_len - 1; a prefill chunk is nq
+ * queries of one sequence at increasing positions (causal).
+ * Out-of-range device values are clamped so that no access leaves
+ * [seq_row0, seq_row0 + n_cand); the results are then undefined.
+ */
+typedef struct dsa_batch {
+  int32_t nq;
+  int32_t nseq;
+  int32_t max_len;
+  const int32_t* q_seq;
+  const int32_t* q_pos;
+  const int32_t* seq_len;
+  const int64_t* seq_row0;
+} dsa_batch_t;
+
+/* DSA_ABI_VERSION of the built library. */
+int32_t dsa_abi_version(void);
+/* Static text for a status code. */
+const char* dsa_status_string(int32_t status);
+/* Detail of the last failing call on this thread ("" if none). */
+const char* dsa_last_error(void);
+
+/*
+ * Indexer scores ("Where to look" / "Sparse attention"; formula above).
+ *   q_idx  [nq][32][128] dtype      w_idx [nq][32] float32
+ *   k_idx  [rows][128]   dtype      (row seq_row0[s] + p is position p)
+ *   scores [nq][ld]      float32    column s < n_cand(q) receives I[q][s];
+ *                                   columns >= n_cand(q) are left untouched.
+ *   ld >= max_len.
+ * Decode batches stream the keys once per query; batches of one sequence
+ * with many queries (prefill) run as a blocked matrix product that shares
+ * each key tile across 32 queries.
+ */
+int32_t dsa_index_score(const dsa_batch_t* batch, int32_t dtype, const void* q_idx,
+                        const float* w_idx, const void* k_idx, float* scores, int64_t ld,
+                        void* stream);
+
+/*
+ * Top-k selection ("Where to look": keep the best 2,048).  For each query,
+ * S_q = the first min(k, n_cand(q)) positions under the total order
+ * (score descending, position ascending); ties therefore go to the lower
+ * position and S_q is unique.  Score -0.0 equals +0.0; NaN is undefined.
+ *   scores [nq][ld] float32 (columns < n_cand(q) are read)
+ *   idx    [nq][k]  int32   S_q in ascending position order, then -1 padding
+ *   count  [nq]     int32   |S_q| (may be NULL)
+ *   1 <= k <= 2,048.  ws: dsa_topk_workspace_size(nq, max_len, k) bytes
+ *   (may be 0, then ws may be NULL).
+ */
+size_t dsa_topk_workspace_size(int32_t nq, int32_t max_len, int32_t k);
+int32_t dsa_topk(const dsa_batch_t* batch, const float* scores, int64_t ld, int32_t k,
+                 int32_t* idx, int32_t* count, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Sparse MLA read of one layer ("What to keep", "Sparse attention").
+ *   q   [nq][64][576] dtype    absorbed query: 512 latent-space + 64 rotary
+ *   kv  [rows][576]   dtype    cache rows (512 latent, 64 rotary key)
+ *   idx [nq][k]       int32    selected positions; entries outside
+ *                              [0, n_cand(q)) (e.g. the -1 padding) are skipped
+ *   scale                      logit scale (the harness uses 1/sqrt(192))
+ *   out [nq][64][512] out_dtype  softmax over the selected entries only
+ *   lse [nq][64]      float32  natural log-sum-exp of the scaled logits
+ *                              (may be NULL); a query with no valid entry
+ *                              gets out = 0 and lse = -inf.
+ *   1 <= k <= 2,048.  ws: mla_sparse_attend_workspace_size(nq, k, 1) bytes.
+ */
+size_t mla_sparse_attend_workspace_size(int32_t nq, int32_t k, int32_t n_layers);
+int32_t mla_sparse_attend(const dsa_batch_t* batch, int32_t dtype, const void* q, const void* kv,
+                          const int32_t* idx, int32_t k, float scale, void* out,
+                          int32_t out_dtype, float* lse, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/*
+ * Fused decode read with selection sharing (change list on the concept
+ * page: 28 layers reuse the selection of the most recent layer that ran its
+ * indexer).  Runs the indexer and the top-k once, then the sparse MLA read
+ * of n_layers layers, each with its own query and cache, over that one
+ * selection.  Arguments as in the three calls above; per-layer arrays come
+ * as HOST tables of n_layers device pointers:
+ *   q_l[l]   [nq][64][576] dtype    kv_l[l] [rows][576] dtype
+ *   out_l[l] [nq][64][512] out_dtype  lse_l[l] [nq][64] float32 (lse_l or
+ *   any entry may be NULL)
+ *   idx_out  [nq][k] int32 (may be NULL): the shared selection.
+ *   1 <= n_layers <= 16.  ws: dsa_mla_decode_fused_workspace_size(...) bytes.
+ */
+size_t dsa_mla_decode_fused_workspace_size(int32_t nq, int32_t max_len, int32_t k,
+                                           int32_t n_layers);
+int32_t dsa_mla_decode_fused(const dsa_batch_t* batch, int32_t dtype, const void* q_idx,
+                             const float* w_idx, const void* k_idx, int32_t k, int32_t n_layers,
+                             const void* const* q_l, const void* const* kv_l,
+                             void* const* out_l, float* const* lse_l, int32_t out_dtype,
+                             float scale, int32_t* idx_out, void* ws, size_t ws_bytes,
+                             void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_MLA_H */

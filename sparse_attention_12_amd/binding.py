@@ -1,0 +1,172 @@
+"""Thin ctypes binding of libdsa_mla.so (C ABI in include/dsa_mla.h).
+
+Argument marshalling only: torch tensors are passed as device pointers on the
+caller's current stream; every step of the read runs in the HIP kernels.
+There is no fallback: if the library is missing or fails to load, importing
+this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa_mla.so")
+
+DSA_F32, DSA_BF16 = 0, 1
+INDEX_HEADS, INDEX_DIM, HEADS, LATENT, ROPE, ROW, TOPK_MAX = 32, 128, 64, 512, 64, 576, 2048
+
+EXPORTS = [
+    "dsa_abi_version", "dsa_status_string", "dsa_last_error", "dsa_index_score",
+    "dsa_topk_workspace_size", "dsa_topk", "mla_sparse_attend_workspace_size",
+    "mla_sparse_attend", "dsa_mla_decode_fused_workspace_size", "dsa_mla_decode_fused",
+]
+
+
+class DsaBatch(ctypes.Structure):
+    _fields_ = [
+        ("nq", ctypes.c_int32), ("nseq", ctypes.c_int32), ("max_len", ctypes.c_int32),
+        ("q_seq", ctypes.c_void_p), ("q_pos", ctypes.c_void_p),
+        ("seq_len", ctypes.c_void_p), ("seq_row0", ctypes.c_void_p),
+    ]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                          "(hipcc --offload-arch=gfx950); there is no CPU fallback")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    bp = ctypes.POINTER(DsaBatch)
+    lib.dsa_abi_version.restype = i32
+    lib.dsa_status_string.argtypes = [i32]
+    lib.dsa_status_string.restype = ctypes.c_char_p
+    lib.dsa_last_error.restype = ctypes.c_char_p
+    lib.dsa_index_score.argtypes = [bp, i32, vp, vp, vp, vp, i64, vp]
+    lib.dsa_index_score.restype = i32
+    lib.dsa_topk_workspace_size.argtypes = [i32, i32, i32]
+    lib.dsa_topk_workspace_size.restype = sz
+    lib.dsa_topk.argtypes = [bp, vp, i64, i32, vp, vp, vp, sz, vp]
+    lib.dsa_topk.restype = i32
+    lib.mla_sparse_attend_workspace_size.argtypes = [i32, i32, i32]
+    lib.mla_sparse_attend_workspace_size.restype = sz
+    lib.mla_sparse_attend.argtypes = [bp, i32, vp, vp, vp, i32, ctypes.c_float, vp, i32, vp, vp, sz, vp]
+    lib.mla_sparse_attend.restype = i32
+    lib.dsa_mla_decode_fused_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.dsa_mla_decode_fused_workspace_size.restype = sz
+    lib.dsa_mla_decode_fused.argtypes = [bp, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, i32,
+                                         ctypes.c_float, vp, vp, sz, vp]
+    lib.dsa_mla_decode_fused.restype = i32
+    return lib
+
+
+lib = _load()
+
+
+class DsaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib.dsa_last_error().decode() or lib.dsa_status_string(status).decode()
+        super().__init__(f"{where}: {lib.dsa_status_string(status).decode()} ({msg})")
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise DsaError(status, where)
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DSA_BF16
+    if t.dtype == torch.float32:
+        return DSA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class Batch:
+    """Queries over sequences: device index arrays plus the host sizes."""
+
+    def __init__(self, q_seq, q_pos, seq_len, seq_row0, max_len: int):
+        self.q_seq = q_seq.to(torch.int32).contiguous()
+        self.q_pos = q_pos.to(torch.int32).contiguous()
+        self.seq_len = seq_len.to(torch.int32).contiguous()
+        self.seq_row0 = seq_row0.to(torch.int64).contiguous()
+        self.nq = int(self.q_seq.shape[0])
+        self.nseq = int(self.seq_len.shape[0])
+        self.max_len = int(max_len)
+        self._s = DsaBatch(self.nq, self.nseq, self.max_len, self.q_seq.data_ptr(),
+                           self.q_pos.data_ptr(), self.seq_len.data_ptr(), self.seq_row0.data_ptr())
+
+    @property
+    def ref(self):
+        return ctypes.byref(self._s)
+
+
+def abi_version() -> int:
+    return int(lib.dsa_abi_version())
+
+
+def dsa_index_score(batch: Batch, q_idx, w_idx, k_idx, scores, ld: Optional[int] = None, stream=None):
+    ld = scores.shape[-1] if ld is None else ld
+    _check(lib.dsa_index_score(batch.ref, _dt(q_idx), _p(q_idx), _p(w_idx), _p(k_idx), _p(scores),
+                               ld, _stream(stream)), "dsa_index_score")
+    return scores
+
+
+def dsa_topk_workspace_size(nq: int, max_len: int, k: int) -> int:
+    return int(lib.dsa_topk_workspace_size(nq, max_len, k))
+
+
+def dsa_topk(batch: Batch, scores, k: int, idx, count=None, ws=None, ld: Optional[int] = None,
+             stream=None):
+    ld = scores.shape[-1] if ld is None else ld
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.dsa_topk(batch.ref, _p(scores), ld, k, _p(idx), _p(count), _p(ws), wsb, _stream(stream)),
+           "dsa_topk")
+    return idx
+
+
+def mla_sparse_attend_workspace_size(nq: int, k: int, n_layers: int = 1) -> int:
+    return int(lib.mla_sparse_attend_workspace_size(nq, k, n_layers))
+
+
+def mla_sparse_attend(batch: Batch, q, kv, idx, k: int, scale: float, out, lse=None, ws=None,
+                      stream=None):
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.mla_sparse_attend(batch.ref, _dt(q), _p(q), _p(kv), _p(idx), k, scale, _p(out), _dt(out),
+                                 _p(lse), _p(ws), wsb, _stream(stream)), "mla_sparse_attend")
+    return out
+
+
+def dsa_mla_decode_fused_workspace_size(nq: int, max_len: int, k: int, n_layers: int) -> int:
+    return int(lib.dsa_mla_decode_fused_workspace_size(nq, max_len, k, n_layers))
+
+
+def dsa_mla_decode_fused(batch: Batch, q_idx, w_idx, k_idx, k: int, q_l: Sequence, kv_l: Sequence,
+                         out_l: Sequence, scale: float, lse_l: Optional[Sequence] = None,
+                         idx_out=None, ws=None, stream=None):
+    n = len(q_l)
+    arr = ctypes.c_void_p * n
+    qa = arr(*[t.data_ptr() for t in q_l])
+    kva = arr(*[t.data_ptr() for t in kv_l])
+    oa = arr(*[t.data_ptr() for t in out_l])
+    la = None if lse_l is None else arr(*[(0 if t is None else t.data_ptr()) for t in lse_l])
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    cv = lambda a: None if a is None else ctypes.cast(a, ctypes.c_void_p)
+    _check(lib.dsa_mla_decode_fused(batch.ref, _dt(q_idx), _p(q_idx), _p(w_idx), _p(k_idx), k, n,
+                                    cv(qa), cv(kva), cv(oa), cv(la), _dt(out_l[0]), scale, _p(idx_out),
+                                    _p(ws), wsb, _stream(stream)), "dsa_mla_decode_fused")
+    return out_l

@@ -1,0 +1,242 @@
+// C ABI of the library (declared in include/dsa_mla.h): host-side argument
+// validation, workspace accounting and kernel dispatch.  Nothing here
+// allocates, frees or synchronises; every launch goes to the caller's stream.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/dsa_mla.h"
+#include "dsa_common.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return DSA_OK;
+  return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define REQUIRE_PTR(p)                                        \
+  do {                                                        \
+    if ((p) == nullptr) return fail(DSA_ERR_NULL, "%s is NULL", #p); \
+    if (!aligned16(p)) return fail(DSA_ERR_ALIGN, "%s is not 16-byte aligned", #p); \
+  } while (0)
+
+int check_batch(const dsa_batch_t* b, dsa::BatchDev* out) {
+  if (b == nullptr) return fail(DSA_ERR_NULL, "batch is NULL");
+  if (b->nq < 0) return fail(DSA_ERR_SHAPE, "nq = %d < 0", b->nq);
+  if (b->nseq < 1) return fail(DSA_ERR_SHAPE, "nseq = %d < 1", b->nseq);
+  if (b->max_len < 1) return fail(DSA_ERR_SHAPE, "max_len = %d < 1", b->max_len);
+  if (b->nq > 0) {
+    if (!b->q_seq || !b->q_pos || !b->seq_len || !b->seq_row0)
+      return fail(DSA_ERR_NULL, "a batch index array is NULL");
+  }
+  out->nq = b->nq;
+  out->nseq = b->nseq;
+  out->max_len = b->max_len;
+  out->q_seq = b->q_seq;
+  out->q_pos = b->q_pos;
+  out->seq_len = b->seq_len;
+  out->seq_row0 = b->seq_row0;
+  return DSA_OK;
+}
+
+int check_dtype(int32_t dt, const char* what) {
+  if (dt != DSA_F32 && dt != DSA_BF16) return fail(DSA_ERR_DTYPE, "%s = %d is not DSA_F32 or DSA_BF16", what, dt);
+  return DSA_OK;
+}
+
+int check_k(int32_t k) {
+  if (k < 1) return fail(DSA_ERR_SHAPE, "k = %d < 1", k);
+  if (k > DSA_TOPK_MAX) return fail(DSA_ERR_UNSUPPORTED, "k = %d > %d", k, DSA_TOPK_MAX);
+  return DSA_OK;
+}
+
+hipStream_t as_stream(void* s) { return (hipStream_t)s; }
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+const char* dsa_status_string(int32_t st) {
+  switch (st) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_NULL: return "DSA_ERR_NULL: a required pointer is NULL";
+    case DSA_ERR_SHAPE: return "DSA_ERR_SHAPE: a size is out of range";
+    case DSA_ERR_DTYPE: return "DSA_ERR_DTYPE: unknown dtype";
+    case DSA_ERR_ALIGN: return "DSA_ERR_ALIGN: a pointer is not 16-byte aligned";
+    case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE: workspace missing or too small";
+    case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED: valid but unsupported arguments";
+    case DSA_ERR_HIP: return "DSA_ERR_HIP: the HIP runtime reported an error";
+    default: return "unknown status";
+  }
+}
+
+const char* dsa_last_error(void) { return g_err; }
+
+int32_t dsa_index_score(const dsa_batch_t* batch, int32_t dtype, const void* q_idx, const float* w_idx,
+                        const void* k_idx, float* scores, int64_t ld, void* stream) {
+  dsa::BatchDev b;
+  int st = check_batch(batch, &b);
+  if (st) return st;
+  if ((st = check_dtype(dtype, "dtype"))) return st;
+  if (b.nq == 0) return DSA_OK;
+  REQUIRE_PTR(q_idx);
+  REQUIRE_PTR(w_idx);
+  REQUIRE_PTR(k_idx);
+  if (scores == nullptr) return fail(DSA_ERR_NULL, "scores is NULL");
+  if (ld < b.max_len) return fail(DSA_ERR_SHAPE, "ld = %lld < max_len = %d", (long long)ld, b.max_len);
+  return hip_status(dsa::launch_index_score(b, dtype, q_idx, w_idx, k_idx, scores, ld, as_stream(stream)),
+                    "dsa_index_score launch");
+}
+
+size_t dsa_topk_workspace_size(int32_t nq, int32_t max_len, int32_t k) {
+  if (nq <= 0 || max_len <= 0 || k <= 0) return 0;
+  return dsa::topk_workspace_bytes(nq, max_len, k);
+}
+
+int32_t dsa_topk(const dsa_batch_t* batch, const float* scores, int64_t ld, int32_t k, int32_t* idx,
+                 int32_t* count, void* ws, size_t ws_bytes, void* stream) {
+  dsa::BatchDev b;
+  int st = check_batch(batch, &b);
+  if (st) return st;
+  if ((st = check_k(k))) return st;
+  if (b.nq == 0) return DSA_OK;
+  if (scores == nullptr) return fail(DSA_ERR_NULL, "scores is NULL");
+  if (idx == nullptr) return fail(DSA_ERR_NULL, "idx is NULL");
+  if (ld < b.max_len) return fail(DSA_ERR_SHAPE, "ld = %lld < max_len = %d", (long long)ld, b.max_len);
+  const size_t need = dsa::topk_workspace_bytes(b.nq, b.max_len, k);
+  if (need > 0 && (ws == nullptr || ws_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "top-k workspace: %zu bytes given, %zu needed", ws_bytes, need);
+  return hip_status(dsa::launch_topk(b, scores, ld, k, idx, count, ws, ws_bytes, as_stream(stream)),
+                    "dsa_topk launch");
+}
+
+size_t mla_sparse_attend_workspace_size(int32_t nq, int32_t k, int32_t n_layers) {
+  if (nq <= 0 || k <= 0 || n_layers <= 0) return 0;
+  // sized for the larger of the two dtypes' split plans
+  size_t a = dsa::mla_workspace_bytes(0, nq, k, n_layers);
+  size_t c = dsa::mla_workspace_bytes(1, nq, k, n_layers);
+  return a > c ? a : c;
+}
+
+static int check_mla_layer(const void* q, const void* kv, const void* out) {
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(kv);
+  REQUIRE_PTR(out);
+  return DSA_OK;
+}
+
+int32_t mla_sparse_attend(const dsa_batch_t* batch, int32_t dtype, const void* q, const void* kv,
+                          const int32_t* idx, int32_t k, float scale, void* out, int32_t out_dtype,
+                          float* lse, void* ws, size_t ws_bytes, void* stream) {
+  dsa::BatchDev b;
+  int st = check_batch(batch, &b);
+  if (st) return st;
+  if ((st = check_dtype(dtype, "dtype"))) return st;
+  if ((st = check_dtype(out_dtype, "out_dtype"))) return st;
+  if ((st = check_k(k))) return st;
+  if (b.nq == 0) return DSA_OK;
+  if ((st = check_mla_layer(q, kv, out))) return st;
+  if (idx == nullptr) return fail(DSA_ERR_NULL, "idx is NULL");
+  const size_t need = dsa::mla_workspace_bytes(dtype, b.nq, k, 1);
+  if (need > 0 && (ws == nullptr || ws_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "MLA workspace: %zu bytes given, %zu needed", ws_bytes, need);
+  if (ws && !aligned16(ws)) return fail(DSA_ERR_ALIGN, "ws is not 16-byte aligned");
+  dsa::MlaLayers L;
+  memset(&L, 0, sizeof(L));
+  L.q[0] = q;
+  L.kv[0] = kv;
+  L.out[0] = out;
+  L.lse[0] = lse;
+  return hip_status(dsa::launch_mla(b, dtype, L, 1, idx, k, scale, out_dtype, ws, ws_bytes, as_stream(stream)),
+                    "mla_sparse_attend launch");
+}
+
+static size_t fused_parts(int32_t nq, int32_t max_len, int32_t k, int32_t n_layers, size_t* off_idx,
+                          size_t* off_topk, size_t* off_mla) {
+  size_t off = 0;
+  // scores [nq][max_len] float32
+  off = align_up(off + (size_t)nq * (size_t)max_len * sizeof(float));
+  *off_idx = off;
+  off = align_up(off + (size_t)nq * (size_t)k * sizeof(int32_t));
+  *off_topk = off;
+  off = align_up(off + dsa::topk_workspace_bytes(nq, max_len, k));
+  *off_mla = off;
+  size_t a = dsa::mla_workspace_bytes(0, nq, k, n_layers);
+  size_t c = dsa::mla_workspace_bytes(1, nq, k, n_layers);
+  off = align_up(off + (a > c ? a : c));
+  return off;
+}
+
+size_t dsa_mla_decode_fused_workspace_size(int32_t nq, int32_t max_len, int32_t k, int32_t n_layers) {
+  if (nq <= 0 || max_len <= 0 || k <= 0 || n_layers <= 0) return 0;
+  size_t a, c, d;
+  return fused_parts(nq, max_len, k, n_layers, &a, &c, &d);
+}
+
+int32_t dsa_mla_decode_fused(const dsa_batch_t* batch, int32_t dtype, const void* q_idx, const float* w_idx,
+                             const void* k_idx, int32_t k, int32_t n_layers, const void* const* q_l,
+                             const void* const* kv_l, void* const* out_l, float* const* lse_l,
+                             int32_t out_dtype, float scale, int32_t* idx_out, void* ws, size_t ws_bytes,
+                             void* stream) {
+  dsa::BatchDev b;
+  int st = check_batch(batch, &b);
+  if (st) return st;
+  if ((st = check_dtype(dtype, "dtype"))) return st;
+  if ((st = check_dtype(out_dtype, "out_dtype"))) return st;
+  if ((st = check_k(k))) return st;
+  if (n_layers < 1) return fail(DSA_ERR_SHAPE, "n_layers = %d < 1", n_layers);
+  if (n_layers > DSA_MAX_LAYERS) return fail(DSA_ERR_UNSUPPORTED, "n_layers = %d > %d", n_layers, DSA_MAX_LAYERS);
+  if (b.nq == 0) return DSA_OK;
+  REQUIRE_PTR(q_idx);
+  REQUIRE_PTR(w_idx);
+  REQUIRE_PTR(k_idx);
+  if (!q_l || !kv_l || !out_l) return fail(DSA_ERR_NULL, "a per-layer pointer table is NULL");
+  dsa::MlaLayers L;
+  memset(&L, 0, sizeof(L));
+  for (int l = 0; l < n_layers; ++l) {
+    if ((st = check_mla_layer(q_l[l], kv_l[l], out_l[l]))) return st;
+    L.q[l] = q_l[l];
+    L.kv[l] = kv_l[l];
+    L.out[l] = out_l[l];
+    L.lse[l] = lse_l ? lse_l[l] : nullptr;
+  }
+  size_t off_idx, off_topk, off_mla;
+  const size_t need = fused_parts(b.nq, b.max_len, k, n_layers, &off_idx, &off_topk, &off_mla);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "fused workspace: %zu bytes given, %zu needed", ws_bytes, need);
+  if (!aligned16(ws)) return fail(DSA_ERR_ALIGN, "ws is not 16-byte aligned");
+  char* base = (char*)ws;
+  float* scores = (float*)base;
+  int32_t* idx = idx_out ? idx_out : (int32_t*)(base + off_idx);
+  hipStream_t s = as_stream(stream);
+  if ((st = hip_status(dsa::launch_index_score(b, dtype, q_idx, w_idx, k_idx, scores, b.max_len, s),
+                       "fused: index score launch")))
+    return st;
+  if ((st = hip_status(dsa::launch_topk(b, scores, b.max_len, k, idx, nullptr, base + off_topk,
+                                        off_mla - off_topk, s),
+                       "fused: top-k launch")))
+    return st;
+  return hip_status(dsa::launch_mla(b, dtype, L, n_layers, idx, k, scale, out_dtype, base + off_mla,
+                                    need - off_mla, s),
+                    "fused: MLA launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,92 @@
+// Shared device helpers of the gfx950 kernels: fixed shapes, bf16 handling,
+// MFMA operand types, per-query candidate ranges and the order-preserving
+// score key used by the selection.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+constexpr int HI = 32;    // indexer heads
+constexpr int DI = 128;   // indexer head width
+constexpr int H = 64;     // attention heads
+constexpr int DC = 512;   // latent (= value) width
+constexpr int DR = 64;    // rotary key width
+constexpr int D = 576;    // cache row
+constexpr int KMAX = 2048;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Device copy of the host batch descriptor (passed by value to kernels).
+struct BatchDev {
+  int nq, nseq, max_len;
+  const int32_t* q_seq;
+  const int32_t* q_pos;
+  const int32_t* seq_len;
+  const int64_t* seq_row0;
+};
+
+struct QueryRange {
+  int n;        // candidates: positions [0, n)
+  int64_t row0; // first row of the query's sequence in the caches
+};
+
+// Candidates of query q: its own position and every earlier one, clamped to
+// the sequence length and to max_len (so no access leaves the sequence).
+__device__ inline QueryRange query_range(const BatchDev& b, int q) {
+  QueryRange r;
+  int s = b.q_seq[q];
+  if (s < 0 || s >= b.nseq) {
+    r.n = 0;
+    r.row0 = 0;
+    return r;
+  }
+  int64_t n = (int64_t)b.q_pos[q] + 1;
+  int64_t L = b.seq_len[s];
+  if (L < n) n = L;
+  if (b.max_len < n) n = b.max_len;
+  if (n < 0) n = 0;
+  r.n = (int)n;
+  r.row0 = b.seq_row0[s];
+  return r;
+}
+
+__device__ inline float bf16_to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+__device__ inline uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Two floats -> packed bf16 pair (low half = a).
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+
+// Unsigned key whose order is the order of the float scores; -0.0 and +0.0
+// map to the same key.
+__device__ inline uint32_t score_key(float s) {
+  uint32_t u = __float_as_uint(s == 0.0f ? 0.0f : s);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// 64-bit key that is unique per position: higher score first, then lower
+// position first.
+__device__ inline uint64_t select_key(uint32_t skey, int pos) {
+  return ((uint64_t)skey << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)pos);
+}
+
+__device__ inline u32x4 load16_nt(const void* p) {
+  return __builtin_nontemporal_load((const u32x4*)p);
+}
+
+__device__ inline u32x4 load16(const void* p) { return *(const u32x4*)p; }
+
+__device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+}  // namespace dsa

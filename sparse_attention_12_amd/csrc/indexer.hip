@@ -1,0 +1,239 @@
+// DSA indexer scores on gfx950.
+//
+// Score of position s for query q (concept page "Mistral Large 4", sections
+// "Where to look" and "Sparse attention"; the 32 x 128 cost per scored
+// position fixes the shapes):
+//   I[q][s] = sum_{h<32} w[q][h] * max(0, qI[q][h][:] . kI[s][:])
+//
+// Decode (one query per sequence) is a stream over the query's keys: the
+// 32 heads sit on the M axis of a v_mfma_f32_32x32x16_bf16 tile, 32 keys on
+// N, and the 128-wide contraction takes 8 MFMAs.  Each lane then holds 16 of
+// the 32 head dot products of one key, so the ReLU and the weighted head sum
+// stay in registers and finish with one cross-lane add.
+//
+// Prefill (many queries of one sequence) is a blocked product: a workgroup
+// keeps 32 queries' indexer rows in registers (4 per wave) and streams key
+// tiles through LDS, so each key tile read from L2 feeds 32 queries.
+#include "dsa_common.h"
+#include "kernels.h"
+
+namespace dsa {
+
+// ---------------------------------------------------------------------------
+// decode, bf16
+// ---------------------------------------------------------------------------
+constexpr int IDX_DEC_THREADS = 256;
+constexpr int IDX_DEC_WAVES = IDX_DEC_THREADS / 64;
+constexpr int IDX_DEC_STEP = 32;       // keys per MFMA step and wave
+constexpr int IDX_DEC_CHUNK = 4096;    // keys per workgroup
+
+__global__ __launch_bounds__(IDX_DEC_THREADS) void idx_decode_bf16(
+    BatchDev b, const uint16_t* __restrict__ qI, const float* __restrict__ w,
+    const uint16_t* __restrict__ kI, float* __restrict__ scores, int64_t ld) {
+  const int q = blockIdx.y;
+  const QueryRange r = query_range(b, q);
+  const int base = blockIdx.x * IDX_DEC_CHUNK;
+  if (base >= r.n) return;
+  const int end = min(base + IDX_DEC_CHUNK, r.n);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 31;   // A row (head) / B column (key) of this lane
+  const int half = lane >> 5;  // which 8 of each 16 contraction slots
+
+  // A operand: head `col`, contraction slots t*16 + half*8 + [0,8).
+  bf16x8 a[8];
+  const uint16_t* qrow = qI + ((int64_t)q * HI + col) * DI + half * 8;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) a[t] = as_bf16x8(load16(qrow + t * 16));
+  // Accumulator register i of this lane holds head 8*(i/4) + 4*half + i%4.
+  float wr[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) wr[i] = w[(int64_t)q * HI + 8 * (i >> 2) + 4 * half + (i & 3)];
+
+  const uint16_t* kb = kI + r.row0 * DI + half * 8;
+  float* out = scores + (int64_t)q * ld;
+  const int last = r.n - 1;
+
+  int key0 = base + wave * IDX_DEC_STEP;
+  if (key0 >= end) return;
+  u32x4 cur[8], nxt[8];
+  {
+    const uint16_t* p = kb + (int64_t)min(key0 + col, last) * DI;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) cur[t] = load16_nt(p + t * 16);
+  }
+  while (true) {
+    const int nkey0 = key0 + IDX_DEC_WAVES * IDX_DEC_STEP;
+    const bool more = nkey0 < end;
+    if (more) {
+      const uint16_t* p = kb + (int64_t)min(nkey0 + col, last) * DI;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) nxt[t] = load16_nt(p + t * 16);
+    }
+    f32x16 acc = {};
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t], as_bf16x8(cur[t]), acc, 0, 0, 0);
+    float part = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) part = fmaf(wr[i], fmaxf(acc[i], 0.0f), part);
+    part += __shfl_xor(part, 32);
+    const int key = key0 + col;
+    if (half == 0 && key < end) out[key] = part;
+    if (!more) break;
+    key0 = nkey0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) cur[t] = nxt[t];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// decode, fp32 (VALU; small fp32 workloads)
+// ---------------------------------------------------------------------------
+constexpr int IDX_F32_THREADS = 256;
+
+__global__ __launch_bounds__(IDX_F32_THREADS) void idx_decode_f32(
+    BatchDev b, const float* __restrict__ qI, const float* __restrict__ w,
+    const float* __restrict__ kI, float* __restrict__ scores, int64_t ld) {
+  __shared__ float qs[HI * DI];
+  __shared__ float wsh[HI];
+  const int q = blockIdx.y;
+  const QueryRange r = query_range(b, q);
+  const int base = blockIdx.x * IDX_F32_THREADS;
+  if (base >= r.n) return;
+  for (int i = threadIdx.x; i < HI * DI; i += IDX_F32_THREADS) qs[i] = qI[(int64_t)q * HI * DI + i];
+  if (threadIdx.x < HI) wsh[threadIdx.x] = w[(int64_t)q * HI + threadIdx.x];
+  __syncthreads();
+  const int key = base + threadIdx.x;
+  if (key >= r.n) return;
+  const float4* kp = (const float4*)(kI + (r.row0 + key) * DI);
+  float4 kr[DI / 4];
+#pragma unroll
+  for (int i = 0; i < DI / 4; ++i) kr[i] = kp[i];
+  float total = 0.0f;
+  for (int h = 0; h < HI; ++h) {
+    const float* qh = qs + h * DI;
+    float dot = 0.0f;
+#pragma unroll
+    for (int i = 0; i < DI / 4; ++i) {
+      dot = fmaf(qh[4 * i + 0], kr[i].x, dot);
+      dot = fmaf(qh[4 * i + 1], kr[i].y, dot);
+      dot = fmaf(qh[4 * i + 2], kr[i].z, dot);
+      dot = fmaf(qh[4 * i + 3], kr[i].w, dot);
+    }
+    total = fmaf(wsh[h], fmaxf(dot, 0.0f), total);
+  }
+  scores[(int64_t)q * ld + key] = total;
+}
+
+// ---------------------------------------------------------------------------
+// prefill, bf16: 32 queries of one sequence per workgroup
+// ---------------------------------------------------------------------------
+constexpr int PF_THREADS = 512;
+constexpr int PF_WAVES = PF_THREADS / 64;
+constexpr int PF_QPW = 4;                    // queries per wave
+constexpr int PF_QB = PF_WAVES * PF_QPW;     // queries per workgroup
+constexpr int PF_TK = 32;                    // keys per LDS tile
+constexpr int PF_KC = 8192;                  // keys per workgroup
+
+__global__ __launch_bounds__(PF_THREADS) void idx_prefill_bf16(
+    BatchDev b, const uint16_t* __restrict__ qI, const float* __restrict__ w,
+    const uint16_t* __restrict__ kI, float* __restrict__ scores, int64_t ld) {
+  // Key tile: 32 keys x 16 chunks of 16 B; chunk c of key k sits at slot
+  // k*16 + (c ^ (k & 15)) so that the B-operand reads hit distinct banks.
+  __shared__ u32x4 ktile[2][PF_TK * 16];
+  __shared__ float wl[PF_QB * HI];
+  __shared__ int ncand[PF_QB];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 31;
+  const int half = lane >> 5;
+  const int qg0 = blockIdx.y * PF_QB;
+  const int kbase = blockIdx.x * PF_KC;
+
+  if (tid < PF_QB) {
+    const int qi = qg0 + tid;
+    ncand[tid] = qi < b.nq ? query_range(b, qi).n : 0;
+  }
+  for (int i = tid; i < PF_QB * HI; i += PF_THREADS) {
+    const int qi = qg0 + i / HI;
+    wl[i] = qi < b.nq ? w[(int64_t)qg0 * HI + i] : 0.0f;
+  }
+  __syncthreads();
+  int nmax = 0;
+#pragma unroll
+  for (int j = 0; j < PF_QB; ++j) nmax = max(nmax, ncand[j]);
+  const int kend = min(kbase + PF_KC, nmax);
+  if (kbase >= kend) return;
+  const int64_t row0 = b.seq_row0[0];
+
+  bf16x8 a[PF_QPW][8];
+  int nj[PF_QPW];
+#pragma unroll
+  for (int j = 0; j < PF_QPW; ++j) {
+    const int ql = wave * PF_QPW + j;
+    const int qc = min(qg0 + ql, b.nq - 1);
+    const uint16_t* qrow = qI + ((int64_t)qc * HI + col) * DI + half * 8;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) a[j][t] = as_bf16x8(load16(qrow + t * 16));
+    nj[j] = ncand[ql];
+  }
+
+  const int lk = tid >> 4;   // key of the tile this thread stages
+  const int lc = tid & 15;   // its 16-byte chunk
+  const int lslot = lk * 16 + (lc ^ (lk & 15));
+  const uint16_t* kb = kI + row0 * DI + lc * 8;
+  u32x4 pre = load16_nt(kb + (int64_t)min(kbase + lk, kend - 1) * DI);
+  int buf = 0;
+  for (int k0 = kbase; k0 < kend; k0 += PF_TK) {
+    ktile[buf][lslot] = pre;
+    __syncthreads();
+    if (k0 + PF_TK < kend) pre = load16_nt(kb + (int64_t)min(k0 + PF_TK + lk, kend - 1) * DI);
+    bf16x8 bfr[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      bfr[t] = as_bf16x8(ktile[buf][col * 16 + ((2 * t + half) ^ (col & 15))]);
+#pragma unroll
+    for (int j = 0; j < PF_QPW; ++j) {
+      if (k0 >= nj[j]) continue;
+      f32x16 acc = {};
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j][t], bfr[t], acc, 0, 0, 0);
+      const float* wq = wl + (wave * PF_QPW + j) * HI + 4 * half;
+      float part = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) part = fmaf(wq[8 * (i >> 2) + (i & 3)], fmaxf(acc[i], 0.0f), part);
+      part += __shfl_xor(part, 32);
+      const int key = k0 + col;
+      if (half == 0 && key < nj[j])
+        scores[(int64_t)(qg0 + wave * PF_QPW + j) * ld + key] = part;
+    }
+    buf ^= 1;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_index_score(const BatchDev& b, int dtype, const void* qI, const float* w,
+                              const void* kI, float* scores, int64_t ld, hipStream_t st) {
+  if (b.nq == 0) return hipSuccess;
+  if (dtype == 0) {
+    dim3 grid((b.max_len + IDX_F32_THREADS - 1) / IDX_F32_THREADS, b.nq);
+    hipLaunchKernelGGL(idx_decode_f32, grid, dim3(IDX_F32_THREADS), 0, st, b, (const float*)qI, w,
+                       (const float*)kI, scores, ld);
+  } else if (b.nseq == 1 && b.nq >= PF_QB) {
+    dim3 grid((b.max_len + PF_KC - 1) / PF_KC, (b.nq + PF_QB - 1) / PF_QB);
+    hipLaunchKernelGGL(idx_prefill_bf16, grid, dim3(PF_THREADS), 0, st, b, (const uint16_t*)qI, w,
+                       (const uint16_t*)kI, scores, ld);
+  } else {
+    dim3 grid((b.max_len + IDX_DEC_CHUNK - 1) / IDX_DEC_CHUNK, b.nq);
+    hipLaunchKernelGGL(idx_decode_bf16, grid, dim3(IDX_DEC_THREADS), 0, st, b,
+                       (const uint16_t*)qI, w, (const uint16_t*)kI, scores, ld);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -1,0 +1,35 @@
+// Host-side launchers of the gfx950 kernels, called by the C ABI layer.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "dsa_common.h"
+
+namespace dsa {
+
+constexpr int MLA_MAX_LAYERS = 16;
+
+// Indexer scores of every query over its candidates (indexer.hip).
+hipError_t launch_index_score(const BatchDev& b, int dtype, const void* qI, const float* w,
+                              const void* kI, float* scores, int64_t ld, hipStream_t st);
+
+// Top-k selection (topk.hip).  ws may be NULL when topk_workspace_bytes() == 0.
+size_t topk_workspace_bytes(int nq, int max_len, int k);
+hipError_t launch_topk(const BatchDev& b, const float* scores, int64_t ld, int k, int32_t* idx,
+                       int32_t* count, void* ws, size_t ws_bytes, hipStream_t st);
+
+// Sparse MLA over a shared selection for n_layers layers (mla.hip).
+struct MlaLayers {
+  const void* q[MLA_MAX_LAYERS];
+  const void* kv[MLA_MAX_LAYERS];
+  void* out[MLA_MAX_LAYERS];
+  float* lse[MLA_MAX_LAYERS];
+};
+int mla_num_splits(int dtype, int nq, int k, int n_layers);
+size_t mla_workspace_bytes(int dtype, int nq, int k, int n_layers);
+hipError_t launch_mla(const BatchDev& b, int dtype, const MlaLayers& layers, int n_layers,
+                      const int32_t* idx, int k, float scale, int out_dtype, void* ws,
+                      size_t ws_bytes, hipStream_t st);
+
+}  // namespace dsa

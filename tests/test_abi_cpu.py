@@ -1,0 +1,146 @@
+"""The C ABI library loads on the CPU, exports every declared entry point and
+rejects invalid arguments on the host, before anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa_mla.h")
+LIB = os.path.join(ROOT, "sparse_attention_12_amd", "libdsa_mla.so")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, WORKSPACE, UNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:dsa|mla)_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from sparse_attention_12_amd import _build
+        _build.build()
+    l = ctypes.CDLL(LIB)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    l.dsa_index_score.argtypes = [vp, i32, vp, vp, vp, vp, i64, vp]
+    l.dsa_topk.argtypes = [vp, vp, i64, i32, vp, vp, vp, sz, vp]
+    l.dsa_topk_workspace_size.argtypes = [i32, i32, i32]
+    l.dsa_topk_workspace_size.restype = sz
+    l.mla_sparse_attend.argtypes = [vp, i32, vp, vp, vp, i32, ctypes.c_float, vp, i32, vp, vp, sz, vp]
+    l.mla_sparse_attend_workspace_size.argtypes = [i32, i32, i32]
+    l.mla_sparse_attend_workspace_size.restype = sz
+    l.dsa_mla_decode_fused.argtypes = [vp, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, i32,
+                                       ctypes.c_float, vp, vp, sz, vp]
+    l.dsa_mla_decode_fused_workspace_size.argtypes = [i32, i32, i32, i32]
+    l.dsa_mla_decode_fused_workspace_size.restype = sz
+    l.dsa_status_string.restype = ctypes.c_char_p
+    l.dsa_last_error.restype = ctypes.c_char_p
+    return l
+
+
+class Batch(ctypes.Structure):
+    _fields_ = [("nq", ctypes.c_int32), ("nseq", ctypes.c_int32), ("max_len", ctypes.c_int32),
+                ("q_seq", ctypes.c_void_p), ("q_pos", ctypes.c_void_p),
+                ("seq_len", ctypes.c_void_p), ("seq_row0", ctypes.c_void_p)]
+
+
+# stand-in addresses: never dereferenced, because every case below fails validation
+A = 0x10000
+MIS = 0x10004
+
+
+def _batch(nq=2, nseq=2, max_len=100):
+    return Batch(nq, nseq, max_len, A, A, A, A)
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert len(names) == 10, names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.dsa_abi_version() == 1
+    for st in (OK, NULL, SHAPE, DTYPE, ALIGN, WORKSPACE, UNSUPPORTED, -7):
+        assert lib.dsa_status_string(st)
+    assert b"unknown" in lib.dsa_status_string(42)
+
+
+def test_index_score_validation(lib):
+    b = _batch()
+    assert lib.dsa_index_score(None, 1, A, A, A, A, 100, None) == NULL
+    assert lib.dsa_index_score(ctypes.byref(_batch(nseq=0)), 1, A, A, A, A, 100, None) == SHAPE
+    assert lib.dsa_index_score(ctypes.byref(_batch(max_len=0)), 1, A, A, A, A, 100, None) == SHAPE
+    assert lib.dsa_index_score(ctypes.byref(_batch(nq=-1)), 1, A, A, A, A, 100, None) == SHAPE
+    assert lib.dsa_index_score(ctypes.byref(b), 7, A, A, A, A, 100, None) == DTYPE
+    assert lib.dsa_index_score(ctypes.byref(b), 1, None, A, A, A, 100, None) == NULL
+    assert lib.dsa_index_score(ctypes.byref(b), 1, MIS, A, A, A, 100, None) == ALIGN
+    assert lib.dsa_index_score(ctypes.byref(b), 1, A, A, A, None, 100, None) == NULL
+    assert lib.dsa_index_score(ctypes.byref(b), 1, A, A, A, A, 99, None) == SHAPE
+    assert b"ld" in lib.dsa_last_error()
+    nob = Batch(1, 1, 10, None, A, A, A)
+    assert lib.dsa_index_score(ctypes.byref(nob), 1, A, A, A, A, 10, None) == NULL
+    # an empty batch is a no-op
+    assert lib.dsa_index_score(ctypes.byref(_batch(nq=0)), 1, None, None, None, None, 100, None) == OK
+
+
+def test_topk_validation(lib):
+    b = _batch()
+    assert lib.dsa_topk(ctypes.byref(b), A, 100, 0, A, None, None, 0, None) == SHAPE
+    assert lib.dsa_topk(ctypes.byref(b), A, 100, 2049, A, None, None, 0, None) == UNSUPPORTED
+    assert lib.dsa_topk(ctypes.byref(b), None, 100, 8, A, None, None, 0, None) == NULL
+    assert lib.dsa_topk(ctypes.byref(b), A, 100, 8, None, None, None, 0, None) == NULL
+    assert lib.dsa_topk(ctypes.byref(b), A, 50, 8, A, None, None, 0, None) == SHAPE
+    assert lib.dsa_topk(ctypes.byref(_batch(nq=0)), None, 100, 8, None, None, None, 0, None) == OK
+    assert lib.dsa_topk_workspace_size(0, 10, 8) == 0
+
+
+def test_mla_validation(lib):
+    b = _batch()
+    args = lambda **kw: dict(dict(dt=1, q=A, kv=A, idx=A, k=2048, out=A, odt=0, ws=A, wsb=1 << 40), **kw)
+
+    def call(**kw):
+        a = args(**kw)
+        return lib.mla_sparse_attend(ctypes.byref(b), a["dt"], a["q"], a["kv"], a["idx"], a["k"], 0.07,
+                                     a["out"], a["odt"], None, a["ws"], a["wsb"], None)
+
+    assert call(dt=2) == DTYPE
+    assert call(odt=-1) == DTYPE
+    assert call(k=0) == SHAPE
+    assert call(k=4096) == UNSUPPORTED
+    assert call(q=None) == NULL
+    assert call(kv=MIS) == ALIGN
+    assert call(out=None) == NULL
+    assert call(idx=None) == NULL
+    need = lib.mla_sparse_attend_workspace_size(2, 2048, 1)
+    assert need > 0
+    assert call(ws=None, wsb=0) == WORKSPACE
+    assert call(wsb=1024) == WORKSPACE
+    assert call(ws=MIS) == ALIGN
+
+
+def test_fused_validation(lib):
+    b = _batch()
+    tab = (ctypes.c_void_p * 2)(A, A)
+    mis = (ctypes.c_void_p * 2)(A, MIS)
+    need = lib.dsa_mla_decode_fused_workspace_size(2, 100, 2048, 2)
+    assert need >= 2 * 100 * 4 + 2 * 2048 * 4
+
+    def call(n_layers=2, q=tab, kv=tab, out=tab, k=2048, ws=A, wsb=need):
+        c = lambda t: ctypes.cast(t, ctypes.c_void_p) if t is not None else None
+        return lib.dsa_mla_decode_fused(ctypes.byref(b), 1, A, A, A, k, n_layers, c(q), c(kv), c(out), None, 0,
+                                        0.07, None, ws, wsb, None)
+
+    assert call(n_layers=0) == SHAPE
+    assert call(n_layers=17) == UNSUPPORTED
+    assert call(k=3000) == UNSUPPORTED
+    assert call(q=None) == NULL
+    assert call(kv=mis) == ALIGN
+    assert call(ws=None) == WORKSPACE
+    assert call(wsb=need - 1) == WORKSPACE
+    assert call(ws=MIS) == ALIGN

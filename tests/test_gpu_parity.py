@@ -1,0 +1,269 @@
+"""GPU parity of every entry point against the CPU oracle, at sizes the
+oracle finishes in seconds that still span several tiles and ragged tails.
+
+Bars: selected index sets and (integer-input) indexer scores bit-exact;
+attention output max|o - o_ref| <= 1e-4 max|o_ref| (fp32) or 1e-2 max|o_ref|
+(bf16); log-sum-exp within 1e-4 (fp32) or 2e-3 (bf16) absolute.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_attention_12_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+TOL = {"f32": 1e-4, "bf16": 1e-2}
+LSE_TOL = {"f32": 1e-4, "bf16": 2e-3}
+
+
+@pytest.fixture(scope="module")
+def B():
+    assert torch.cuda.is_available(), "a GPU is required"
+    from sparse_attention_12_amd import binding
+    return binding
+
+
+def _batch(B, w, t):
+    return B.Batch(t["q_seq"], t["q_pos"], t["seq_len"], t["seq_row0"], w.max_len)
+
+
+def _assert_rel(got, ref, rel, what):
+    got = np.asarray(got, np.float64)
+    err = np.abs(got - ref).max()
+    scale = np.abs(ref).max()
+    assert err <= rel * scale, f"{what}: max|err| {err:.3e} > {rel} * {scale:.3e}"
+
+
+def _oracle_scores(w, qi):
+    s = int(w.q_seq[qi])
+    n = oracle.n_candidates(int(w.q_pos[qi]), int(w.seq_len[s]))
+    return oracle.index_score(w.widen(w.qI)[qi], w.w[qi], w.widen(w.seq_rows(w.kI, s))[:n])
+
+
+# ----------------------------------------------------------------------------
+# indexer
+# ----------------------------------------------------------------------------
+
+DECODE_LENS = [1, 31, 32, 33, 100, 2047, 2048, 2049, 4097, 9000, 16385]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_index_score_decode_exact(B, dtype):
+    w = wl.make_decode(DECODE_LENS, dtype, 1, seed=21)
+    t = w.to_torch(DEV)
+    ld = w.max_len + 5
+    scores = torch.full((w.nq, ld), float("nan"), device=DEV)
+    B.dsa_index_score(_batch(B, w, t), t["qI"], t["w"], t["kI"], scores)
+    torch.cuda.synchronize()
+    sc = scores.cpu().numpy()
+    for qi, n in enumerate(DECODE_LENS):
+        ref = _oracle_scores(w, qi)
+        assert np.array_equal(sc[qi, :n].astype(np.float64), ref), f"query {qi} (L={n})"
+        assert np.all(np.isnan(sc[qi, n:])), f"query {qi}: columns beyond the candidates were written"
+
+
+@pytest.mark.parametrize("cache,first,nq", [(3000, 2900, 70), (5000, 10, 64), (9000, 8960, 40)])
+def test_index_score_prefill_exact(B, cache, first, nq):
+    w = wl.make_prefill(cache, first, nq, "bf16", seed=22)
+    t = w.to_torch(DEV)
+    scores = torch.full((w.nq, cache), float("nan"), device=DEV)
+    B.dsa_index_score(_batch(B, w, t), t["qI"], t["w"], t["kI"], scores)
+    torch.cuda.synchronize()
+    sc = scores.cpu().numpy()
+    for qi in range(nq):
+        n = min(first + qi + 1, cache)
+        ref = _oracle_scores(w, qi)
+        assert ref.shape[0] == n
+        assert np.array_equal(sc[qi, :n].astype(np.float64), ref), f"query {qi}"
+        assert np.all(np.isnan(sc[qi, n:]))
+
+
+# ----------------------------------------------------------------------------
+# top-k
+# ----------------------------------------------------------------------------
+
+
+def _topk_gpu(B, rows, k, ld=None):
+    """rows: list of float32 score arrays (one query per sequence)."""
+    lens = np.array([len(r) for r in rows], np.int32)
+    L = int(lens.max())
+    ld = ld or L
+    sc = np.zeros((len(rows), ld), np.float32)
+    for i, r in enumerate(rows):
+        sc[i, :len(r)] = r
+    q_seq = torch.arange(len(rows), dtype=torch.int32, device=DEV)
+    batch = B.Batch(q_seq, torch.from_numpy(lens - 1).to(DEV), torch.from_numpy(lens).to(DEV),
+                    torch.zeros(len(rows), dtype=torch.int64, device=DEV), L)
+    idx = torch.full((len(rows), k), -7, dtype=torch.int32, device=DEV)
+    cnt = torch.full((len(rows),), -7, dtype=torch.int32, device=DEV)
+    ws_n = B.dsa_topk_workspace_size(len(rows), L, k)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=DEV) if ws_n else None
+    B.dsa_topk(batch, torch.from_numpy(sc).to(DEV), k, idx, cnt, ws)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), cnt.cpu().numpy()
+
+
+@pytest.mark.parametrize("k", [1, 5, 64, 2048])
+def test_topk_engineered_rows(B, k):
+    rng = np.random.default_rng(23)
+    rows = [
+        rng.integers(0, 50, 3000).astype(np.float32),                 # heavy ties
+        np.zeros(20000, np.float32),                                    # all equal, > LDS candidate cap
+        rng.standard_normal(7777).astype(np.float32),                   # distinct
+        np.where(rng.random(5000) < 0.5, 0.0, -0.0).astype(np.float32),  # signed zeros
+        -np.abs(rng.standard_normal(4100)).astype(np.float32),          # all negative
+        rng.integers(0, 3, 40000).astype(np.float32) * 1000.0,          # three huge tie groups
+        rng.standard_normal(max(1, k - 3)).astype(np.float32),          # fewer candidates than k
+        np.full(k, 5.0, np.float32),                                    # exactly k candidates
+    ]
+    idx, cnt = _topk_gpu(B, rows, k)
+    for i, r in enumerate(rows):
+        ref, m = oracle.topk(r.astype(np.float64), k)
+        assert cnt[i] == m, f"row {i}"
+        assert np.array_equal(idx[i], ref), f"row {i}: selection differs"
+
+
+def test_topk_on_indexer_scores(B):
+    w = wl.make_decode([2048, 2049, 5000, 33000], "bf16", 1, seed=24)
+    t = w.to_torch(DEV)
+    batch = _batch(B, w, t)
+    scores = torch.empty((w.nq, w.max_len), device=DEV)
+    B.dsa_index_score(batch, t["qI"], t["w"], t["kI"], scores)
+    idx = torch.empty((w.nq, 2048), dtype=torch.int32, device=DEV)
+    cnt = torch.empty((w.nq,), dtype=torch.int32, device=DEV)
+    B.dsa_topk(batch, scores, 2048, idx, cnt)
+    torch.cuda.synchronize()
+    for qi in range(w.nq):
+        ref, m = oracle.topk(_oracle_scores(w, qi), 2048)
+        assert int(cnt[qi]) == m
+        assert np.array_equal(idx[qi].cpu().numpy(), ref)
+
+
+def test_topk_nonint_scores_property(B):
+    """Real-valued indexer inputs: fp32 rounding may swap near-ties, so the
+    check is that every kept position scores within a hair of the oracle's
+    threshold and that the count is right."""
+    rng = np.random.default_rng(25)
+    L = 6000
+    qI = rng.standard_normal((1, 32, 128)).astype(np.float32)
+    wv = rng.uniform(0.5, 2.0, (1, 32)).astype(np.float32)
+    kI = rng.standard_normal((L, 128)).astype(np.float32)
+    batch = B.Batch(torch.zeros(1, dtype=torch.int32, device=DEV), torch.tensor([L - 1], dtype=torch.int32, device=DEV),
+                    torch.tensor([L], dtype=torch.int32, device=DEV), torch.zeros(1, dtype=torch.int64, device=DEV), L)
+    scores = torch.empty((1, L), device=DEV)
+    B.dsa_index_score(batch, torch.from_numpy(qI).to(DEV), torch.from_numpy(wv).to(DEV),
+                      torch.from_numpy(kI).to(DEV), scores)
+    idx = torch.empty((1, 2048), dtype=torch.int32, device=DEV)
+    B.dsa_topk(batch, scores, 2048, idx)
+    ref_sc = oracle.index_score(qI[0], wv[0], kI)
+    thr = np.sort(ref_sc)[::-1][2047]
+    got = idx[0].cpu().numpy()
+    assert np.all(got >= 0) and len(set(got.tolist())) == 2048 and np.all(np.diff(got) > 0)
+    assert ref_sc[got].min() >= thr - 1e-4 * np.abs(ref_sc).max()
+
+
+# ----------------------------------------------------------------------------
+# sparse MLA
+# ----------------------------------------------------------------------------
+
+
+def _mla_case(B, dtype, lens, k, nq_pad=0, out_dtype=torch.float32, seed=26):
+    w = wl.make_decode(lens, dtype, 1, seed=seed)
+    t = w.to_torch(DEV)
+    rng = np.random.default_rng(seed + 1)
+    idx = np.full((w.nq, k), -1, np.int32)
+    for qi, n in enumerate(lens):
+        m = min(k, n)
+        chosen = np.sort(rng.choice(n, m, replace=False))
+        idx[qi, :m] = chosen
+        if nq_pad and qi % 2 == 1 and m > 4:   # holes anywhere in the list are skipped
+            idx[qi, 1:4] = -1
+    out = torch.empty((w.nq, 64, 512), dtype=out_dtype, device=DEV)
+    lse = torch.empty((w.nq, 64), device=DEV)
+    ws_n = B.mla_sparse_attend_workspace_size(w.nq, k, 1)
+    ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=DEV)
+    B.mla_sparse_attend(_batch(B, w, t), t["q"][0], t["kv"][0], torch.from_numpy(idx).to(DEV), k, w.tau,
+                        out, lse, ws)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy()
+    l = lse.cpu().numpy()
+    for qi in range(w.nq):
+        sel = idx[qi][idx[qi] >= 0]
+        r_o, r_l = oracle.mla_attend(w.widen(w.q[0])[qi], w.widen(w.seq_rows(w.kv[0], qi)), sel, w.tau)
+        rel = TOL[dtype] if out_dtype == torch.float32 else 1e-2
+        _assert_rel(o[qi], r_o, rel, f"query {qi} output")
+        assert np.abs(l[qi] - r_l).max() <= LSE_TOL[dtype], f"query {qi} lse"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_mla_split_path(B, dtype):
+    # few queries -> the selection is split across workgroups and merged
+    _mla_case(B, dtype, [5, 40, 2048, 3000, 70000], 2048, nq_pad=1)
+
+
+def test_mla_unsplit_path_bf16(B):
+    # enough queries that each runs in one workgroup
+    lens = [2100 + 37 * i for i in range(520)]
+    _mla_case(B, "bf16", lens[:520], 2048, seed=27)
+
+
+@pytest.mark.parametrize("k", [1, 100, 2047])
+def test_mla_small_k(B, k):
+    _mla_case(B, "bf16", [50, 3000], k, seed=28)
+
+
+def test_mla_bf16_output(B):
+    _mla_case(B, "bf16", [3000, 4000], 2048, out_dtype=torch.bfloat16, seed=29)
+
+
+# ----------------------------------------------------------------------------
+# fused decode with a shared selection
+# ----------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("dtype,lens,layers", [
+    ("bf16", [1024, 2048, 2049, 3333, 40000], 4),
+    ("f32", [700, 4096], 2),
+])
+def test_fused_decode(B, dtype, lens, layers):
+    w = wl.make_decode(lens, dtype, layers, seed=30)
+    t = w.to_torch(DEV)
+    outs = [torch.empty((w.nq, 64, 512), device=DEV) for _ in range(layers)]
+    lses = [torch.empty((w.nq, 64), device=DEV) for _ in range(layers)]
+    idx = torch.empty((w.nq, w.k), dtype=torch.int32, device=DEV)
+    ws = torch.empty(B.dsa_mla_decode_fused_workspace_size(w.nq, w.max_len, w.k, layers), dtype=torch.uint8,
+                     device=DEV)
+    B.dsa_mla_decode_fused(_batch(B, w, t), t["qI"], t["w"], t["kI"], w.k, t["q"], t["kv"], outs, w.tau,
+                           lses, idx, ws)
+    torch.cuda.synchronize()
+    first = [o.clone() for o in outs]
+    # run again: results are deterministic
+    B.dsa_mla_decode_fused(_batch(B, w, t), t["qI"], t["w"], t["kI"], w.k, t["q"], t["kv"], outs, w.tau,
+                           lses, idx, ws)
+    torch.cuda.synchronize()
+    for a, b in zip(first, outs):
+        assert torch.equal(a, b)
+    idx_h = idx.cpu().numpy()
+    for qi, n in enumerate(lens):
+        r_idx, m, r_o, r_l = oracle.decode_query(
+            w.widen(w.qI)[qi], w.w[qi], w.widen(w.seq_rows(w.kI, qi)), [w.widen(x)[qi] for x in w.q],
+            [w.widen(w.seq_rows(x, qi)) for x in w.kv], n, w.k, w.tau)
+        assert np.array_equal(idx_h[qi], r_idx), f"query {qi}: selection"
+        for l in range(layers):
+            _assert_rel(outs[l][qi].cpu().numpy(), r_o[l], TOL[dtype], f"query {qi} layer {l}")
+            assert np.abs(lses[l][qi].cpu().numpy() - r_l[l]).max() <= LSE_TOL[dtype]
+
+
+def test_empty_batch_is_noop(B):
+    z = torch.zeros(0, dtype=torch.int32, device=DEV)
+    batch = B.Batch(z, z, torch.ones(1, dtype=torch.int32, device=DEV), torch.zeros(1, dtype=torch.int64, device=DEV), 1)
+    scores = torch.empty((0, 1), device=DEV)
+    B.dsa_index_score(batch, torch.empty((0, 32, 128), dtype=torch.bfloat16, device=DEV),
+                      torch.empty((0, 32), device=DEV), torch.empty((1, 128), dtype=torch.bfloat16, device=DEV),
+                      scores, ld=1)
+    torch.cuda.synchronize()
