@@ -58,31 +58,192 @@ __device__ inline void store_out4(const MlaParams& p, int layer, int64_t off, f3
 // bf16 split kernel
 // ---------------------------------------------------------------------------
 constexpr int MLA_THREADS = 256;
-constexpr int MLA_TILE = 32;
-constexpr int MLA_RS = D * 2 + 16;               // LDS row stride in bytes (padded)
-constexpr int MLA_CHUNKS = D * 2 / 16;           // 72 chunks of 16 B per row
-constexpr int MLA_LOADS = MLA_TILE * MLA_CHUNKS / MLA_THREADS;  // 9
+constexpr int MLA_TILE = 32;                    // positions per tile
+constexpr int MLA_ROWB = D * 2;                 // 1,152 bytes per bf16 row
+constexpr int MLA_CHUNKS = MLA_ROWB / 16;       // 72 chunks of 16 B per row
+constexpr int MLA_TILEB = MLA_TILE * MLA_ROWB;  // 36,864 bytes per tile
+constexpr int MLA_LOADS = MLA_TILE * MLA_CHUNKS / MLA_THREADS;  // 9 chunks per thread
+constexpr int MLA_NBUF = 2;
+constexpr int MLA_SPLIT_MAX = KMAX;
 static_assert(MLA_TILE * MLA_CHUNKS == MLA_LOADS * MLA_THREADS, "tile staging must be exact");
-constexpr float MLA_RESCALE_SLACK = 8.0f;        // log2 units
+constexpr float MLA_RESCALE_SLACK = 8.0f;       // log2 units
 
-__global__ __launch_bounds__(MLA_THREADS) void mla_bf16_kernel(MlaParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t tile[MLA_TILE * MLA_RS];
-  __shared__ int vflag[MLA_TILE];
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS tile layout: row r occupies bytes [r*1152, (r+1)*1152); its logical
+// 16-byte chunk c is stored at chunk position c ^ (r & 7), which spreads the
+// column reads of consecutive rows over distinct banks.
+__device__ inline int swz(int row, int chunk) { return row * MLA_ROWB + ((chunk ^ (row & 7)) << 4); }
+
+struct MlaTileState {
+  f32x4 o[DC / 16];
+  float m_run;
+  float l_part;
+};
+
+// Gather tile t of the selection straight into LDS (16 bytes per lane, in
+// lane order: the wave-uniform base goes to M0).
+__device__ inline void mla_issue(uint8_t* buf, const uint16_t* kv, const int* sel_l, int nent, int t, int tid,
+                                 int wave_u) {
+#pragma unroll
+  for (int i = 0; i < MLA_LOADS; ++i) {
+    const int slot = i * MLA_THREADS + tid;
+    const int row = slot / MLA_CHUNKS;
+    const int pc = slot - row * MLA_CHUNKS;
+    const int j = t * MLA_TILE + row;
+    const int pos = j < nent ? sel_l[j] : -1;
+    const uint16_t* src = kv + (int64_t)(pos >= 0 ? pos : 0) * D + ((pc ^ (row & 7)) << 3);
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(buf + (i * MLA_THREADS + wave_u * 64) * 16),
+                                     16, 0, 0);
+  }
+}
+
+// One tile: S^T = K.Q^T, online softmax, O^T += V^T.P^T.
+__device__ inline void mla_tile(MlaTileState& st, const uint8_t* tile, const bf16x8 (&qf)[D / 32],
+                                const int* sel_l, int nent, int t0, int n16, int g, float scale_log2) {
+  // Row r's chunk 4t+g sits at 8*(t/2) + ((4*(t%2) + g) ^ (r & 7)): two base
+  // addresses per row plus an immediate 128*(t/2).  Loads run two steps
+  // ahead of the MFMAs; each block keeps two accumulator chains.
+  const uint8_t* ev[2];
+  const uint8_t* od[2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int row = 16 * mb + n16;
+    ev[mb] = tile + row * MLA_ROWB + ((g ^ (row & 7)) << 4);
+    od[mb] = tile + row * MLA_ROWB + (((4 | g) ^ (row & 7)) << 4);
+  }
+  auto kfrag = [&](int mb, int t) -> u32x4 {
+    return *(const u32x4*)(((t & 1) ? od[mb] : ev[mb]) + (t >> 1) * 128);
+  };
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) acc[mb][0] = acc[mb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 ring[3][2];
+  ring[0][0] = kfrag(0, 0);
+  ring[0][1] = kfrag(1, 0);
+  ring[1][0] = kfrag(0, 1);
+  ring[1][1] = kfrag(1, 1);
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) {
+    if (t + 2 < D / 32) {
+      ring[(t + 2) % 3][0] = kfrag(0, t + 2);
+      ring[(t + 2) % 3][1] = kfrag(1, t + 2);
+    }
+    acc[0][t & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ring[t % 3][0]), qf[t], acc[0][t & 1], 0, 0, 0);
+    acc[1][t & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ring[t % 3][1]), qf[t], acc[1][t & 1], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMAs
+  }
+  f32x4 s[2];
+  s[0] = acc[0][0] + acc[0][1];
+  s[1] = acc[1][0] + acc[1][1];
+  __builtin_amdgcn_sched_barrier(0);
+  // lane holds one head and positions 16*mb + 4g + i
+  float x[8];
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = t0 + 16 * mb + 4 * g + i;
+      const bool ok = j < nent && sel_l[j] >= 0;
+      const float v = ok ? s[mb][i] * scale_log2 : -INFINITY;
+      x[mb * 4 + i] = v;
+      tmax = fmaxf(tmax, v);
+    }
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  const bool resc = tmax > st.m_run + MLA_RESCALE_SLACK;
+  if (__any(resc)) {
+    const float alpha = resc ? exp2f(st.m_run - tmax) : 1.0f;
+    if (resc) st.m_run = tmax;
+    st.l_part *= alpha;
+#pragma unroll
+    for (int db = 0; db < DC / 16; ++db) st.o[db] *= alpha;
+  }
+  float pv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    pv[e] = (x[e] == -INFINITY) ? 0.0f : exp2f(x[e] - st.m_run);
+    st.l_part += pv[e];
+  }
+  u32x4 pk;
+  pk[0] = pack_bf16x2(pv[0], pv[1]);
+  pk[1] = pack_bf16x2(pv[2], pv[3]);
+  pk[2] = pack_bf16x2(pv[4], pv[5]);
+  pk[3] = pack_bf16x2(pv[6], pv[7]);
+  const bf16x8 pb = as_bf16x8(pk);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // O^T += V_tile^T . P^T.  k-slot e of lane group g is tile row
+  // (e < 4 ? 4g + e : 16 + 4g + e - 4).  A transposing LDS read gives lane
+  // i of a 16-lane group element i%4 of source lane 4j + i/4, so source
+  // lane s points at row 4g + s/4 (+16) and latent column 16db + 4(s%4).
+  // Column 16db + sdim lies in chunk 2db + sdim/8 = 8*(db/4) + (2*(db%4) + sdim/8):
+  // four base addresses per source row plus an immediate 128*(db/4).
+  const int srow0 = 4 * g + (n16 >> 2);
+  const int srow1 = srow0 + 16;
+  const int sdim = 4 * (n16 & 3);
+  const int c0 = sdim >> 3;
+  const int boff = (sdim & 7) << 1;
+  const uint8_t* b0[4];
+  const uint8_t* b1[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    b0[u] = tile + srow0 * MLA_ROWB + (((2 * u + c0) ^ (srow0 & 7)) << 4) + boff;
+    b1[u] = tile + srow1 * MLA_ROWB + (((2 * u + c0) ^ (srow1 & 7)) << 4) + boff;
+  }
+  auto vfrag = [&](int db) -> bf16x8 {
+    const int u = db & 3;
+    const int imm = (db >> 2) * 128;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b0[u] + imm));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b1[u] + imm));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  bf16x8 vr[4];
+  vr[0] = vfrag(0);
+  vr[1] = vfrag(1);
+  vr[2] = vfrag(2);
+#pragma unroll
+  for (int db = 0; db < DC / 16; ++db) {
+    if (db + 3 < DC / 16) vr[(db + 3) & 3] = vfrag(db + 3);
+    st.o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vr[db & 3], pb, st.o[db], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);  // 2 LDS transpose reads
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // 1 MFMA
+  }
+}
+
+__global__ __launch_bounds__(MLA_THREADS, 1) void mla_bf16_kernel(MlaParams p) {
+  // two distinct arrays, so that reads of one tile are known not to alias
+  // the asynchronous gather into the other
+  __shared__ __attribute__((aligned(16))) uint8_t tile0[MLA_TILEB];
+  __shared__ __attribute__((aligned(16))) uint8_t tile1[MLA_TILEB];
+  __shared__ int sel_l[MLA_SPLIT_MAX];
   const int split = blockIdx.x;
   const int q = blockIdx.y;
   const int layer = blockIdx.z;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15;
   const int g = lane >> 4;
   const QueryRange r = query_range(p.b, q);
   const int j_begin = split * p.split_len;
-  const int j_end = min(j_begin + p.split_len, p.k);
-  const int ntiles = (r.n > 0 && j_end > j_begin) ? (j_end - j_begin + MLA_TILE - 1) / MLA_TILE : 0;
-  const int head = wave * 16 + n16;
+  const int nent = max(0, min(j_begin + p.split_len, p.k) - j_begin);
+  const int ntiles = r.n > 0 ? (nent + MLA_TILE - 1) / MLA_TILE : 0;
+  const int head = wave_u * 16 + n16;
 
-  // Q_w^T as the B operand: head `head`, contraction slots t*32 + 8g + [0,8).
+  // this split's selected positions; entries outside [0, n) become -1
+  {
+    const int32_t* sel = p.idx + (int64_t)q * p.k + j_begin;
+    for (int j = tid; j < nent; j += MLA_THREADS) {
+      const int pos = sel[j];
+      sel_l[j] = (pos >= 0 && pos < r.n) ? pos : -1;
+    }
+  }
+  // Q_w^T as the B operand: head `head`, contraction slots t*32 + 8g + [0,8)
   bf16x8 qf[D / 32];
   {
     const uint16_t* qp = (const uint16_t*)p.L.q[layer] + ((int64_t)q * H + head) * D + g * 8;
@@ -90,124 +251,43 @@ __global__ __launch_bounds__(MLA_THREADS) void mla_bf16_kernel(MlaParams p) {
     for (int t = 0; t < D / 32; ++t) qf[t] = as_bf16x8(load16(qp + t * 32));
   }
   const uint16_t* kv = (const uint16_t*)p.L.kv[layer] + r.row0 * D;
-  const int32_t* sel = p.idx + (int64_t)q * p.k;
-
-  f32x4 o[DC / 16];
+  MlaTileState st;
 #pragma unroll
-  for (int db = 0; db < DC / 16; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;
-  float l_part = 0.0f;
+  for (int db = 0; db < DC / 16; ++db) st.o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m_run = -INFINITY;
+  st.l_part = 0.0f;
+  __syncthreads();
 
-  u32x4 pre[MLA_LOADS];
-  int pre_ok[MLA_LOADS];
-  auto issue = [&](int j0) {
-#pragma unroll
-    for (int i = 0; i < MLA_LOADS; ++i) {
-      const int c = i * MLA_THREADS + tid;
-      const int rr = c / MLA_CHUNKS;
-      const int ch = c - rr * MLA_CHUNKS;
-      const int j = j0 + rr;
-      const int pos = j < j_end ? sel[j] : -1;
-      const bool ok = pos >= 0 && pos < r.n;
-      pre_ok[i] = ok;
-      pre[i] = load16_nt(kv + (int64_t)(ok ? pos : 0) * D + ch * 8);
-    }
-  };
-  if (ntiles > 0) issue(j_begin);
-
-  for (int it = 0; it < ntiles; ++it) {
+  if (ntiles > 0) mla_issue(tile0, kv, sel_l, nent, 0, tid, wave_u);
+  for (int it = 0; it < ntiles; it += 2) {
+    __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): this thread's part of tile `it` landed
+    __syncthreads();                     // every part landed; the other buffer is free
+    if (it + 1 < ntiles) mla_issue(tile1, kv, sel_l, nent, it + 1, tid, wave_u);
+    mla_tile(st, tile0, qf, sel_l, nent, it * MLA_TILE, n16, g, p.scale_log2);
+    if (it + 1 >= ntiles) break;
+    __builtin_amdgcn_s_waitcnt(0x3F70);
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < MLA_LOADS; ++i) {
-      const int c = i * MLA_THREADS + tid;
-      const int rr = c / MLA_CHUNKS;
-      const int ch = c - rr * MLA_CHUNKS;
-      *(u32x4*)(tile + rr * MLA_RS + ch * 16) = pre[i];
-      if (ch == 0) vflag[rr] = pre_ok[i];
-    }
-    __syncthreads();
-    if (it + 1 < ntiles) issue(j_begin + (it + 1) * MLA_TILE);
-
-    // S^T = K_tile . Q_w^T : two 16-position blocks
-    f32x4 s[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      s[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint8_t* rowp = tile + (16 * mb + n16) * MLA_RS + g * 16;
-#pragma unroll
-      for (int t = 0; t < D / 32; ++t)
-        s[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(*(const u32x4*)(rowp + t * 64)), qf[t],
-                                                        s[mb], 0, 0, 0);
-    }
-    // lane holds head `head`, positions 16*mb + 4g + i
-    float x[8];
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool ok = vflag[16 * mb + 4 * g + i] != 0;
-        const float v = ok ? s[mb][i] * p.scale_log2 : -INFINITY;
-        x[mb * 4 + i] = v;
-        tmax = fmaxf(tmax, v);
-      }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const bool resc = tmax > m_run + MLA_RESCALE_SLACK;
-    if (__any(resc)) {
-      const float alpha = resc ? exp2f(m_run - tmax) : 1.0f;
-      if (resc) m_run = tmax;
-      l_part *= alpha;
-#pragma unroll
-      for (int db = 0; db < DC / 16; ++db) o[db] *= alpha;
-    }
-    float pv[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      pv[e] = (x[e] == -INFINITY) ? 0.0f : exp2f(x[e] - m_run);
-      l_part += pv[e];
-    }
-    u32x4 pk;
-    pk[0] = pack_bf16x2(pv[0], pv[1]);
-    pk[1] = pack_bf16x2(pv[2], pv[3]);
-    pk[2] = pack_bf16x2(pv[4], pv[5]);
-    pk[3] = pack_bf16x2(pv[6], pv[7]);
-    const bf16x8 pb = as_bf16x8(pk);
-
-    // O^T += V_tile^T . P^T ; k-slot e of lane group g is tile row rowsel(e)
-    const uint8_t* vb = tile + n16 * 2;
-#pragma unroll
-    for (int db = 0; db < DC / 16; ++db) {
-      u32x4 va;
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const int ea = 2 * e2, eb = 2 * e2 + 1;
-        const int ra = (ea < 4) ? (4 * g + ea) : (16 + 4 * g + ea - 4);
-        const int rb = (eb < 4) ? (4 * g + eb) : (16 + 4 * g + eb - 4);
-        const uint32_t lo = *(const uint16_t*)(vb + ra * MLA_RS + db * 32);
-        const uint32_t hi = *(const uint16_t*)(vb + rb * MLA_RS + db * 32);
-        va[e2] = lo | (hi << 16);
-      }
-      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), pb, o[db], 0, 0, 0);
-    }
+    if (it + 2 < ntiles) mla_issue(tile0, kv, sel_l, nent, it + 2, tid, wave_u);
+    mla_tile(st, tile1, qf, sel_l, nent, (it + 1) * MLA_TILE, n16, g, p.scale_log2);
   }
 
+  float l_part = st.l_part;
   l_part += __shfl_xor(l_part, 16);
   l_part += __shfl_xor(l_part, 32);
   const int64_t qh = (int64_t)q * H + head;
   if (p.nsplit == 1) {
     const float inv = l_part > 0.0f ? 1.0f / l_part : 0.0f;
 #pragma unroll
-    for (int db = 0; db < DC / 16; ++db) store_out4(p, layer, qh * DC + db * 16 + 4 * g, o[db] * inv);
+    for (int db = 0; db < DC / 16; ++db) store_out4(p, layer, qh * DC + db * 16 + 4 * g, st.o[db] * inv);
     if (g == 0 && p.L.lse[layer])
-      p.L.lse[layer][qh] = l_part > 0.0f ? (m_run + log2f(l_part)) * LN2 : -INFINITY;
+      p.L.lse[layer][qh] = l_part > 0.0f ? (st.m_run + log2f(l_part)) * LN2 : -INFINITY;
   } else {
     const int64_t slot = ((int64_t)split * p.n_layers + layer) * p.b.nq * H + qh;
     float* acc = p.part_acc + slot * DC;
 #pragma unroll
-    for (int db = 0; db < DC / 16; ++db) *(f32x4*)(acc + db * 16 + 4 * g) = o[db];
+    for (int db = 0; db < DC / 16; ++db) *(f32x4*)(acc + db * 16 + 4 * g) = st.o[db];
     if (g == 0) {
-      p.part_ml[slot * 2 + 0] = l_part > 0.0f ? m_run : -INFINITY;
+      p.part_ml[slot * 2 + 0] = l_part > 0.0f ? st.m_run : -INFINITY;
       p.part_ml[slot * 2 + 1] = l_part;
     }
   }
@@ -300,13 +380,14 @@ __global__ __launch_bounds__(MLA32_THREADS) void mla_f32_kernel(MlaParams p) {
 // log-sum-exp merge of the splits of each (query, layer)
 // ---------------------------------------------------------------------------
 constexpr int CMB_THREADS = 256;
+constexpr int CMB_HEADS = 8;   // heads per workgroup: 32 threads x 16 values each
 
 __global__ __launch_bounds__(CMB_THREADS) void mla_combine(MlaParams p) {
   const int q = blockIdx.x;
   const int layer = blockIdx.y;
-  const int head = threadIdx.x >> 2;
-  const int part = threadIdx.x & 3;
-  constexpr int VS = DC / 4;
+  const int head = blockIdx.z * CMB_HEADS + (threadIdx.x >> 5);
+  const int part = threadIdx.x & 31;
+  constexpr int VS = DC / 32;   // 16 value dims per thread
   const int64_t qh = (int64_t)q * H + head;
   const int64_t stride = (int64_t)p.n_layers * p.b.nq * H;  // slots between splits
   const int64_t slot0 = (int64_t)layer * p.b.nq * H + qh;
@@ -323,21 +404,21 @@ __global__ __launch_bounds__(CMB_THREADS) void mla_combine(MlaParams p) {
       if (mi == -INFINITY) continue;
       const float wgt = exp2f(mi - mx);
       den += wgt * p.part_ml[slot * 2 + 1];
-      const f32x4* pa = (const f32x4*)(p.part_acc + slot * DC + part * VS);
+      const f32x4* pa = (const f32x4*)(p.part_acc + slot * DC) + part;
 #pragma unroll
-      for (int v = 0; v < VS / 4; ++v) acc[v] += wgt * pa[v];
+      for (int v = 0; v < VS / 4; ++v) acc[v] += wgt * pa[32 * v];
     }
   }
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;
 #pragma unroll
-  for (int v = 0; v < VS / 4; ++v) store_out4(p, layer, qh * DC + part * VS + 4 * v, acc[v] * inv);
+  for (int v = 0; v < VS / 4; ++v) store_out4(p, layer, qh * DC + 4 * (part + 32 * v), acc[v] * inv);
   if (part == 0 && p.L.lse[layer]) p.L.lse[layer][qh] = den > 0.0f ? (mx + log2f(den)) * LN2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-constexpr int MLA_TARGET_BLOCKS = 512;  // two rounds of workgroups on 256 compute units
+constexpr int MLA_TARGET_BLOCKS = 256;  // one workgroup per compute unit
 
 int mla_num_splits(int dtype, int nq, int k, int n_layers) {
   const int tile = dtype == 0 ? MLA32_TILE : MLA_TILE;
@@ -392,7 +473,7 @@ hipError_t launch_mla(const BatchDev& b, int dtype, const MlaLayers& layers, int
     hipLaunchKernelGGL(mla_bf16_kernel, grid, dim3(MLA_THREADS), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
-  hipLaunchKernelGGL(mla_combine, dim3(b.nq, n_layers), dim3(CMB_THREADS), 0, st, p);
+  hipLaunchKernelGGL(mla_combine, dim3(b.nq, n_layers, H / CMB_HEADS), dim3(CMB_THREADS), 0, st, p);
   return hipGetLastError();
 }
 
