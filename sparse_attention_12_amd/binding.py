@@ -90,6 +90,14 @@ def _dt(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+def _workspace(ws, nbytes: int, like: torch.Tensor):
+    """The caller's workspace, or a fresh torch allocation of the size the
+    library asked for (PyTorch is the device-memory provider)."""
+    if ws is not None or nbytes == 0:
+        return ws
+    return torch.empty(nbytes, dtype=torch.uint8, device=like.device)
+
+
 def _stream(stream) -> ctypes.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -133,6 +141,7 @@ def dsa_topk_workspace_size(nq: int, max_len: int, k: int) -> int:
 def dsa_topk(batch: Batch, scores, k: int, idx, count=None, ws=None, ld: Optional[int] = None,
              stream=None):
     ld = scores.shape[-1] if ld is None else ld
+    ws = _workspace(ws, dsa_topk_workspace_size(batch.nq, batch.max_len, k), scores)
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.dsa_topk(batch.ref, _p(scores), ld, k, _p(idx), _p(count), _p(ws), wsb, _stream(stream)),
            "dsa_topk")
@@ -145,6 +154,7 @@ def mla_sparse_attend_workspace_size(nq: int, k: int, n_layers: int = 1) -> int:
 
 def mla_sparse_attend(batch: Batch, q, kv, idx, k: int, scale: float, out, lse=None, ws=None,
                       stream=None):
+    ws = _workspace(ws, mla_sparse_attend_workspace_size(batch.nq, k, 1), q)
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.mla_sparse_attend(batch.ref, _dt(q), _p(q), _p(kv), _p(idx), k, scale, _p(out), _dt(out),
                                  _p(lse), _p(ws), wsb, _stream(stream)), "mla_sparse_attend")
@@ -164,6 +174,7 @@ def dsa_mla_decode_fused(batch: Batch, q_idx, w_idx, k_idx, k: int, q_l: Sequenc
     kva = arr(*[t.data_ptr() for t in kv_l])
     oa = arr(*[t.data_ptr() for t in out_l])
     la = None if lse_l is None else arr(*[(0 if t is None else t.data_ptr()) for t in lse_l])
+    ws = _workspace(ws, dsa_mla_decode_fused_workspace_size(batch.nq, batch.max_len, k, n), q_idx)
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     cv = lambda a: None if a is None else ctypes.cast(a, ctypes.c_void_p)
     _check(lib.dsa_mla_decode_fused(batch.ref, _dt(q_idx), _p(q_idx), _p(w_idx), _p(k_idx), k, n,

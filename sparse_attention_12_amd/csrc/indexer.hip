@@ -25,7 +25,11 @@ namespace dsa {
 constexpr int IDX_DEC_THREADS = 256;
 constexpr int IDX_DEC_WAVES = IDX_DEC_THREADS / 64;
 constexpr int IDX_DEC_STEP = 32;       // keys per MFMA step and wave
-constexpr int IDX_DEC_CHUNK = 4096;    // keys per workgroup
+constexpr int IDX_DEC_CHUNK = 2048;    // keys per workgroup
+
+struct KeyTile {
+  u32x4 v[8];
+};
 
 __global__ __launch_bounds__(IDX_DEC_THREADS) void idx_decode_bf16(
     BatchDev b, const uint16_t* __restrict__ qI, const float* __restrict__ w,
@@ -52,38 +56,45 @@ __global__ __launch_bounds__(IDX_DEC_THREADS) void idx_decode_bf16(
 
   const uint16_t* kb = kI + r.row0 * DI + half * 8;
   float* out = scores + (int64_t)q * ld;
-  const int last = r.n - 1;
+  const int last = end - 1;
+  constexpr int WSTEP = IDX_DEC_WAVES * IDX_DEC_STEP;
 
-  int key0 = base + wave * IDX_DEC_STEP;
-  if (key0 >= end) return;
-  u32x4 cur[8], nxt[8];
-  {
-    const uint16_t* p = kb + (int64_t)min(key0 + col, last) * DI;
+  // Keys past the chunk end re-read the chunk's last row (a cache hit), so
+  // every load is unconditional and three tiles stay in flight.
+  auto load = [&](KeyTile& kt, int k0) {
+    const uint16_t* p = kb + (int64_t)min(k0 + col, last) * DI;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) cur[t] = load16_nt(p + t * 16);
-  }
-  while (true) {
-    const int nkey0 = key0 + IDX_DEC_WAVES * IDX_DEC_STEP;
-    const bool more = nkey0 < end;
-    if (more) {
-      const uint16_t* p = kb + (int64_t)min(nkey0 + col, last) * DI;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) nxt[t] = load16_nt(p + t * 16);
-    }
+    for (int t = 0; t < 8; ++t) kt.v[t] = load16_nt(p + t * 16);
+  };
+  auto score = [&](const KeyTile& kt, int k0) {
     f32x16 acc = {};
 #pragma unroll
     for (int t = 0; t < 8; ++t)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t], as_bf16x8(cur[t]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t], as_bf16x8(kt.v[t]), acc, 0, 0, 0);
     float part = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) part = fmaf(wr[i], fmaxf(acc[i], 0.0f), part);
     part += __shfl_xor(part, 32);
-    const int key = key0 + col;
+    const int key = k0 + col;
     if (half == 0 && key < end) out[key] = part;
-    if (!more) break;
-    key0 = nkey0;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) cur[t] = nxt[t];
+  };
+
+  int k0 = base + wave * IDX_DEC_STEP;
+  if (k0 >= end) return;
+  KeyTile t0, t1, t2;
+  load(t0, k0);
+  load(t1, k0 + WSTEP);
+  while (true) {
+    load(t2, k0 + 2 * WSTEP);
+    score(t0, k0);
+    if (k0 + WSTEP >= end) break;
+    load(t0, k0 + 3 * WSTEP);
+    score(t1, k0 + WSTEP);
+    if (k0 + 2 * WSTEP >= end) break;
+    load(t1, k0 + 4 * WSTEP);
+    score(t2, k0 + 2 * WSTEP);
+    k0 += 3 * WSTEP;
+    if (k0 >= end) break;
   }
 }
 

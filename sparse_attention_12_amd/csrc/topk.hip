@@ -2,19 +2,22 @@
 // to look": the indexer keeps the best 2,048 positions per query).
 //
 // The kept set is the first min(k, n) positions under (score descending,
-// position ascending).  Each position gets a unique 64-bit key
-//   key = orderable(score) << 32 | (2^32 - 1 - position)
-// so the selection is "the k largest keys" and a radix select needs no
-// separate tie handling.  One 1024-thread workgroup per query:
-//   1. LDS histogram of the top 12 bits of every candidate's key,
-//   2. find the bucket holding the k-th key; positions in higher buckets are
-//      kept outright, positions in that bucket become candidates in LDS,
-//   3. radix levels of 11 bits over the candidates' remaining 52 key bits
-//      until the threshold key is fixed (usually two levels),
-//   4. the kept positions are sorted ascending in LDS and written out.
-// If the threshold bucket holds more candidates than LDS takes (e.g. many
-// equal scores), step 3 runs over the score row itself and step 4 becomes
-// an ordered compaction of the row.
+// position ascending), emitted in ascending position order.  Scores are
+// mapped to unsigned keys u whose order is the score order (-0.0 = +0.0).
+//
+// Radix select, ordered throughout so that no sort is ever needed:
+//   1. histogram of the top 12 bits of u  ->  bucket d1 holding the k-th key;
+//   2. every position whose top 12 bits are >= d1 is copied, in position
+//      order, into a candidate list (ordered compaction with block scans);
+//   3. two more levels of 10 bits over the candidates of bucket d1 fix the
+//      k-th key T exactly; with `need` positions still to take at T,
+//   4. one ordered pass keeps u > T, and u == T while fewer than `need`
+//      earlier positions with u == T were kept (lower position wins ties).
+// Long rows with few queries (decode) split steps 1-2 over many workgroups
+// (per-chunk lists, concatenated in chunk order); many rows (prefill) run
+// one workgroup per row.  If the candidate list would not fit in LDS (for
+// instance every score equal), a row-streaming fallback selects with
+// 64-bit (u, position) keys and compacts the row itself.
 #include "dsa_common.h"
 #include "kernels.h"
 
@@ -24,44 +27,36 @@ constexpr int TK_THREADS = 1024;
 constexpr int TK_WAVES = TK_THREADS / 64;
 constexpr int TK_BITS1 = 12;
 constexpr int TK_BINS1 = 1 << TK_BITS1;
-constexpr int TK_LEVEL_BITS = 11;
-constexpr int TK_CAP = 8192;  // threshold-bucket candidates held in LDS
+constexpr int TK_SHIFT1 = 32 - TK_BITS1;
+constexpr int TK_FCAP = 12288;          // candidate entries held in LDS
+constexpr int TK_CHUNK = 8192;          // scores per workgroup in the split path
+constexpr int TK_ROWS_SPLIT_MAX = 255;  // batches with more rows use one workgroup per row
+constexpr int TK_LEVEL_BITS = 11;       // fallback levels over 64-bit keys
 
-struct TopkShared {
-  uint32_t hist[TK_BINS1];
-  uint32_t ckey[TK_CAP];
-  int32_t cpos[TK_CAP];
-  int32_t sel[KMAX];
-  uint32_t wsum[TK_WAVES];
-  uint32_t nsel;
-  uint32_t ncand;
-  int digit;
-  uint32_t above;
-};
-
-// Exclusive prefix sum over the 1024 threads (thread order); *total gets
-// the sum.  Contains barriers: every thread of the block must call it.
+// ---------------------------------------------------------------------------
+// block-wide helpers (1024 threads; every thread must call them)
+// ---------------------------------------------------------------------------
 __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   uint32_t x = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    uint32_t y = __shfl_up(x, o);
+    const uint32_t y = __shfl_up(x, o);
     if (lane >= o) x += y;
   }
   if (lane == 63) wsum[wave] = x;
   __syncthreads();
   if (wave == 0) {
-    uint32_t s = lane < TK_WAVES ? wsum[lane] : 0u;
+    const uint32_t s = lane < TK_WAVES ? wsum[lane] : 0u;
     uint32_t t = s;
 #pragma unroll
     for (int o = 1; o < TK_WAVES; o <<= 1) {
-      uint32_t y = __shfl_up(t, o);
+      const uint32_t y = __shfl_up(t, o);
       if (lane >= o) t += y;
     }
-    if (lane < TK_WAVES) wsum[lane] = t - s;  // exclusive wave offsets
-    if (lane == TK_WAVES - 1) wsum[TK_WAVES - 1] = t - s, *total = t;
+    if (lane < TK_WAVES) wsum[lane] = t - s;
+    if (lane == TK_WAVES - 1) *total = t;
   }
   __syncthreads();
   const uint32_t res = wsum[wave] + x - v;
@@ -69,38 +64,194 @@ __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t* t
   return res;
 }
 
-// Finds the bucket d such that fewer than `need` entries lie in buckets
-// above d and at least `need` lie in d or above.  Thread 0 covers the
-// highest buckets.  Result in sm.digit / sm.above (count strictly above).
-__device__ void find_bucket(TopkShared& sm, int nbins, uint32_t need) {
+struct ScanShared {
+  uint32_t wsum[TK_WAVES];
+  uint32_t total;
+  int digit;
+  uint32_t above;
+};
+
+// Bucket d of hist[0, nbins) with fewer than `need` entries above it and at
+// least `need` in d or above (thread 0 covers the highest buckets).
+__device__ void find_bucket(const uint32_t* hist, int nbins, uint32_t need, ScanShared& ss, int* digit,
+                            uint32_t* above) {
+  if (threadIdx.x == 0) {
+    ss.digit = 0;
+    ss.above = 0;
+  }
   const int per = (nbins + TK_THREADS - 1) / TK_THREADS;
   const int hi = nbins - (int)threadIdx.x * per;
   const int lo = max(hi - per, 0);
   uint32_t local = 0;
-  for (int b = lo; b < hi; ++b) local += sm.hist[b];
-  uint32_t total;
-  __shared__ uint32_t scan_total;
-  uint32_t run = block_exclusive_scan(local, sm.wsum, &scan_total);
+  for (int b = lo; b < hi; ++b) local += hist[b];
+  uint32_t run = block_exclusive_scan(local, ss.wsum, &ss.total);
   for (int b = hi - 1; b >= lo; --b) {
-    const uint32_t c = sm.hist[b];
+    const uint32_t c = hist[b];
     if (run < need && run + c >= need) {
-      sm.digit = b;
-      sm.above = run;
+      ss.digit = b;
+      ss.above = run;
     }
     run += c;
   }
-  (void)total;
+  __syncthreads();
+  *digit = ss.digit;
+  *above = ss.above;
   __syncthreads();
 }
 
-__device__ inline uint64_t row_key(const float* row, int s) {
-  return select_key(score_key(row[s]), s);
+// ---------------------------------------------------------------------------
+// finalize from an ordered candidate list held in LDS
+// ---------------------------------------------------------------------------
+struct ListShared {
+  uint32_t ukey[TK_FCAP];
+  int32_t pos[TK_FCAP];
+  uint32_t hist[1 << 10];
+  ScanShared ss;
+};
+
+// The list holds, in ascending position order, every position whose top 12
+// key bits are >= d1 (`total` entries, `need` of bucket d1 still to take).
+// Writes the kept positions in order to out[0, k).
+__device__ void finalize_list(ListShared& sm, int total, uint32_t d1, uint32_t need, int32_t* out) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = d1;
+  int plen = TK_BITS1;
+  while (plen < 32) {
+    const int bits = 10;
+    const int shift = 32 - plen - bits;
+    for (int i = tid; i < (1 << bits); i += TK_THREADS) sm.hist[i] = 0;
+    __syncthreads();
+    for (int e = tid; e < total; e += TK_THREADS) {
+      const uint32_t u = sm.ukey[e];
+      if ((u >> (32 - plen)) == prefix) atomicAdd(&sm.hist[(u >> shift) & ((1u << bits) - 1)], 1u);
+    }
+    __syncthreads();
+    int d;
+    uint32_t above;
+    find_bucket(sm.hist, 1 << bits, need, sm.ss, &d, &above);
+    need -= above;
+    const uint32_t cnt = sm.hist[d];
+    prefix = (prefix << bits) | (uint32_t)d;
+    plen += bits;
+    __syncthreads();
+    if (cnt == need) break;
+  }
+  const int s = 32 - plen;
+  // thread t owns the contiguous entries [t*per, (t+1)*per)
+  const int per = (total + TK_THREADS - 1) / TK_THREADS;
+  const int e0 = min(tid * per, total);
+  const int e1 = min(e0 + per, total);
+  uint32_t ties = 0;
+  for (int e = e0; e < e1; ++e) ties += ((sm.ukey[e] >> s) == prefix) ? 1u : 0u;
+  uint32_t tie_rank = block_exclusive_scan(ties, sm.ss.wsum, &sm.ss.total);
+  uint32_t keeps = 0;
+  {
+    uint32_t tr = tie_rank;
+    for (int e = e0; e < e1; ++e) {
+      const uint32_t v = sm.ukey[e] >> s;
+      if (v > prefix) ++keeps;
+      else if (v == prefix) keeps += (tr++ < need) ? 1u : 0u;
+    }
+  }
+  uint32_t slot = block_exclusive_scan(keeps, sm.ss.wsum, &sm.ss.total);
+  for (int e = e0; e < e1; ++e) {
+    const uint32_t v = sm.ukey[e] >> s;
+    bool keep = v > prefix;
+    if (v == prefix) keep = tie_rank++ < need;
+    if (keep) {
+      if (slot < (uint32_t)KMAX) out[slot] = sm.pos[e];
+      ++slot;
+    }
+  }
 }
+
+// ---------------------------------------------------------------------------
+// row-streaming fallback (candidate bucket too large for LDS)
+// ---------------------------------------------------------------------------
+__device__ inline uint64_t row_key(const float* row, int s) { return select_key(score_key(row[s]), s); }
+
+__device__ void select_row_streaming(const float* row, int n, int k, uint32_t d1, uint32_t need, uint32_t* hist,
+                                     ScanShared& ss, int32_t* out) {
+  const int tid = threadIdx.x;
+  uint64_t prefix = d1;
+  int plen = TK_BITS1;
+  while (plen < 64) {
+    const int bits = min(TK_LEVEL_BITS, 64 - plen);
+    const int shift = 64 - plen - bits;
+    const int nb = 1 << bits;
+    for (int i = tid; i < nb; i += TK_THREADS) hist[i] = 0;
+    __syncthreads();
+    for (int s = tid; s < n; s += TK_THREADS) {
+      const uint64_t key = row_key(row, s);
+      if ((key >> (64 - plen)) == prefix) atomicAdd(&hist[(key >> shift) & (uint64_t)(nb - 1)], 1u);
+    }
+    __syncthreads();
+    int d;
+    uint32_t above;
+    find_bucket(hist, nb, need, ss, &d, &above);
+    need -= above;
+    const uint32_t cnt = hist[d];
+    prefix = (prefix << bits) | (uint32_t)d;
+    plen += bits;
+    __syncthreads();
+    if (cnt == need) break;
+  }
+  const uint64_t thresh = plen >= 64 ? prefix : (prefix << (64 - plen));
+  uint32_t base = 0;
+  for (int t0 = 0; t0 < n; t0 += TK_THREADS) {
+    const int s = t0 + tid;
+    const uint32_t f = (s < n && row_key(row, s) >= thresh) ? 1u : 0u;
+    const uint32_t p = block_exclusive_scan(f, ss.wsum, &ss.total);
+    if (f && base + p < (uint32_t)k) out[base + p] = s;
+    base += ss.total;
+    __syncthreads();
+  }
+}
+
+// Ordered compaction of row[c0, c1): entries with top-12 key bits >= d1 go
+// to (dst_key, dst_pos) in position order.  Returns the count (all threads).
+__device__ uint32_t compact_chunk(const float* row, int c0, int c1, uint32_t d1, uint32_t* dst_key,
+                                  int32_t* dst_pos, uint32_t cap, ScanShared& ss) {
+  const int tid = threadIdx.x;
+  uint32_t base = 0;
+  for (int t0 = c0; t0 < c1; t0 += 4 * TK_THREADS) {
+    uint32_t u[4];
+    uint32_t f = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = t0 + tid * 4 + i;
+      u[i] = s < c1 ? score_key(row[s]) : 0u;
+      if (s < c1 && (u[i] >> TK_SHIFT1) >= d1) f |= 1u << i;
+    }
+    uint32_t p = block_exclusive_scan(__builtin_popcount(f), ss.wsum, &ss.total);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (f & (1u << i)) {
+        const uint32_t slot = base + p++;
+        if (slot < cap) {
+          dst_key[slot] = u[i];
+          dst_pos[slot] = t0 + tid * 4 + i;
+        }
+      }
+    }
+    base += ss.total;
+    __syncthreads();
+  }
+  return base;
+}
+
+// ---------------------------------------------------------------------------
+// one workgroup per row
+// ---------------------------------------------------------------------------
+struct RowShared {
+  uint32_t hist1[TK_BINS1];
+  ListShared list;
+};
 
 __global__ __launch_bounds__(TK_THREADS) void topk_row_kernel(BatchDev b, const float* __restrict__ scores,
                                                               int64_t ld, int k, int32_t* __restrict__ idx,
                                                               int32_t* __restrict__ count) {
-  __shared__ TopkShared sm;
+  __shared__ RowShared sm;
   const int q = blockIdx.x;
   const int tid = threadIdx.x;
   const QueryRange r = query_range(b, q);
@@ -112,129 +263,185 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_kernel(BatchDev b, const 
     return;
   }
   const float* row = scores + (int64_t)q * ld;
-
-  // 1. histogram of the top 12 key bits
-  for (int i = tid; i < TK_BINS1; i += TK_THREADS) sm.hist[i] = 0;
-  if (tid == 0) {
-    sm.nsel = 0;
-    sm.ncand = 0;
-  }
+  for (int i = tid; i < TK_BINS1; i += TK_THREADS) sm.hist1[i] = 0;
   __syncthreads();
-  for (int s = tid; s < n; s += TK_THREADS) atomicAdd(&sm.hist[score_key(row[s]) >> (32 - TK_BITS1)], 1u);
+  for (int s = tid; s < n; s += TK_THREADS) atomicAdd(&sm.hist1[score_key(row[s]) >> TK_SHIFT1], 1u);
   __syncthreads();
-  find_bucket(sm, TK_BINS1, (uint32_t)k);
-  const uint32_t d1 = (uint32_t)sm.digit;
-  uint32_t need = (uint32_t)k - sm.above;
-  const uint32_t m = sm.hist[d1];
-  const bool fits = m <= (uint32_t)TK_CAP;
-
-  // 2. keep the higher buckets, collect the threshold bucket
-  for (int s = tid; s < n; s += TK_THREADS) {
-    const uint32_t u = score_key(row[s]);
-    const uint32_t d = u >> (32 - TK_BITS1);
-    if (d > d1) {
-      const uint32_t slot = atomicAdd(&sm.nsel, 1u);
-      if (slot < (uint32_t)KMAX) sm.sel[slot] = s;
-    } else if (d == d1 && fits) {
-      const uint32_t c = atomicAdd(&sm.ncand, 1u);
-      if (c < (uint32_t)TK_CAP) {
-        sm.ckey[c] = u;
-        sm.cpos[c] = s;
-      }
-    }
-  }
-  __syncthreads();
-
-  // 3. radix levels over the remaining key bits of the threshold bucket
-  uint64_t prefix = d1;
-  int plen = TK_BITS1;
-  while (plen < 64) {
-    const int bits = min(TK_LEVEL_BITS, 64 - plen);
-    const int shift = 64 - plen - bits;
-    const int nb = 1 << bits;
-    for (int i = tid; i < nb; i += TK_THREADS) sm.hist[i] = 0;
+  int d1;
+  uint32_t above;
+  find_bucket(sm.hist1, TK_BINS1, (uint32_t)k, sm.list.ss, &d1, &above);
+  const uint32_t need = (uint32_t)k - above;
+  const uint32_t total = above + sm.hist1[d1];
+  if (total <= (uint32_t)TK_FCAP) {
+    compact_chunk(row, 0, n, (uint32_t)d1, sm.list.ukey, sm.list.pos, TK_FCAP, sm.list.ss);
     __syncthreads();
-    if (fits) {
-      for (int c = tid; c < (int)m; c += TK_THREADS) {
-        const uint64_t key = select_key(sm.ckey[c], sm.cpos[c]);
-        if ((key >> (64 - plen)) == prefix) atomicAdd(&sm.hist[(key >> shift) & (uint64_t)(nb - 1)], 1u);
-      }
-    } else {
-      for (int s = tid; s < n; s += TK_THREADS) {
-        const uint64_t key = row_key(row, s);
-        if ((key >> (64 - plen)) == prefix) atomicAdd(&sm.hist[(key >> shift) & (uint64_t)(nb - 1)], 1u);
-      }
-    }
-    __syncthreads();
-    find_bucket(sm, nb, need);
-    const uint32_t d = (uint32_t)sm.digit;
-    need -= sm.above;
-    const uint32_t cnt = sm.hist[d];
-    prefix = (prefix << bits) | d;
-    plen += bits;
-    __syncthreads();
-    if (cnt == need) break;
-  }
-  const uint64_t thresh = plen >= 64 ? prefix : (prefix << (64 - plen));
-
-  if (fits) {
-    // 4. add the kept candidates, sort ascending, write
-    for (int c = tid; c < (int)m; c += TK_THREADS) {
-      if (select_key(sm.ckey[c], sm.cpos[c]) >= thresh) {
-        const uint32_t slot = atomicAdd(&sm.nsel, 1u);
-        if (slot < (uint32_t)KMAX) sm.sel[slot] = sm.cpos[c];
-      }
-    }
-    int P = 1;
-    while (P < k) P <<= 1;
-    __syncthreads();
-    for (int j = k + tid; j < P; j += TK_THREADS) sm.sel[j] = 0x7FFFFFFF;
-    __syncthreads();
-    for (int size = 2; size <= P; size <<= 1) {
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        for (int i = tid; i < (P >> 1); i += TK_THREADS) {
-          const int lo = 2 * i - (i & (stride - 1));
-          const int hi = lo + stride;
-          const bool up = (lo & size) == 0;
-          const int x = sm.sel[lo], y = sm.sel[hi];
-          if ((x > y) == up) {
-            sm.sel[lo] = y;
-            sm.sel[hi] = x;
-          }
-        }
-        __syncthreads();
-      }
-    }
-    for (int j = tid; j < k; j += TK_THREADS) out[j] = sm.sel[j];
+    finalize_list(sm.list, (int)total, (uint32_t)d1, need, out);
   } else {
-    // 4'. ordered compaction of the row: keep every key >= threshold
-    uint32_t base = 0;
-    __shared__ uint32_t tile_total;
-    for (int t0 = 0; t0 < n; t0 += TK_THREADS) {
-      const int s = t0 + tid;
-      const uint32_t f = (s < n && row_key(row, s) >= thresh) ? 1u : 0u;
-      const uint32_t pos = block_exclusive_scan(f, sm.wsum, &tile_total);
-      if (f && base + pos < (uint32_t)k) out[base + pos] = s;
-      base += tile_total;
-      __syncthreads();
-    }
+    select_row_streaming(row, n, k, (uint32_t)d1, need, sm.hist1, sm.list.ss, out);
   }
   if (tid == 0 && count) count[q] = k;
 }
 
+// ---------------------------------------------------------------------------
+// split path: hist -> per-chunk ordered lists -> finalize
+// ---------------------------------------------------------------------------
+struct SplitWs {
+  uint32_t* hist;     // [nq][4096]
+  uint32_t* cnt;      // [nq][nchunk]
+  uint32_t* lkey;     // [nq][nchunk * TK_CHUNK]
+  int32_t* lpos;      // [nq][nchunk * TK_CHUNK]
+  int nchunk;
+};
+
+__global__ __launch_bounds__(256) void topk_zero_kernel(uint32_t* hist, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) hist[i] = 0;
+}
+
+__global__ __launch_bounds__(TK_THREADS) void topk_hist_kernel(BatchDev b, const float* __restrict__ scores,
+                                                               int64_t ld, int k, SplitWs ws) {
+  __shared__ uint32_t hist[TK_BINS1];
+  const int q = blockIdx.y;
+  const QueryRange r = query_range(b, q);
+  const int c0 = blockIdx.x * TK_CHUNK;
+  if (r.n <= k || c0 >= r.n) return;
+  const int c1 = min(c0 + TK_CHUNK, r.n);
+  const int tid = threadIdx.x;
+  for (int i = tid; i < TK_BINS1; i += TK_THREADS) hist[i] = 0;
+  __syncthreads();
+  const float* row = scores + (int64_t)q * ld;
+  for (int s = c0 + tid; s < c1; s += TK_THREADS) atomicAdd(&hist[score_key(row[s]) >> TK_SHIFT1], 1u);
+  __syncthreads();
+  uint32_t* gh = ws.hist + (int64_t)q * TK_BINS1;
+  for (int i = tid; i < TK_BINS1; i += TK_THREADS)
+    if (hist[i]) atomicAdd(&gh[i], hist[i]);
+}
+
+__global__ __launch_bounds__(TK_THREADS) void topk_gather_kernel(BatchDev b, const float* __restrict__ scores,
+                                                                 int64_t ld, int k, SplitWs ws) {
+  __shared__ uint32_t hist[TK_BINS1];
+  __shared__ ScanShared ss;
+  const int q = blockIdx.y;
+  const int c = blockIdx.x;
+  const QueryRange r = query_range(b, q);
+  const int c0 = c * TK_CHUNK;
+  if (r.n <= k || c0 >= r.n) return;
+  const int c1 = min(c0 + TK_CHUNK, r.n);
+  const int tid = threadIdx.x;
+  const uint32_t* gh = ws.hist + (int64_t)q * TK_BINS1;
+  for (int i = tid; i < TK_BINS1; i += TK_THREADS) hist[i] = gh[i];
+  __syncthreads();
+  int d1;
+  uint32_t above;
+  find_bucket(hist, TK_BINS1, (uint32_t)k, ss, &d1, &above);
+  const int64_t lbase = ((int64_t)q * ws.nchunk + c) * TK_CHUNK;
+  const uint32_t got = compact_chunk(scores + (int64_t)q * ld, c0, c1, (uint32_t)d1, ws.lkey + lbase,
+                                     ws.lpos + lbase, TK_CHUNK, ss);
+  if (tid == 0) ws.cnt[(int64_t)q * ws.nchunk + c] = got;
+}
+
+struct FinalShared {
+  uint32_t hist1[TK_BINS1];
+  uint32_t off[TK_THREADS];
+  ListShared list;
+};
+
+__global__ __launch_bounds__(TK_THREADS) void topk_final_kernel(BatchDev b, const float* __restrict__ scores,
+                                                                int64_t ld, int k, int32_t* __restrict__ idx,
+                                                                int32_t* __restrict__ count, SplitWs ws) {
+  __shared__ FinalShared sm;
+  const int q = blockIdx.x;
+  const int tid = threadIdx.x;
+  const QueryRange r = query_range(b, q);
+  const int n = r.n;
+  int32_t* out = idx + (int64_t)q * k;
+  if (n <= k) {
+    for (int j = tid; j < k; j += TK_THREADS) out[j] = j < n ? j : -1;
+    if (tid == 0 && count) count[q] = n;
+    return;
+  }
+  const uint32_t* gh = ws.hist + (int64_t)q * TK_BINS1;
+  for (int i = tid; i < TK_BINS1; i += TK_THREADS) sm.hist1[i] = gh[i];
+  __syncthreads();
+  int d1;
+  uint32_t above;
+  find_bucket(sm.hist1, TK_BINS1, (uint32_t)k, sm.list.ss, &d1, &above);
+  const uint32_t need = (uint32_t)k - above;
+  const uint32_t total = above + sm.hist1[d1];
+  const int nch = (n + TK_CHUNK - 1) / TK_CHUNK;
+  if (total <= (uint32_t)TK_FCAP) {
+    // concatenate the per-chunk lists in chunk (= position) order
+    const uint32_t mine = tid < nch ? ws.cnt[(int64_t)q * ws.nchunk + tid] : 0u;
+    const uint32_t o = block_exclusive_scan(mine, sm.list.ss.wsum, &sm.list.ss.total);
+    if (tid < nch) sm.off[tid] = o;
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+      const uint32_t m = ws.cnt[(int64_t)q * ws.nchunk + c];
+      const int64_t lbase = ((int64_t)q * ws.nchunk + c) * TK_CHUNK;
+      for (uint32_t e = tid; e < m; e += TK_THREADS) {
+        sm.list.ukey[sm.off[c] + e] = ws.lkey[lbase + e];
+        sm.list.pos[sm.off[c] + e] = ws.lpos[lbase + e];
+      }
+    }
+    __syncthreads();
+    finalize_list(sm.list, (int)total, (uint32_t)d1, need, out);
+  } else {
+    select_row_streaming(scores + (int64_t)q * ld, n, k, (uint32_t)d1, need, sm.hist1, sm.list.ss, out);
+  }
+  if (tid == 0 && count) count[q] = k;
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+// The split path needs one finalize thread per chunk of the longest row.
+static bool use_split(int nq, int max_len) {
+  return nq <= TK_ROWS_SPLIT_MAX && (int64_t)max_len <= (int64_t)TK_THREADS * TK_CHUNK;
+}
+
+static size_t split_bytes(int nq, int max_len, SplitWs* ws, char* base) {
+  const int nchunk = (max_len + TK_CHUNK - 1) / TK_CHUNK;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += (bytes + 255) & ~(size_t)255;
+    return at;
+  };
+  const size_t h = take((size_t)nq * TK_BINS1 * 4);
+  const size_t c = take((size_t)nq * nchunk * 4);
+  const size_t kk = take((size_t)nq * nchunk * TK_CHUNK * 4);
+  const size_t p = take((size_t)nq * nchunk * TK_CHUNK * 4);
+  if (ws) {
+    ws->hist = (uint32_t*)(base + h);
+    ws->cnt = (uint32_t*)(base + c);
+    ws->lkey = (uint32_t*)(base + kk);
+    ws->lpos = (int32_t*)(base + p);
+    ws->nchunk = nchunk;
+  }
+  return off;
+}
+
 size_t topk_workspace_bytes(int nq, int max_len, int k) {
-  (void)nq;
-  (void)max_len;
   (void)k;
-  return 0;
+  if (nq <= 0 || max_len <= 0 || !use_split(nq, max_len)) return 0;
+  return split_bytes(nq, max_len, nullptr, nullptr);
 }
 
 hipError_t launch_topk(const BatchDev& b, const float* scores, int64_t ld, int k, int32_t* idx,
-                       int32_t* count, void* ws, size_t ws_bytes, hipStream_t st) {
-  (void)ws;
-  (void)ws_bytes;
+                       int32_t* count, void* wsp, size_t ws_bytes, hipStream_t st) {
   if (b.nq == 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_row_kernel, dim3(b.nq), dim3(TK_THREADS), 0, st, b, scores, ld, k, idx, count);
+  if (!use_split(b.nq, b.max_len)) {
+    hipLaunchKernelGGL(topk_row_kernel, dim3(b.nq), dim3(TK_THREADS), 0, st, b, scores, ld, k, idx, count);
+    return hipGetLastError();
+  }
+  SplitWs ws;
+  if (wsp == nullptr || ws_bytes < split_bytes(b.nq, b.max_len, &ws, (char*)wsp)) return hipErrorInvalidValue;
+  const int nh = b.nq * TK_BINS1;
+  hipLaunchKernelGGL(topk_zero_kernel, dim3((nh + 255) / 256), dim3(256), 0, st, ws.hist, nh);
+  dim3 grid(ws.nchunk, b.nq);
+  hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(TK_THREADS), 0, st, b, scores, ld, k, ws);
+  hipLaunchKernelGGL(topk_gather_kernel, grid, dim3(TK_THREADS), 0, st, b, scores, ld, k, ws);
+  hipLaunchKernelGGL(topk_final_kernel, dim3(b.nq), dim3(TK_THREADS), 0, st, b, scores, ld, k, idx, count, ws);
   return hipGetLastError();
 }
 

@@ -128,6 +128,30 @@ def test_topk_engineered_rows(B, k):
         assert np.array_equal(idx[i], ref), f"row {i}: selection differs"
 
 
+def test_topk_many_rows(B):
+    """Batches of many rows take the one-workgroup-per-row path."""
+    rng = np.random.default_rng(31)
+    rows = []
+    for i in range(300):
+        kind = i % 5
+        n = int(rng.integers(1, 9000))
+        if kind == 0:
+            rows.append(rng.integers(0, 40, n).astype(np.float32))
+        elif kind == 1:
+            rows.append(rng.standard_normal(n).astype(np.float32))
+        elif kind == 2:
+            rows.append(np.zeros(n if i != 2 else 20000, np.float32))
+        elif kind == 3:
+            rows.append(np.where(rng.random(n) < 0.5, 0.0, -0.0).astype(np.float32))
+        else:
+            rows.append((rng.integers(0, 3, n) * 7.0 - 5.0).astype(np.float32))
+    idx, cnt = _topk_gpu(B, rows, 2048)
+    for i, r in enumerate(rows):
+        ref, m = oracle.topk(r.astype(np.float64), 2048)
+        assert cnt[i] == m, f"row {i}"
+        assert np.array_equal(idx[i], ref), f"row {i}: selection differs"
+
+
 def test_topk_on_indexer_scores(B):
     w = wl.make_decode([2048, 2049, 5000, 33000], "bf16", 1, seed=24)
     t = w.to_torch(DEV)
