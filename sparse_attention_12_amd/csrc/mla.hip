@@ -62,20 +62,25 @@ constexpr int MLA_TILE = 32;                    // positions per tile
 constexpr int MLA_ROWB = D * 2;                 // 1,152 bytes per bf16 row
 constexpr int MLA_CHUNKS = MLA_ROWB / 16;       // 72 chunks of 16 B per row
 constexpr int MLA_TILEB = MLA_TILE * MLA_ROWB;  // 36,864 bytes per tile
-constexpr int MLA_LOADS = MLA_TILE * MLA_CHUNKS / MLA_THREADS;  // 9 chunks per thread
 constexpr int MLA_NBUF = 2;
 constexpr int MLA_SPLIT_MAX = KMAX;
-static_assert(MLA_TILE * MLA_CHUNKS == MLA_LOADS * MLA_THREADS, "tile staging must be exact");
+static_assert(MLA_TILE * 8 == MLA_THREADS, "one gathering thread per (row, in-group chunk)");
 constexpr float MLA_RESCALE_SLACK = 8.0f;       // log2 units
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-// LDS tile layout: row r occupies bytes [r*1152, (r+1)*1152); its logical
-// 16-byte chunk c is stored at chunk position c ^ (r & 7), which spreads the
-// column reads of consecutive rows over distinct banks.
-__device__ inline int swz(int row, int chunk) { return row * MLA_ROWB + ((chunk ^ (row & 7)) << 4); }
+// LDS tile layout (36,864 bytes): nine column groups of 64 latent/rotary
+// values; group G holds rows 0..31 at 128 bytes each, and row r's logical
+// 16-byte chunk c (of the group's eight) sits at chunk slot c ^ (r & 7).
+// One gather instruction of wave w fills rows 8w..8w+7 of one group: 1 KB,
+// written in lane order.
+constexpr int MLA_GROUPB = MLA_TILE * 128;  // 4,096 bytes per column group
+
+__device__ inline int tile_off(int row, int chunk) {
+  return (chunk >> 3) * MLA_GROUPB + row * 128 + (((chunk & 7) ^ (row & 7)) << 4);
+}
 
 struct MlaTileState {
   f32x4 o[DC / 16];
@@ -83,39 +88,39 @@ struct MlaTileState {
   float l_part;
 };
 
-// Gather tile t of the selection straight into LDS (16 bytes per lane, in
-// lane order: the wave-uniform base goes to M0).
-__device__ inline void mla_issue(uint8_t* buf, const uint16_t* kv, const int* sel_l, int nent, int t, int tid,
+// Gather tile t of the selection straight into LDS.  Thread (wave w, lane l)
+// fetches row 8w + l/8 of the tile: for each column group i, the 16-byte
+// chunk ((l % 8) ^ (row & 7)) + 8i, which lands at lane slot l of the 1 KB
+// block of (group i, rows 8w..8w+7).
+__device__ inline void mla_issue(uint8_t* buf, const uint16_t* kv, const int* sel_l, int nent, int t, int lane,
                                  int wave_u) {
+  const int row = wave_u * 8 + (lane >> 3);
+  const int j = t * MLA_TILE + row;
+  const int pos = j < nent ? sel_l[j] : -1;
+  const uint16_t* src = kv + (int64_t)(pos >= 0 ? pos : 0) * D + (((lane & 7) ^ (row & 7)) << 3);
+  uint8_t* dst = buf + wave_u * 1024;
 #pragma unroll
-  for (int i = 0; i < MLA_LOADS; ++i) {
-    const int slot = i * MLA_THREADS + tid;
-    const int row = slot / MLA_CHUNKS;
-    const int pc = slot - row * MLA_CHUNKS;
-    const int j = t * MLA_TILE + row;
-    const int pos = j < nent ? sel_l[j] : -1;
-    const uint16_t* src = kv + (int64_t)(pos >= 0 ? pos : 0) * D + ((pc ^ (row & 7)) << 3);
-    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(buf + (i * MLA_THREADS + wave_u * 64) * 16),
-                                     16, 0, 0);
-  }
+  for (int i = 0; i < D * 2 / 128; ++i)
+    __builtin_amdgcn_global_load_lds((const void*)(src + i * 64), (lds_void*)(dst + i * MLA_GROUPB), 16, 0, 0);
 }
 
 // One tile: S^T = K.Q^T, online softmax, O^T += V^T.P^T.
 __device__ inline void mla_tile(MlaTileState& st, const uint8_t* tile, const bf16x8 (&qf)[D / 32],
                                 const int* sel_l, int nent, int t0, int n16, int g, float scale_log2) {
-  // Row r's chunk 4t+g sits at 8*(t/2) + ((4*(t%2) + g) ^ (r & 7)): two base
-  // addresses per row plus an immediate 128*(t/2).  Loads run two steps
-  // ahead of the MFMAs; each block keeps two accumulator chains.
+  // Row r's logical chunk 4t+g lies in column group t/2 at in-group chunk
+  // 4*(t%2) + g: two base addresses per row plus an immediate 4096*(t/2).
+  // Loads run two steps ahead of the MFMAs; each block keeps two
+  // accumulator chains.
   const uint8_t* ev[2];
   const uint8_t* od[2];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
     const int row = 16 * mb + n16;
-    ev[mb] = tile + row * MLA_ROWB + ((g ^ (row & 7)) << 4);
-    od[mb] = tile + row * MLA_ROWB + (((4 | g) ^ (row & 7)) << 4);
+    ev[mb] = tile + tile_off(row, g);
+    od[mb] = tile + tile_off(row, 4 + g);
   }
   auto kfrag = [&](int mb, int t) -> u32x4 {
-    return *(const u32x4*)(((t & 1) ? od[mb] : ev[mb]) + (t >> 1) * 128);
+    return *(const u32x4*)(((t & 1) ? od[mb] : ev[mb]) + (t >> 1) * MLA_GROUPB);
   };
   f32x4 acc[2][2];
 #pragma unroll
@@ -181,8 +186,9 @@ __device__ inline void mla_tile(MlaTileState& st, const uint8_t* tile, const bf1
   // (e < 4 ? 4g + e : 16 + 4g + e - 4).  A transposing LDS read gives lane
   // i of a 16-lane group element i%4 of source lane 4j + i/4, so source
   // lane s points at row 4g + s/4 (+16) and latent column 16db + 4(s%4).
-  // Column 16db + sdim lies in chunk 2db + sdim/8 = 8*(db/4) + (2*(db%4) + sdim/8):
-  // four base addresses per source row plus an immediate 128*(db/4).
+  // Column 16db + sdim lies in column group db/4, in-group chunk
+  // 2*(db%4) + sdim/8: four base addresses per source row plus an
+  // immediate 4096*(db/4).
   const int srow0 = 4 * g + (n16 >> 2);
   const int srow1 = srow0 + 16;
   const int sdim = 4 * (n16 & 3);
@@ -192,12 +198,12 @@ __device__ inline void mla_tile(MlaTileState& st, const uint8_t* tile, const bf1
   const uint8_t* b1[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    b0[u] = tile + srow0 * MLA_ROWB + (((2 * u + c0) ^ (srow0 & 7)) << 4) + boff;
-    b1[u] = tile + srow1 * MLA_ROWB + (((2 * u + c0) ^ (srow1 & 7)) << 4) + boff;
+    b0[u] = tile + tile_off(srow0, 2 * u + c0) + boff;
+    b1[u] = tile + tile_off(srow1, 2 * u + c0) + boff;
   }
   auto vfrag = [&](int db) -> bf16x8 {
     const int u = db & 3;
-    const int imm = (db >> 2) * 128;
+    const int imm = (db >> 2) * MLA_GROUPB;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b0[u] + imm));
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b1[u] + imm));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -215,7 +221,7 @@ __device__ inline void mla_tile(MlaTileState& st, const uint8_t* tile, const bf1
   }
 }
 
-__global__ __launch_bounds__(MLA_THREADS, 1) void mla_bf16_kernel(MlaParams p) {
+__global__ __launch_bounds__(MLA_THREADS, 2) void mla_bf16_kernel(MlaParams p) {
   // two distinct arrays, so that reads of one tile are known not to alias
   // the asynchronous gather into the other
   __shared__ __attribute__((aligned(16))) uint8_t tile0[MLA_TILEB];
@@ -258,16 +264,16 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_bf16_kernel(MlaParams p) {
   st.l_part = 0.0f;
   __syncthreads();
 
-  if (ntiles > 0) mla_issue(tile0, kv, sel_l, nent, 0, tid, wave_u);
+  if (ntiles > 0) mla_issue(tile0, kv, sel_l, nent, 0, lane, wave_u);
   for (int it = 0; it < ntiles; it += 2) {
     __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): this thread's part of tile `it` landed
     __syncthreads();                     // every part landed; the other buffer is free
-    if (it + 1 < ntiles) mla_issue(tile1, kv, sel_l, nent, it + 1, tid, wave_u);
+    if (it + 1 < ntiles) mla_issue(tile1, kv, sel_l, nent, it + 1, lane, wave_u);
     mla_tile(st, tile0, qf, sel_l, nent, it * MLA_TILE, n16, g, p.scale_log2);
     if (it + 1 >= ntiles) break;
     __builtin_amdgcn_s_waitcnt(0x3F70);
     __syncthreads();
-    if (it + 2 < ntiles) mla_issue(tile0, kv, sel_l, nent, it + 2, tid, wave_u);
+    if (it + 2 < ntiles) mla_issue(tile0, kv, sel_l, nent, it + 2, lane, wave_u);
     mla_tile(st, tile1, qf, sel_l, nent, (it + 1) * MLA_TILE, n16, g, p.scale_log2);
   }
 
@@ -418,7 +424,7 @@ __global__ __launch_bounds__(CMB_THREADS) void mla_combine(MlaParams p) {
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-constexpr int MLA_TARGET_BLOCKS = 256;  // one workgroup per compute unit
+constexpr int MLA_TARGET_BLOCKS = 512;  // two workgroups per compute unit
 
 int mla_num_splits(int dtype, int nq, int k, int n_layers) {
   const int tile = dtype == 0 ? MLA32_TILE : MLA_TILE;
