@@ -2,14 +2,15 @@
 
 One step = one pass of the whole read over one batch (index scores, top-k,
 then the sparse MLA read of every layer that shares the selection), through
-the C ABI, with all inputs resident in HBM.  Prints one JSON line.
+the C ABI, with all inputs resident in HBM: the fused decode entry for decode
+batches, the three calls in turn for a prefill chunk.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 0..4] [--no-cpu]
 
 The default workload is the decode batch of 64 sequences at 32,768 positions
 (bf16).  `roofline` describes the dominant kernel (the indexer): algorithmic
 bytes (or FLOP) per launch over its average duration, timed with HIP events
-on the launch stream inside the timed region.  `cpu_baseline` times the CPU
+on the launch stream over a timed loop of that kernel alone.  `cpu_baseline` times the CPU
 oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -74,55 +75,50 @@ def main():
                          device=dev)
     stream = torch.cuda.current_stream()
 
-    ev_idx = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+    fused_ws = torch.empty(max(B.dsa_mla_decode_fused_workspace_size(w.nq, w.max_len, k, L), 256),
+                           dtype=torch.uint8, device=dev)
 
-    def step(i=None):
-        if i is not None:
-            ev_idx[i][0].record(stream)
-        B.dsa_index_score(batch, t["qI"], t["w"], t["kI"], scores)
-        if i is not None:
-            ev_idx[i][1].record(stream)
-        B.dsa_topk(batch, scores, k, idx, count, tk_ws if tk_ws_n else None)
-        for l in range(L):
-            B.mla_sparse_attend(batch, t["q"][l], t["kv"][l], idx, k, w.tau, outs[l], lses[l], mla_ws)
+    def step():
+        if w.kind == "decode":
+            # the decode read as one call: indexer, top-k, every layer's MLA
+            B.dsa_mla_decode_fused(batch, t["qI"], t["w"], t["kI"], k, t["q"], t["kv"], outs, w.tau, lses, idx,
+                                   fused_ws)
+        else:
+            B.dsa_index_score(batch, t["qI"], t["w"], t["kI"], scores)
+            B.dsa_topk(batch, scores, k, idx, count, tk_ws if tk_ws_n else None)
+            for l in range(L):
+                B.mla_sparse_attend(batch, t["q"][l], t["kv"][l], idx, k, w.tau, outs[l], lses[l], mla_ws)
+
+    def timed(fn, n):
+        """Average ms per call of fn over n calls, HIP events on the launch stream."""
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    t0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    t1.record(stream)
-    torch.cuda.synchronize()
+    ms_per_step = timed(step, args.steps)
     wall = time.perf_counter() - wall0
-    ms_per_step = t0.elapsed_time(t1) / args.steps
-    idx_ms = sum(a.elapsed_time(b) for a, b in ev_idx) / args.steps
-    print(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step (wall {wall * 1e3 / args.steps:.4f}); "
-          f"indexer {idx_ms:.4f} ms", file=sys.stderr, flush=True)
 
-    # the fused entry point (one call: indexer, top-k, every layer's MLA)
-    fused_ws = torch.empty(B.dsa_mla_decode_fused_workspace_size(w.nq, w.max_len, k, L), dtype=torch.uint8,
-                           device=dev)
-    fused_ms = None
-    if w.kind == "decode":
-        for _ in range(max(2, args.warmup)):
-            B.dsa_mla_decode_fused(batch, t["qI"], t["w"], t["kI"], k, t["q"], t["kv"], outs, w.tau, lses, idx,
-                                   fused_ws)
-        f0 = torch.cuda.Event(enable_timing=True)
-        f1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        f0.record(stream)
-        for _ in range(args.steps):
-            B.dsa_mla_decode_fused(batch, t["qI"], t["w"], t["kI"], k, t["q"], t["kv"], outs, w.tau, lses, idx,
-                                   fused_ws)
-        f1.record(stream)
-        torch.cuda.synchronize()
-        fused_ms = f0.elapsed_time(f1) / args.steps
+    # per-stage timings of the same kernels, same launch configurations
+    idx_fn = lambda: B.dsa_index_score(batch, t["qI"], t["w"], t["kI"], scores)
+    idx_fn()
+    idx_ms = timed(idx_fn, args.steps)
+    tk_fn = lambda: B.dsa_topk(batch, scores, k, idx, count, tk_ws if tk_ws_n else None)
+    tk_ms = timed(tk_fn, args.steps)
+    mla_fn = lambda: B.mla_sparse_attend(batch, t["q"][0], t["kv"][0], idx, k, w.tau, outs[0], lses[0], mla_ws)
+    mla_ms = timed(mla_fn, args.steps)
+    print(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step (wall {wall * 1e3 / args.steps:.4f}); "
+          f"indexer {idx_ms:.4f} ms, top-k {tk_ms:.4f} ms, one-layer MLA {mla_ms:.4f} ms",
+          file=sys.stderr, flush=True)
 
     tr = costmodel.path_traffic(w.seq_len, w.q_seq, w.q_pos, w.dtype, L, k)
     value = w.nq / (ms_per_step / 1e3)
@@ -166,8 +162,10 @@ def main():
         "cpu_baseline": cpu,
         "path": {"algorithmic_bytes": tr["path_bytes"], "algorithmic_flop": tr["path_flop"],
                  "GBps": round(path_gbps, 1), "hbm_frac": round(path_gbps / HBM_PEAK_GBPS, 4),
-                 "indexer_ms": round(idx_ms, 5),
-                 "fused_entry_ms_per_step": None if fused_ms is None else round(fused_ms, 5)},
+                 "step_entry": "dsa_mla_decode_fused" if w.kind == "decode" else
+                               "dsa_index_score + dsa_topk + mla_sparse_attend",
+                 "indexer_ms": round(idx_ms, 5), "topk_ms": round(tk_ms, 5),
+                 "mla_one_layer_ms": round(mla_ms, 5)},
     }
     print(json.dumps(rec))
 

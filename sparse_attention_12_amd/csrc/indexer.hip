@@ -5,11 +5,10 @@
 // position fixes the shapes):
 //   I[q][s] = sum_{h<32} w[q][h] * max(0, qI[q][h][:] . kI[s][:])
 //
-// Decode (one query per sequence) is a stream over the query's keys: the
-// 32 heads sit on the M axis of a v_mfma_f32_32x32x16_bf16 tile, 32 keys on
-// N, and the 128-wide contraction takes 8 MFMAs.  Each lane then holds 16 of
-// the 32 head dot products of one key, so the ReLU and the weighted head sum
-// stay in registers and finish with one cross-lane add.
+// Decode (one query per sequence) is a stream over the query's keys: heads
+// sit on the M axis of 16x16x32 MFMA tiles and keys on N, so each lane ends
+// with 8 of the 32 head dot products of one key; the ReLU and the weighted
+// head sum stay in registers and finish with two cross-lane adds.
 //
 // Prefill (many queries of one sequence) is a blocked product: a workgroup
 // keeps 32 queries' indexer rows in registers (4 per wave) and streams key
@@ -22,13 +21,19 @@ namespace dsa {
 // ---------------------------------------------------------------------------
 // decode, bf16
 // ---------------------------------------------------------------------------
+// v_mfma_f32_16x16x32_bf16 with 16 heads on M (two blocks for 32 heads), 16
+// keys on N and the 128-wide contraction in four steps of 32.  Lane
+// (c = l%16, g = l/16) loads, for contraction step s, the 16 bytes at
+// s*64 + g*16 of key c, so one load instruction covers 64 contiguous bytes
+// of each of 16 keys -- a shape that streams at full HBM rate, unlike 32
+// keys x 32 bytes.  A step of 32 keys is two such key blocks.
 constexpr int IDX_DEC_THREADS = 256;
 constexpr int IDX_DEC_WAVES = IDX_DEC_THREADS / 64;
-constexpr int IDX_DEC_STEP = 32;       // keys per MFMA step and wave
+constexpr int IDX_DEC_STEP = 32;       // keys per pipeline stage and wave
 constexpr int IDX_DEC_CHUNK = 2048;    // keys per workgroup
 
 struct KeyTile {
-  u32x4 v[8];
+  u32x4 v[8];  // [key block kb][contraction step s] at v[kb*4 + s]
 };
 
 __global__ __launch_bounds__(IDX_DEC_THREADS) void idx_decode_bf16(
@@ -41,42 +46,60 @@ __global__ __launch_bounds__(IDX_DEC_THREADS) void idx_decode_bf16(
   const int end = min(base + IDX_DEC_CHUNK, r.n);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int col = lane & 31;   // A row (head) / B column (key) of this lane
-  const int half = lane >> 5;  // which 8 of each 16 contraction slots
+  const int c16 = lane & 15;  // A row (head within block) / B column (key within block)
+  const int g = lane >> 4;    // which 8 of each 32 contraction slots
 
-  // A operand: head `col`, contraction slots t*16 + half*8 + [0,8).
-  bf16x8 a[8];
-  const uint16_t* qrow = qI + ((int64_t)q * HI + col) * DI + half * 8;
+  // A operand: head hb*16 + c16, contraction slots s*32 + 8g + [0,8).
+  bf16x8 a[2][4];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) a[t] = as_bf16x8(load16(qrow + t * 16));
-  // Accumulator register i of this lane holds head 8*(i/4) + 4*half + i%4.
-  float wr[16];
+  for (int hb = 0; hb < 2; ++hb) {
+    const uint16_t* qrow = qI + ((int64_t)q * HI + hb * 16 + c16) * DI + g * 8;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) wr[i] = w[(int64_t)q * HI + 8 * (i >> 2) + 4 * half + (i & 3)];
+    for (int st = 0; st < 4; ++st) a[hb][st] = as_bf16x8(load16(qrow + st * 32));
+  }
+  // Accumulator register i of head block hb holds head hb*16 + 4g + i.
+  float wr[2][4];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wr[hb][i] = w[(int64_t)q * HI + hb * 16 + 4 * g + i];
 
-  const uint16_t* kb = kI + r.row0 * DI + half * 8;
+  const uint16_t* kb = kI + r.row0 * DI + g * 8;
   float* out = scores + (int64_t)q * ld;
   const int last = end - 1;
   constexpr int WSTEP = IDX_DEC_WAVES * IDX_DEC_STEP;
 
   // Keys past the chunk end re-read the chunk's last row (a cache hit), so
-  // every load is unconditional and three tiles stay in flight.
+  // every load is unconditional and three stages stay in flight.
   auto load = [&](KeyTile& kt, int k0) {
-    const uint16_t* p = kb + (int64_t)min(k0 + col, last) * DI;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) kt.v[t] = load16_nt(p + t * 16);
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      const uint16_t* p = kb + (int64_t)min(k0 + kb2 * 16 + c16, last) * DI;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) kt.v[kb2 * 4 + st] = load16_nt(p + st * 32);
+    }
   };
   auto score = [&](const KeyTile& kt, int k0) {
-    f32x16 acc = {};
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t], as_bf16x8(kt.v[t]), acc, 0, 0, 0);
-    float part = 0.0f;
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 16; ++i) part = fmaf(wr[i], fmaxf(acc[i], 0.0f), part);
-    part += __shfl_xor(part, 32);
-    const int key = k0 + col;
-    if (half == 0 && key < end) out[key] = part;
+      for (int st = 0; st < 4; ++st) {
+        const bf16x8 bk = as_bf16x8(kt.v[kb2 * 4 + st]);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0][st], bk, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1][st], bk, acc1, 0, 0, 0);
+      }
+      float part = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        part = fmaf(wr[0][i], fmaxf(acc0[i], 0.0f), part);
+        part = fmaf(wr[1][i], fmaxf(acc1[i], 0.0f), part);
+      }
+      part += __shfl_xor(part, 16);
+      part += __shfl_xor(part, 32);
+      const int key = k0 + kb2 * 16 + c16;
+      if (g == 0 && key < end) out[key] = part;
+    }
   };
 
   int k0 = base + wave * IDX_DEC_STEP;
