@@ -30,7 +30,6 @@ namespace dsa {
 constexpr int IDX_DEC_THREADS = 256;
 constexpr int IDX_DEC_WAVES = IDX_DEC_THREADS / 64;
 constexpr int IDX_DEC_STEP = 32;       // keys per pipeline stage and wave
-constexpr int IDX_DEC_CHUNK = 2048;    // keys per workgroup
 
 struct KeyTile {
   u32x4 v[8];  // [key block kb][contraction step s] at v[kb*4 + s]
@@ -38,12 +37,12 @@ struct KeyTile {
 
 __global__ __launch_bounds__(IDX_DEC_THREADS) void idx_decode_bf16(
     BatchDev b, const uint16_t* __restrict__ qI, const float* __restrict__ w,
-    const uint16_t* __restrict__ kI, float* __restrict__ scores, int64_t ld) {
+    const uint16_t* __restrict__ kI, float* __restrict__ scores, int64_t ld, int chunk) {
   const int q = blockIdx.y;
   const QueryRange r = query_range(b, q);
-  const int base = blockIdx.x * IDX_DEC_CHUNK;
+  const int base = blockIdx.x * chunk;
   if (base >= r.n) return;
-  const int end = min(base + IDX_DEC_CHUNK, r.n);
+  const int end = min(base + chunk, r.n);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int c16 = lane & 15;  // A row (head within block) / B column (key within block)
@@ -251,6 +250,16 @@ __global__ __launch_bounds__(PF_THREADS) void idx_prefill_bf16(
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
+// Keys per decode workgroup: the largest power of two in [512, 4096] that
+// still gives about 2,048 workgroups for the padded batch (nq x max_len), so
+// short or ragged batches keep every compute unit streaming.
+static int decode_chunk(int nq, int max_len) {
+  const int64_t keys = (int64_t)nq * max_len;
+  int chunk = 4096;
+  while (chunk > 512 && keys / chunk < 2048) chunk >>= 1;
+  return chunk;
+}
+
 hipError_t launch_index_score(const BatchDev& b, int dtype, const void* qI, const float* w,
                               const void* kI, float* scores, int64_t ld, hipStream_t st) {
   if (b.nq == 0) return hipSuccess;
@@ -263,9 +272,10 @@ hipError_t launch_index_score(const BatchDev& b, int dtype, const void* qI, cons
     hipLaunchKernelGGL(idx_prefill_bf16, grid, dim3(PF_THREADS), 0, st, b, (const uint16_t*)qI, w,
                        (const uint16_t*)kI, scores, ld);
   } else {
-    dim3 grid((b.max_len + IDX_DEC_CHUNK - 1) / IDX_DEC_CHUNK, b.nq);
+    const int chunk = decode_chunk(b.nq, b.max_len);
+    dim3 grid((b.max_len + chunk - 1) / chunk, b.nq);
     hipLaunchKernelGGL(idx_decode_bf16, grid, dim3(IDX_DEC_THREADS), 0, st, b,
-                       (const uint16_t*)qI, w, (const uint16_t*)kI, scores, ld);
+                       (const uint16_t*)qI, w, (const uint16_t*)kI, scores, ld, chunk);
   }
   return hipGetLastError();
 }

@@ -370,18 +370,23 @@ __global__ __launch_bounds__(TK_THREADS) void topk_final_kernel(BatchDev b, cons
   const uint32_t total = above + sm.hist1[d1];
   const int nch = (n + TK_CHUNK - 1) / TK_CHUNK;
   if (total <= (uint32_t)TK_FCAP) {
-    // concatenate the per-chunk lists in chunk (= position) order
+    // concatenate the per-chunk lists in chunk (= position) order: offsets
+    // by a block scan, then every entry copied in one parallel pass
     const uint32_t mine = tid < nch ? ws.cnt[(int64_t)q * ws.nchunk + tid] : 0u;
     const uint32_t o = block_exclusive_scan(mine, sm.list.ss.wsum, &sm.list.ss.total);
     if (tid < nch) sm.off[tid] = o;
     __syncthreads();
-    for (int c = 0; c < nch; ++c) {
-      const uint32_t m = ws.cnt[(int64_t)q * ws.nchunk + c];
-      const int64_t lbase = ((int64_t)q * ws.nchunk + c) * TK_CHUNK;
-      for (uint32_t e = tid; e < m; e += TK_THREADS) {
-        sm.list.ukey[sm.off[c] + e] = ws.lkey[lbase + e];
-        sm.list.pos[sm.off[c] + e] = ws.lpos[lbase + e];
+    const int64_t lq = (int64_t)q * ws.nchunk * TK_CHUNK;
+    for (uint32_t e = tid; e < total; e += TK_THREADS) {
+      int lo = 0, hi = nch - 1;  // last chunk whose offset is <= e
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (sm.off[mid] <= e) lo = mid;
+        else hi = mid - 1;
       }
+      const int64_t src = lq + (int64_t)lo * TK_CHUNK + (e - sm.off[lo]);
+      sm.list.ukey[e] = ws.lkey[src];
+      sm.list.pos[e] = ws.lpos[src];
     }
     __syncthreads();
     finalize_list(sm.list, (int)total, (uint32_t)d1, need, out);
