@@ -57,14 +57,23 @@ __device__ inline void store_out4(const MlaParams& p, int layer, int64_t off, f3
 // ---------------------------------------------------------------------------
 // bf16 split kernel
 // ---------------------------------------------------------------------------
-constexpr int MLA_THREADS = 256;
+// One workgroup of 8 waves per (split, query, layer).  Wave w = (h, d) with
+// h = w % 4 (heads 16h..16h+15) and d = w / 4:
+//   * S^T for its 16 heads over the tile: wave d contracts dims
+//     [288d, 288d+288) and the two waves of a head group add their partial
+//     logits through LDS (a + b = b + a, so both hold identical logits and
+//     take identical softmax steps);
+//   * O^T for its 16 heads and latent columns [256d, 256d+256).
+// Tiles of 32 selected rows are gathered straight into a ring of three LDS
+// buffers; the two wave halves issue alternate tiles, so two tiles are in
+// flight while one is consumed.
+constexpr int MLA_THREADS = 512;
 constexpr int MLA_TILE = 32;                    // positions per tile
 constexpr int MLA_ROWB = D * 2;                 // 1,152 bytes per bf16 row
-constexpr int MLA_CHUNKS = MLA_ROWB / 16;       // 72 chunks of 16 B per row
 constexpr int MLA_TILEB = MLA_TILE * MLA_ROWB;  // 36,864 bytes per tile
-constexpr int MLA_NBUF = 2;
 constexpr int MLA_SPLIT_MAX = KMAX;
-static_assert(MLA_TILE * 8 == MLA_THREADS, "one gathering thread per (row, in-group chunk)");
+constexpr int MLA_KSTEPS = D / 32 / 2;          // contraction steps per wave (9)
+constexpr int MLA_VBLK = DC / 16 / 2;           // 16-column value blocks per wave (16)
 constexpr float MLA_RESCALE_SLACK = 8.0f;       // log2 units
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -74,7 +83,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 // LDS tile layout (36,864 bytes): nine column groups of 64 latent/rotary
 // values; group G holds rows 0..31 at 128 bytes each, and row r's logical
 // 16-byte chunk c (of the group's eight) sits at chunk slot c ^ (r & 7).
-// One gather instruction of wave w fills rows 8w..8w+7 of one group: 1 KB,
+// One gather instruction of a wave fills rows 8w'..8w'+7 of one group: 1 KB,
 // written in lane order.
 constexpr int MLA_GROUPB = MLA_TILE * 128;  // 4,096 bytes per column group
 
@@ -83,34 +92,43 @@ __device__ inline int tile_off(int row, int chunk) {
 }
 
 struct MlaTileState {
-  f32x4 o[DC / 16];
+  f32x4 o[MLA_VBLK];
   float m_run;
   float l_part;
 };
 
-// Gather tile t of the selection straight into LDS.  Thread (wave w, lane l)
-// fetches row 8w + l/8 of the tile: for each column group i, the 16-byte
-// chunk ((l % 8) ^ (row & 7)) + 8i, which lands at lane slot l of the 1 KB
-// block of (group i, rows 8w..8w+7).
-__device__ inline void mla_issue(uint8_t* buf, const uint16_t* kv, const int* sel_l, int nent, int t, int lane,
-                                 int wave_u) {
-  const int row = wave_u * 8 + (lane >> 3);
-  const int j = t * MLA_TILE + row;
-  const int pos = j < nent ? sel_l[j] : -1;
-  const uint16_t* src = kv + (int64_t)(pos >= 0 ? pos : 0) * D + (((lane & 7) ^ (row & 7)) << 3);
-  uint8_t* dst = buf + wave_u * 1024;
+// Gather tile t into LDS.  A tile is 36 blocks of 1 KB (column group i,
+// row octet o); every wave issues exactly MLA_WAVE_DMAS gather instructions
+// per tile -- blocks 5w .. 5w+4, where ids past the last block re-load block
+// 35's rows into a scratch slot -- so all waves keep the same number of
+// gathers in flight.  Within a block, lane l fetches row 8o + l/8, 16-byte
+// chunk ((l % 8) ^ (row & 7)) + 8i, landing at lane slot l.
+constexpr int MLA_BLOCKS = (D * 2 / 128) * (MLA_TILE / 8);  // 36
+constexpr int MLA_WAVE_DMAS = 5;
+static_assert(MLA_WAVE_DMAS * (MLA_THREADS / 64) >= MLA_BLOCKS, "every block must be gathered");
+
+__device__ __forceinline__ void mla_issue(uint8_t* buf, uint8_t* dummy, const uint16_t* kv, const int* sel_l,
+                                          int t, int lane, int wave_u) {
 #pragma unroll
-  for (int i = 0; i < D * 2 / 128; ++i)
-    __builtin_amdgcn_global_load_lds((const void*)(src + i * 64), (lds_void*)(dst + i * MLA_GROUPB), 16, 0, 0);
+  for (int jj = 0; jj < MLA_WAVE_DMAS; ++jj) {
+    const int id = wave_u * MLA_WAVE_DMAS + jj;
+    const int blk = min(id, MLA_BLOCKS - 1);
+    const int gi = blk >> 2;
+    const int oc = blk & 3;
+    const int row = oc * 8 + (lane >> 3);
+    const int pos = sel_l[t * MLA_TILE + row];
+    const uint16_t* src = kv + (int64_t)(pos >= 0 ? pos : 0) * D + (gi * 8 + ((lane & 7) ^ (row & 7))) * 8;
+    uint8_t* dst = id < MLA_BLOCKS ? buf + gi * MLA_GROUPB + oc * 1024 : dummy;
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)dst, 16, 0, 0);
+  }
 }
 
-// One tile: S^T = K.Q^T, online softmax, O^T += V^T.P^T.
-__device__ inline void mla_tile(MlaTileState& st, const uint8_t* tile, const bf16x8 (&qf)[D / 32],
-                                const int* sel_l, int nent, int t0, int n16, int g, float scale_log2) {
+// Partial S^T (32 positions x 16 heads) over this wave's half of the
+// contraction; lane (n16, g) gets positions 16*mb + 4g + i of head n16.
+__device__ __forceinline__ void mla_partial_logits(const uint8_t* tile, const bf16x8 (&qf)[MLA_KSTEPS], int d, int n16,
+                                          int g, f32x4 (&s)[2]) {
   // Row r's logical chunk 4t+g lies in column group t/2 at in-group chunk
-  // 4*(t%2) + g: two base addresses per row plus an immediate 4096*(t/2).
-  // Loads run two steps ahead of the MFMAs; each block keeps two
-  // accumulator chains.
+  // 4*(t%2) + g.  Loads run two steps ahead; each block keeps two chains.
   const uint8_t* ev[2];
   const uint8_t* od[2];
 #pragma unroll
@@ -119,7 +137,9 @@ __device__ inline void mla_tile(MlaTileState& st, const uint8_t* tile, const bf1
     ev[mb] = tile + tile_off(row, g);
     od[mb] = tile + tile_off(row, 4 + g);
   }
-  auto kfrag = [&](int mb, int t) -> u32x4 {
+  const int t0 = d * MLA_KSTEPS;
+  auto kfrag = [&](int mb, int tt) -> u32x4 {
+    const int t = t0 + tt;
     return *(const u32x4*)(((t & 1) ? od[mb] : ev[mb]) + (t >> 1) * MLA_GROUPB);
   };
   f32x4 acc[2][2];
@@ -131,29 +151,29 @@ __device__ inline void mla_tile(MlaTileState& st, const uint8_t* tile, const bf1
   ring[1][0] = kfrag(0, 1);
   ring[1][1] = kfrag(1, 1);
 #pragma unroll
-  for (int t = 0; t < D / 32; ++t) {
-    if (t + 2 < D / 32) {
-      ring[(t + 2) % 3][0] = kfrag(0, t + 2);
-      ring[(t + 2) % 3][1] = kfrag(1, t + 2);
+  for (int tt = 0; tt < MLA_KSTEPS; ++tt) {
+    if (tt + 2 < MLA_KSTEPS) {
+      ring[(tt + 2) % 3][0] = kfrag(0, tt + 2);
+      ring[(tt + 2) % 3][1] = kfrag(1, tt + 2);
     }
-    acc[0][t & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ring[t % 3][0]), qf[t], acc[0][t & 1], 0, 0, 0);
-    acc[1][t & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ring[t % 3][1]), qf[t], acc[1][t & 1], 0, 0, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMAs
+    acc[0][tt & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ring[tt % 3][0]), qf[tt], acc[0][tt & 1], 0, 0, 0);
+    acc[1][tt & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ring[tt % 3][1]), qf[tt], acc[1][tt & 1], 0, 0, 0);
   }
-  f32x4 s[2];
   s[0] = acc[0][0] + acc[0][1];
   s[1] = acc[1][0] + acc[1][1];
-  __builtin_amdgcn_sched_barrier(0);
-  // lane holds one head and positions 16*mb + 4g + i
+}
+
+// Online softmax over the tile's logits and O^T += V_tile^T . P^T for this
+// wave's 256 latent columns.
+__device__ __forceinline__ void mla_softmax_pv(MlaTileState& st, const uint8_t* tile, const f32x4 (&s)[2], const int* sel_l,
+                                               int t0, int d, int n16, int g, float scale_log2) {
   float x[8];
   float tmax = -INFINITY;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int j = t0 + 16 * mb + 4 * g + i;
-      const bool ok = j < nent && sel_l[j] >= 0;
+      const bool ok = sel_l[t0 + 16 * mb + 4 * g + i] >= 0;
       const float v = ok ? s[mb][i] * scale_log2 : -INFINITY;
       x[mb * 4 + i] = v;
       tmax = fmaxf(tmax, v);
@@ -166,7 +186,7 @@ __device__ inline void mla_tile(MlaTileState& st, const uint8_t* tile, const bf1
     if (resc) st.m_run = tmax;
     st.l_part *= alpha;
 #pragma unroll
-    for (int db = 0; db < DC / 16; ++db) st.o[db] *= alpha;
+    for (int vb = 0; vb < MLA_VBLK; ++vb) st.o[vb] *= alpha;
   }
   float pv[8];
 #pragma unroll
@@ -180,30 +200,27 @@ __device__ inline void mla_tile(MlaTileState& st, const uint8_t* tile, const bf1
   pk[2] = pack_bf16x2(pv[4], pv[5]);
   pk[3] = pack_bf16x2(pv[6], pv[7]);
   const bf16x8 pb = as_bf16x8(pk);
-  __builtin_amdgcn_sched_barrier(0);
 
-  // O^T += V_tile^T . P^T.  k-slot e of lane group g is tile row
-  // (e < 4 ? 4g + e : 16 + 4g + e - 4).  A transposing LDS read gives lane
-  // i of a 16-lane group element i%4 of source lane 4j + i/4, so source
-  // lane s points at row 4g + s/4 (+16) and latent column 16db + 4(s%4).
-  // Column 16db + sdim lies in column group db/4, in-group chunk
-  // 2*(db%4) + sdim/8: four base addresses per source row plus an
-  // immediate 4096*(db/4).
+  // k-slot e of lane group g is tile row (e < 4 ? 4g + e : 16 + 4g + e - 4).
+  // A transposing LDS read gives lane i of a 16-lane group element i%4 of
+  // source lane 4j + i/4, so source lane s points at row 4g + s/4 (+16) and
+  // latent column c0 + 4(s%4).  Column 256d + 16vb + sdim lies in column
+  // group 4d + vb/4 at in-group chunk 2*(vb%4) + sdim/8.
   const int srow0 = 4 * g + (n16 >> 2);
   const int srow1 = srow0 + 16;
   const int sdim = 4 * (n16 & 3);
-  const int c0 = sdim >> 3;
+  const int c0 = 32 * d + (sdim >> 3);
   const int boff = (sdim & 7) << 1;
   const uint8_t* b0[4];
   const uint8_t* b1[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    b0[u] = tile + tile_off(srow0, 2 * u + c0) + boff;
-    b1[u] = tile + tile_off(srow1, 2 * u + c0) + boff;
+    b0[u] = tile + tile_off(srow0, c0 + 2 * u) + boff;
+    b1[u] = tile + tile_off(srow1, c0 + 2 * u) + boff;
   }
-  auto vfrag = [&](int db) -> bf16x8 {
-    const int u = db & 3;
-    const int imm = (db >> 2) * MLA_GROUPB;
+  auto vfrag = [&](int vb) -> bf16x8 {
+    const int u = vb & 3;
+    const int imm = (vb >> 2) * MLA_GROUPB;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b0[u] + imm));
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b1[u] + imm));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -213,86 +230,122 @@ __device__ inline void mla_tile(MlaTileState& st, const uint8_t* tile, const bf1
   vr[1] = vfrag(1);
   vr[2] = vfrag(2);
 #pragma unroll
-  for (int db = 0; db < DC / 16; ++db) {
-    if (db + 3 < DC / 16) vr[(db + 3) & 3] = vfrag(db + 3);
-    st.o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vr[db & 3], pb, st.o[db], 0, 0, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);  // 2 LDS transpose reads
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // 1 MFMA
+  for (int vb = 0; vb < MLA_VBLK; ++vb) {
+    if (vb + 3 < MLA_VBLK) vr[(vb + 3) & 3] = vfrag(vb + 3);
+    st.o[vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vr[vb & 3], pb, st.o[vb], 0, 0, 0);
   }
 }
 
-__global__ __launch_bounds__(MLA_THREADS, 2) void mla_bf16_kernel(MlaParams p) {
-  // two distinct arrays, so that reads of one tile are known not to alias
-  // the asynchronous gather into the other
+// Workgroup barrier without a memory fence.  __syncthreads() would make
+// every wave wait for all of its outstanding gathers (they count as vector
+// memory operations); here each wave first waits for exactly what it must
+// publish (see the callers), and the empty asm statements keep the compiler
+// from moving memory accesses across the barrier.
+__device__ __forceinline__ void barrier_no_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__global__ __launch_bounds__(MLA_THREADS, 1) void mla_bf16_kernel(MlaParams p) {
+  // three distinct arrays, so that reads of one tile are known not to alias
+  // the asynchronous gathers into the others
   __shared__ __attribute__((aligned(16))) uint8_t tile0[MLA_TILEB];
   __shared__ __attribute__((aligned(16))) uint8_t tile1[MLA_TILEB];
+  __shared__ __attribute__((aligned(16))) uint8_t tile2[MLA_TILEB];
+  __shared__ __attribute__((aligned(16))) uint8_t scratch_blk[1024];  // target of the filler gathers
   __shared__ int sel_l[MLA_SPLIT_MAX];
+  __shared__ __attribute__((aligned(16))) f32x4 xpart[8][64][2];  // partial logits per wave
   const int split = blockIdx.x;
   const int q = blockIdx.y;
   const int layer = blockIdx.z;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hgrp = wave_u & 3;
+  const int d = wave_u >> 2;
   const int n16 = lane & 15;
   const int g = lane >> 4;
   const QueryRange r = query_range(p.b, q);
   const int j_begin = split * p.split_len;
   const int nent = max(0, min(j_begin + p.split_len, p.k) - j_begin);
   const int ntiles = r.n > 0 ? (nent + MLA_TILE - 1) / MLA_TILE : 0;
-  const int head = wave_u * 16 + n16;
+  const int head = hgrp * 16 + n16;
 
-  // this split's selected positions; entries outside [0, n) become -1
+  // this split's selected positions, padded with -1 to whole tiles;
+  // entries outside [0, n) become -1
   {
     const int32_t* sel = p.idx + (int64_t)q * p.k + j_begin;
-    for (int j = tid; j < nent; j += MLA_THREADS) {
-      const int pos = sel[j];
+    for (int j = tid; j < ntiles * MLA_TILE; j += MLA_THREADS) {
+      const int pos = j < nent ? sel[j] : -1;
       sel_l[j] = (pos >= 0 && pos < r.n) ? pos : -1;
     }
   }
-  // Q_w^T as the B operand: head `head`, contraction slots t*32 + 8g + [0,8)
-  bf16x8 qf[D / 32];
+  // Q^T (this wave's heads and half of the contraction) as the B operand:
+  // head `head`, contraction slots (9d + tt)*32 + 8g + [0,8)
+  bf16x8 qf[MLA_KSTEPS];
   {
-    const uint16_t* qp = (const uint16_t*)p.L.q[layer] + ((int64_t)q * H + head) * D + g * 8;
+    const uint16_t* qp = (const uint16_t*)p.L.q[layer] + ((int64_t)q * H + head) * D + d * (D / 2) + g * 8;
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t) qf[t] = as_bf16x8(load16(qp + t * 32));
+    for (int tt = 0; tt < MLA_KSTEPS; ++tt) qf[tt] = as_bf16x8(load16(qp + tt * 32));
   }
   const uint16_t* kv = (const uint16_t*)p.L.kv[layer] + r.row0 * D;
   MlaTileState st;
 #pragma unroll
-  for (int db = 0; db < DC / 16; ++db) st.o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int vb = 0; vb < MLA_VBLK; ++vb) st.o[vb] = f32x4{0.f, 0.f, 0.f, 0.f};
   st.m_run = -INFINITY;
   st.l_part = 0.0f;
   __syncthreads();
 
-  if (ntiles > 0) mla_issue(tile0, kv, sel_l, nent, 0, lane, wave_u);
-  for (int it = 0; it < ntiles; it += 2) {
-    __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): this thread's part of tile `it` landed
-    __syncthreads();                     // every part landed; the other buffer is free
-    if (it + 1 < ntiles) mla_issue(tile1, kv, sel_l, nent, it + 1, lane, wave_u);
-    mla_tile(st, tile0, qf, sel_l, nent, it * MLA_TILE, n16, g, p.scale_log2);
+  // tile t goes to buffer t % 3; two tiles are gathered ahead
+  if (ntiles > 0) mla_issue(tile0, scratch_blk, kv, sel_l, 0, lane, wave_u);
+  if (ntiles > 1) mla_issue(tile1, scratch_blk, kv, sel_l, 1, lane, wave_u);
+
+  auto step = [&](int it, const uint8_t* cur, uint8_t* nxt2) __attribute__((always_inline)) {
+    // Every wave waits for its own part of tile `it` (the gathers of tile
+    // it+1 stay in flight); after the barrier the tile is complete and tile
+    // it-1's buffer is free for tile it+2.
+    if (it + 1 < ntiles)
+      __builtin_amdgcn_s_waitcnt(0x0075);  // vmcnt(5) lgkmcnt(0)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    barrier_no_fence();
+    if (it + 2 < ntiles) mla_issue(nxt2, scratch_blk, kv, sel_l, it + 2, lane, wave_u);
+    f32x4 s[2];
+    mla_partial_logits(cur, qf, d, n16, g, s);
+    xpart[wave_u][lane][0] = s[0];
+    xpart[wave_u][lane][1] = s[1];
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): partial logits written
+    barrier_no_fence();
+    s[0] += xpart[wave_u ^ 4][lane][0];
+    s[1] += xpart[wave_u ^ 4][lane][1];
+    mla_softmax_pv(st, cur, s, sel_l, it * MLA_TILE, d, n16, g, p.scale_log2);
+  };
+  for (int it = 0; it < ntiles; it += 3) {
+    step(it, tile0, tile2);
     if (it + 1 >= ntiles) break;
-    __builtin_amdgcn_s_waitcnt(0x3F70);
-    __syncthreads();
-    if (it + 2 < ntiles) mla_issue(tile0, kv, sel_l, nent, it + 2, lane, wave_u);
-    mla_tile(st, tile1, qf, sel_l, nent, (it + 1) * MLA_TILE, n16, g, p.scale_log2);
+    step(it + 1, tile1, tile0);
+    if (it + 2 >= ntiles) break;
+    step(it + 2, tile2, tile1);
   }
 
   float l_part = st.l_part;
   l_part += __shfl_xor(l_part, 16);
   l_part += __shfl_xor(l_part, 32);
   const int64_t qh = (int64_t)q * H + head;
+  const int col0 = d * (DC / 2);
   if (p.nsplit == 1) {
     const float inv = l_part > 0.0f ? 1.0f / l_part : 0.0f;
 #pragma unroll
-    for (int db = 0; db < DC / 16; ++db) store_out4(p, layer, qh * DC + db * 16 + 4 * g, st.o[db] * inv);
-    if (g == 0 && p.L.lse[layer])
+    for (int vb = 0; vb < MLA_VBLK; ++vb) store_out4(p, layer, qh * DC + col0 + vb * 16 + 4 * g, st.o[vb] * inv);
+    if (d == 0 && g == 0 && p.L.lse[layer])
       p.L.lse[layer][qh] = l_part > 0.0f ? (st.m_run + log2f(l_part)) * LN2 : -INFINITY;
   } else {
     const int64_t slot = ((int64_t)split * p.n_layers + layer) * p.b.nq * H + qh;
-    float* acc = p.part_acc + slot * DC;
+    float* acc = p.part_acc + slot * DC + col0;
 #pragma unroll
-    for (int db = 0; db < DC / 16; ++db) *(f32x4*)(acc + db * 16 + 4 * g) = st.o[db];
-    if (g == 0) {
+    for (int vb = 0; vb < MLA_VBLK; ++vb) *(f32x4*)(acc + vb * 16 + 4 * g) = st.o[vb];
+    if (d == 0 && g == 0) {
       p.part_ml[slot * 2 + 0] = l_part > 0.0f ? st.m_run : -INFINITY;
       p.part_ml[slot * 2 + 1] = l_part;
     }
@@ -424,7 +477,7 @@ __global__ __launch_bounds__(CMB_THREADS) void mla_combine(MlaParams p) {
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-constexpr int MLA_TARGET_BLOCKS = 512;  // two workgroups per compute unit
+constexpr int MLA_TARGET_BLOCKS = 256;  // one workgroup per compute unit
 
 int mla_num_splits(int dtype, int nq, int k, int n_layers) {
   const int tile = dtype == 0 ? MLA32_TILE : MLA_TILE;
