@@ -61,6 +61,8 @@ extern "C" {
 #define DSA_ROW 576         /* cache row = latent + rotary key        */
 #define DSA_TOPK_MAX 2048   /* largest supported k (the pages' 2,048) */
 #define DSA_MAX_LAYERS 16   /* largest n_layers of the fused call     */
+#define DSA_MAX_LEN 3728270 /* longest sequence: its 1,152-byte bf16
+                               cache rows are addressed with 32 bits   */
 
 typedef enum {
   DSA_OK = 0,
@@ -78,8 +80,9 @@ typedef enum { DSA_F32 = 0, DSA_BF16 = 1 } dsa_dtype_t;
 /*
  * A batch of queries over one or more sequences.
  *   nq, nseq, max_len : host integers.  nq >= 0 (0 is a no-op), nseq >= 1,
- *                       max_len >= 1 bounds every sequence length and sizes
- *                       the launch grids.
+ *                       1 <= max_len <= DSA_MAX_LEN bounds every sequence
+ *                       length and sizes the launch grids (larger:
+ *                       DSA_ERR_UNSUPPORTED).
  *   q_seq  [nq]   (device) sequence of each query, in [0, nseq).
  *   q_pos  [nq]   (device) absolute position of each query.
  *   seq_len[nseq] (device) cached positions of each sequence, <= max_len.

@@ -39,6 +39,8 @@ int check_batch(const dsa_batch_t* b, dsa::BatchDev* out) {
   if (b->nq < 0) return fail(DSA_ERR_SHAPE, "nq = %d < 0", b->nq);
   if (b->nseq < 1) return fail(DSA_ERR_SHAPE, "nseq = %d < 1", b->nseq);
   if (b->max_len < 1) return fail(DSA_ERR_SHAPE, "max_len = %d < 1", b->max_len);
+  if (b->max_len > DSA_MAX_LEN)
+    return fail(DSA_ERR_UNSUPPORTED, "max_len = %d > %d", b->max_len, DSA_MAX_LEN);
   if (b->nq > 0) {
     if (!b->q_seq || !b->q_pos || !b->seq_len || !b->seq_row0)
       return fail(DSA_ERR_NULL, "a batch index array is NULL");
@@ -227,11 +229,16 @@ int32_t dsa_mla_decode_fused(const dsa_batch_t* batch, int32_t dtype, const void
   float* scores = (float*)base;
   int32_t* idx = idx_out ? idx_out : (int32_t*)(base + off_idx);
   hipStream_t s = as_stream(stream);
-  if ((st = hip_status(dsa::launch_index_score(b, dtype, q_idx, w_idx, k_idx, scores, b.max_len, s),
+  // The indexer launch also clears the top-k histograms of this call, so
+  // the workspace needs no clearing by the caller and no launch of its own.
+  dsa::ZeroSpans z;
+  z.s[0] = dsa::topk_zero_span(base + off_topk, b.nq, b.max_len);
+  z.s[1] = dsa::ZeroSpan{nullptr, 0, 0};
+  if ((st = hip_status(dsa::launch_index_score(b, dtype, q_idx, w_idx, k_idx, scores, b.max_len, s, &z),
                        "fused: index score launch")))
     return st;
   if ((st = hip_status(dsa::launch_topk(b, scores, b.max_len, k, idx, nullptr, base + off_topk,
-                                        off_mla - off_topk, s),
+                                        off_mla - off_topk, s, true),
                        "fused: top-k launch")))
     return st;
   return hip_status(dsa::launch_mla(b, dtype, L, n_layers, idx, k, scale, out_dtype, base + off_mla,

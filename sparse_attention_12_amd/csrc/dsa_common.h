@@ -16,6 +16,7 @@ constexpr int D = 576;    // cache row
 constexpr int KMAX = 2048;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -56,16 +57,12 @@ __device__ inline QueryRange query_range(const BatchDev& b, int q) {
 
 __device__ inline float bf16_to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
 
-__device__ inline uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-// Two floats -> packed bf16 pair (low half = a).
+// Two floats -> packed bf16 pair (low half = a), rounded to nearest even by
+// the gfx950 conversion instruction (v_cvt_pk_bf16_f32).
+typedef __bf16 hw_bf16x2 __attribute__((ext_vector_type(2)));
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
-  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, hw_bf16x2));
 }
 
 // Unsigned key whose order is the order of the float scores; -0.0 and +0.0

@@ -18,6 +18,20 @@
 
 namespace dsa {
 
+// Zeroes query q's words of every span (see ZeroSpans in kernels.h).
+__device__ inline void zero_query_spans(const ZeroSpans& z, int q, int tid, int nthreads) {
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    if (z.s[s].base == nullptr) continue;
+    uint32_t* p = z.s[s].base + (int64_t)q * z.s[s].stride;
+    for (int i = tid; i < z.s[s].count; i += nthreads) p[i] = 0u;
+  }
+}
+
+__global__ __launch_bounds__(256) void zero_spans_kernel(ZeroSpans z) {
+  zero_query_spans(z, blockIdx.x, threadIdx.x, 256);
+}
+
 // ---------------------------------------------------------------------------
 // decode, bf16
 // ---------------------------------------------------------------------------
@@ -37,8 +51,9 @@ struct KeyTile {
 
 __global__ __launch_bounds__(IDX_DEC_THREADS) void idx_decode_bf16(
     BatchDev b, const uint16_t* __restrict__ qI, const float* __restrict__ w,
-    const uint16_t* __restrict__ kI, float* __restrict__ scores, int64_t ld, int chunk) {
+    const uint16_t* __restrict__ kI, float* __restrict__ scores, int64_t ld, int chunk, ZeroSpans z) {
   const int q = blockIdx.y;
+  if (blockIdx.x == 0) zero_query_spans(z, q, threadIdx.x, IDX_DEC_THREADS);
   const QueryRange r = query_range(b, q);
   const int base = blockIdx.x * chunk;
   if (base >= r.n) return;
@@ -127,10 +142,11 @@ constexpr int IDX_F32_THREADS = 256;
 
 __global__ __launch_bounds__(IDX_F32_THREADS) void idx_decode_f32(
     BatchDev b, const float* __restrict__ qI, const float* __restrict__ w,
-    const float* __restrict__ kI, float* __restrict__ scores, int64_t ld) {
+    const float* __restrict__ kI, float* __restrict__ scores, int64_t ld, ZeroSpans z) {
   __shared__ float qs[HI * DI];
   __shared__ float wsh[HI];
   const int q = blockIdx.y;
+  if (blockIdx.x == 0) zero_query_spans(z, q, threadIdx.x, IDX_F32_THREADS);
   const QueryRange r = query_range(b, q);
   const int base = blockIdx.x * IDX_F32_THREADS;
   if (base >= r.n) return;
@@ -260,14 +276,26 @@ static int decode_chunk(int nq, int max_len) {
   return chunk;
 }
 
+hipError_t launch_zero(const ZeroSpans& z, int nq, hipStream_t st) {
+  if (nq == 0 || (z.s[0].base == nullptr && z.s[1].base == nullptr)) return hipSuccess;
+  hipLaunchKernelGGL(zero_spans_kernel, dim3(nq), dim3(256), 0, st, z);
+  return hipGetLastError();
+}
+
 hipError_t launch_index_score(const BatchDev& b, int dtype, const void* qI, const float* w,
-                              const void* kI, float* scores, int64_t ld, hipStream_t st) {
+                              const void* kI, float* scores, int64_t ld, hipStream_t st, const ZeroSpans* zp) {
   if (b.nq == 0) return hipSuccess;
+  ZeroSpans z;
+  z.s[0] = ZeroSpan{nullptr, 0, 0};
+  z.s[1] = ZeroSpan{nullptr, 0, 0};
+  if (zp) z = *zp;
   if (dtype == 0) {
     dim3 grid((b.max_len + IDX_F32_THREADS - 1) / IDX_F32_THREADS, b.nq);
     hipLaunchKernelGGL(idx_decode_f32, grid, dim3(IDX_F32_THREADS), 0, st, b, (const float*)qI, w,
-                       (const float*)kI, scores, ld);
+                       (const float*)kI, scores, ld, z);
   } else if (b.nseq == 1 && b.nq >= PF_QB) {
+    hipError_t e = launch_zero(z, b.nq, st);
+    if (e != hipSuccess) return e;
     dim3 grid((b.max_len + PF_KC - 1) / PF_KC, (b.nq + PF_QB - 1) / PF_QB);
     hipLaunchKernelGGL(idx_prefill_bf16, grid, dim3(PF_THREADS), 0, st, b, (const uint16_t*)qI, w,
                        (const uint16_t*)kI, scores, ld);
@@ -275,7 +303,7 @@ hipError_t launch_index_score(const BatchDev& b, int dtype, const void* qI, cons
     const int chunk = decode_chunk(b.nq, b.max_len);
     dim3 grid((b.max_len + chunk - 1) / chunk, b.nq);
     hipLaunchKernelGGL(idx_decode_bf16, grid, dim3(IDX_DEC_THREADS), 0, st, b,
-                       (const uint16_t*)qI, w, (const uint16_t*)kI, scores, ld, chunk);
+                       (const uint16_t*)qI, w, (const uint16_t*)kI, scores, ld, chunk, z);
   }
   return hipGetLastError();
 }

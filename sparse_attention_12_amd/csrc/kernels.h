@@ -10,14 +10,33 @@ namespace dsa {
 
 constexpr int MLA_MAX_LAYERS = 16;
 
-// Indexer scores of every query over its candidates (indexer.hip).
+// Per-query blocks of 32-bit words that must be zero before a later kernel
+// runs: query q owns words [q*stride, q*stride + count) of `base`.
+struct ZeroSpan {
+  uint32_t* base;
+  int stride;
+  int count;
+};
+struct ZeroSpans {
+  ZeroSpan s[2];
+};
+
+// Zeroes every span (one workgroup per query).
+hipError_t launch_zero(const ZeroSpans& z, int nq, hipStream_t st);
+
+// Indexer scores of every query over its candidates (indexer.hip).  The
+// first workgroup of each query also zeroes that query's words of `z`
+// (nobody else touches them during the launch).
 hipError_t launch_index_score(const BatchDev& b, int dtype, const void* qI, const float* w,
-                              const void* kI, float* scores, int64_t ld, hipStream_t st);
+                              const void* kI, float* scores, int64_t ld, hipStream_t st,
+                              const ZeroSpans* z = nullptr);
 
 // Top-k selection (topk.hip).  ws may be NULL when topk_workspace_bytes() == 0.
+// With ws_zeroed, the words topk_zero_span() describes are already zero.
 size_t topk_workspace_bytes(int nq, int max_len, int k);
+ZeroSpan topk_zero_span(void* ws, int nq, int max_len);
 hipError_t launch_topk(const BatchDev& b, const float* scores, int64_t ld, int k, int32_t* idx,
-                       int32_t* count, void* ws, size_t ws_bytes, hipStream_t st);
+                       int32_t* count, void* ws, size_t ws_bytes, hipStream_t st, bool ws_zeroed = false);
 
 // Sparse MLA over a shared selection for n_layers layers (mla.hip).
 struct MlaLayers {

@@ -107,8 +107,21 @@ constexpr int MLA_BLOCKS = (D * 2 / 128) * (MLA_TILE / 8);  // 36
 constexpr int MLA_WAVE_DMAS = 5;
 static_assert(MLA_WAVE_DMAS * (MLA_THREADS / 64) >= MLA_BLOCKS, "every block must be gathered");
 
-__device__ __forceinline__ void mla_issue(uint8_t* buf, uint8_t* dummy, const uint16_t* kv, const int* sel_l,
-                                          int t, int lane, int wave_u) {
+// Selected positions of the rows this lane gathers for tile t (read ahead of
+// the gathers, so no gather waits on an LDS read).
+__device__ __forceinline__ void mla_rows(int (&pos)[MLA_WAVE_DMAS], const int* sel_l, int t, int lane, int wave_u) {
+#pragma unroll
+  for (int jj = 0; jj < MLA_WAVE_DMAS; ++jj) {
+    const int blk = min(wave_u * MLA_WAVE_DMAS + jj, MLA_BLOCKS - 1);
+    pos[jj] = sel_l[t * MLA_TILE + (blk & 3) * 8 + (lane >> 3)];
+  }
+}
+
+// The gathers are buffer loads with an LDS destination (MUBUF, not FLAT, so
+// the compiler keeps precise LDS wait counts around them) addressed from the
+// sequence's first row; sequences up to 2^32 bytes of rows are supported.
+__device__ __forceinline__ void mla_issue(uint8_t* buf, uint8_t* dummy, __amdgpu_buffer_rsrc_t kv,
+                                          const int (&pos)[MLA_WAVE_DMAS], int lane, int wave_u) {
 #pragma unroll
   for (int jj = 0; jj < MLA_WAVE_DMAS; ++jj) {
     const int id = wave_u * MLA_WAVE_DMAS + jj;
@@ -116,10 +129,9 @@ __device__ __forceinline__ void mla_issue(uint8_t* buf, uint8_t* dummy, const ui
     const int gi = blk >> 2;
     const int oc = blk & 3;
     const int row = oc * 8 + (lane >> 3);
-    const int pos = sel_l[t * MLA_TILE + row];
-    const uint16_t* src = kv + (int64_t)(pos >= 0 ? pos : 0) * D + (gi * 8 + ((lane & 7) ^ (row & 7))) * 8;
+    const uint32_t off = (uint32_t)max(pos[jj], 0) * (uint32_t)MLA_ROWB + (uint32_t)(gi * 8 + ((lane & 7) ^ (row & 7))) * 16u;
     uint8_t* dst = id < MLA_BLOCKS ? buf + gi * MLA_GROUPB + oc * 1024 : dummy;
-    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)dst, 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kv, (lds_void*)dst, 16, off, 0, 0, 0);
   }
 }
 
@@ -159,6 +171,15 @@ __device__ __forceinline__ void mla_partial_logits(const uint8_t* tile, const bf
     acc[0][tt & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ring[tt % 3][0]), qf[tt], acc[0][tt & 1], 0, 0, 0);
     acc[1][tt & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ring[tt % 3][1]), qf[tt], acc[1][tt & 1], 0, 0, 0);
   }
+  // keep the loads two steps ahead of their use: 4 reads, then (2 reads,
+  // 2 products) per step, then the last 4 products
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int tt = 0; tt + 2 < MLA_KSTEPS; ++tt) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   s[0] = acc[0][0] + acc[0][1];
   s[1] = acc[1][0] + acc[1][1];
 }
@@ -182,7 +203,7 @@ __device__ __forceinline__ void mla_softmax_pv(MlaTileState& st, const uint8_t* 
   tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
   const bool resc = tmax > st.m_run + MLA_RESCALE_SLACK;
   if (__any(resc)) {
-    const float alpha = resc ? exp2f(st.m_run - tmax) : 1.0f;
+    const float alpha = resc ? __builtin_amdgcn_exp2f(st.m_run - tmax) : 1.0f;
     if (resc) st.m_run = tmax;
     st.l_part *= alpha;
 #pragma unroll
@@ -191,7 +212,9 @@ __device__ __forceinline__ void mla_softmax_pv(MlaTileState& st, const uint8_t* 
   float pv[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    pv[e] = (x[e] == -INFINITY) ? 0.0f : exp2f(x[e] - st.m_run);
+    // hardware exp2 (no subnormal results: weights below 2^-126 vanish)
+    const float ev = __builtin_amdgcn_exp2f(x[e] - st.m_run);
+    pv[e] = (x[e] == -INFINITY) ? 0.0f : ev;
     st.l_part += pv[e];
   }
   u32x4 pk;
@@ -200,6 +223,7 @@ __device__ __forceinline__ void mla_softmax_pv(MlaTileState& st, const uint8_t* 
   pk[2] = pack_bf16x2(pv[4], pv[5]);
   pk[3] = pack_bf16x2(pv[6], pv[7]);
   const bf16x8 pb = as_bf16x8(pk);
+  __builtin_amdgcn_sched_barrier(0);
 
   // k-slot e of lane group g is tile row (e < 4 ? 4g + e : 16 + 4g + e - 4).
   // A transposing LDS read gives lane i of a 16-lane group element i%4 of
@@ -234,6 +258,14 @@ __device__ __forceinline__ void mla_softmax_pv(MlaTileState& st, const uint8_t* 
     if (vb + 3 < MLA_VBLK) vr[(vb + 3) & 3] = vfrag(vb + 3);
     st.o[vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vr[vb & 3], pb, st.o[vb], 0, 0, 0);
   }
+  // transposing reads three blocks ahead of the products
+  __builtin_amdgcn_sched_group_barrier(0x100, 6, 1);
+#pragma unroll
+  for (int vb = 0; vb + 3 < MLA_VBLK; ++vb) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 3, 1);
 }
 
 // Workgroup barrier without a memory fence.  __syncthreads() would make
@@ -272,11 +304,12 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_bf16_kernel(MlaParams p) {
   const int ntiles = r.n > 0 ? (nent + MLA_TILE - 1) / MLA_TILE : 0;
   const int head = hgrp * 16 + n16;
 
-  // this split's selected positions, padded with -1 to whole tiles;
-  // entries outside [0, n) become -1
+  // this split's selected positions, padded with -1 to whole tiles (at
+  // least two: tiles 0 and 1 are always gathered); entries outside [0, n)
+  // become -1
   {
     const int32_t* sel = p.idx + (int64_t)q * p.k + j_begin;
-    for (int j = tid; j < ntiles * MLA_TILE; j += MLA_THREADS) {
+    for (int j = tid; j < max(ntiles, 2) * MLA_TILE; j += MLA_THREADS) {
       const int pos = j < nent ? sel[j] : -1;
       sel_l[j] = (pos >= 0 && pos < r.n) ? pos : -1;
     }
@@ -289,7 +322,11 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_bf16_kernel(MlaParams p) {
 #pragma unroll
     for (int tt = 0; tt < MLA_KSTEPS; ++tt) qf[tt] = as_bf16x8(load16(qp + tt * 32));
   }
-  const uint16_t* kv = (const uint16_t*)p.L.kv[layer] + r.row0 * D;
+  // buffer resource over exactly this sequence's rows (raw addressing): a
+  // gather outside them reads zeros and touches no memory
+  const __amdgpu_buffer_rsrc_t kv = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const uint16_t*)p.L.kv[layer] + r.row0 * D), (short)0, (int)((uint32_t)r.n * (uint32_t)MLA_ROWB),
+      0x00020000);
   MlaTileState st;
 #pragma unroll
   for (int vb = 0; vb < MLA_VBLK; ++vb) st.o[vb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -297,9 +334,24 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_bf16_kernel(MlaParams p) {
   st.l_part = 0.0f;
   __syncthreads();
 
-  // tile t goes to buffer t % 3; two tiles are gathered ahead
-  if (ntiles > 0) mla_issue(tile0, scratch_blk, kv, sel_l, 0, lane, wave_u);
-  if (ntiles > 1) mla_issue(tile1, scratch_blk, kv, sel_l, 1, lane, wave_u);
+  // tile t goes to buffer t % 3; two tiles are gathered ahead.  Tiles 0
+  // and 1 are issued whatever the tile count (a missing tile gathers rows
+  // of position -1, which the buffer range check turns into zeros without
+  // a memory access), so the wait below is the same on every path.
+  int rows[MLA_WAVE_DMAS];
+  mla_rows(rows, sel_l, 0, lane, wave_u);
+  mla_issue(tile0, scratch_blk, kv, rows, lane, wave_u);
+  mla_rows(rows, sel_l, 1, lane, wave_u);
+  mla_issue(tile1, scratch_blk, kv, rows, lane, wave_u);
+  mla_rows(rows, sel_l, min(2, max(ntiles, 1) - 1), lane, wave_u);
+  // Q (loaded before the gathers) must be in registers before the loop:
+  // wait for it alone, leaving both tiles' gathers in flight
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * MLA_WAVE_DMAS));  // vmcnt(10)
+  // From here on Q counts as computed, not loaded: otherwise the compiler
+  // drains every gather before the loop because the loop reads registers
+  // loaded outside it.
+#pragma unroll
+  for (int tt = 0; tt < MLA_KSTEPS; ++tt) asm volatile("" : "+v"(qf[tt]));
 
   auto step = [&](int it, const uint8_t* cur, uint8_t* nxt2) __attribute__((always_inline)) {
     // Every wave waits for its own part of tile `it` (the gathers of tile
@@ -310,9 +362,14 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_bf16_kernel(MlaParams p) {
     else
       __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
     barrier_no_fence();
-    if (it + 2 < ntiles) mla_issue(nxt2, scratch_blk, kv, sel_l, it + 2, lane, wave_u);
+    if (it + 2 < ntiles) mla_issue(nxt2, scratch_blk, kv, rows, lane, wave_u);
+    // unconditional (a clamped, harmless re-read at the end), so that the
+    // wait counts below need not merge two control paths
+    mla_rows(rows, sel_l, min(it + 3, ntiles - 1), lane, wave_u);
     f32x4 s[2];
+    __builtin_amdgcn_sched_barrier(0);
     mla_partial_logits(cur, qf, d, n16, g, s);
+    __builtin_amdgcn_sched_barrier(0);
     xpart[wave_u][lane][0] = s[0];
     xpart[wave_u][lane][1] = s[1];
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): partial logits written
@@ -328,6 +385,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_bf16_kernel(MlaParams p) {
     if (it + 2 >= ntiles) break;
     step(it + 2, tile2, tile1);
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // every gather has landed before the LDS is released
 
   float l_part = st.l_part;
   l_part += __shfl_xor(l_part, 16);

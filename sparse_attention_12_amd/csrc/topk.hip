@@ -293,11 +293,6 @@ struct SplitWs {
   int nchunk;
 };
 
-__global__ __launch_bounds__(256) void topk_zero_kernel(uint32_t* hist, int n) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n) hist[i] = 0;
-}
-
 __global__ __launch_bounds__(TK_THREADS) void topk_hist_kernel(BatchDev b, const float* __restrict__ scores,
                                                                int64_t ld, int k, SplitWs ws) {
   __shared__ uint32_t hist[TK_BINS1];
@@ -432,8 +427,15 @@ size_t topk_workspace_bytes(int nq, int max_len, int k) {
   return split_bytes(nq, max_len, nullptr, nullptr);
 }
 
+ZeroSpan topk_zero_span(void* wsp, int nq, int max_len) {
+  if (wsp == nullptr || nq <= 0 || max_len <= 0 || !use_split(nq, max_len)) return ZeroSpan{nullptr, 0, 0};
+  SplitWs ws;
+  split_bytes(nq, max_len, &ws, (char*)wsp);
+  return ZeroSpan{ws.hist, TK_BINS1, TK_BINS1};
+}
+
 hipError_t launch_topk(const BatchDev& b, const float* scores, int64_t ld, int k, int32_t* idx,
-                       int32_t* count, void* wsp, size_t ws_bytes, hipStream_t st) {
+                       int32_t* count, void* wsp, size_t ws_bytes, hipStream_t st, bool ws_zeroed) {
   if (b.nq == 0) return hipSuccess;
   if (!use_split(b.nq, b.max_len)) {
     hipLaunchKernelGGL(topk_row_kernel, dim3(b.nq), dim3(TK_THREADS), 0, st, b, scores, ld, k, idx, count);
@@ -441,8 +443,13 @@ hipError_t launch_topk(const BatchDev& b, const float* scores, int64_t ld, int k
   }
   SplitWs ws;
   if (wsp == nullptr || ws_bytes < split_bytes(b.nq, b.max_len, &ws, (char*)wsp)) return hipErrorInvalidValue;
-  const int nh = b.nq * TK_BINS1;
-  hipLaunchKernelGGL(topk_zero_kernel, dim3((nh + 255) / 256), dim3(256), 0, st, ws.hist, nh);
+  if (!ws_zeroed) {
+    ZeroSpans z;
+    z.s[0] = topk_zero_span(wsp, b.nq, b.max_len);
+    z.s[1] = ZeroSpan{nullptr, 0, 0};
+    hipError_t e = launch_zero(z, b.nq, st);
+    if (e != hipSuccess) return e;
+  }
   dim3 grid(ws.nchunk, b.nq);
   hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(TK_THREADS), 0, st, b, scores, ld, k, ws);
   hipLaunchKernelGGL(topk_gather_kernel, grid, dim3(TK_THREADS), 0, st, b, scores, ld, k, ws);

@@ -111,6 +111,10 @@ def test_mla_validation(lib):
 
     assert call(dt=2) == DTYPE
     assert call(odt=-1) == DTYPE
+    long_b = _batch()
+    long_b.max_len = 3728271   # rows past 2^32 bytes of a sequence are not addressable
+    assert lib.mla_sparse_attend(ctypes.byref(long_b), 1, A, A, A, 2048, 0.07, A, 0, None, A, 1 << 40,
+                                 None) == UNSUPPORTED
     assert call(k=0) == SHAPE
     assert call(k=4096) == UNSUPPORTED
     assert call(q=None) == NULL
