@@ -99,6 +99,38 @@ __device__ void find_bucket(const uint32_t* hist, int nbins, uint32_t need, Scan
   __syncthreads();
 }
 
+// Adds the top-12-bit digits of row[c0, c1) to an LDS histogram.  The
+// 16-byte aligned body is read as float4, four per thread in flight, so a
+// pass is bandwidth- rather than latency-bound; the unaligned head and tail
+// (at most three values each) are read one by one.
+__device__ void hist_range(const float* row, int c0, int c1, uint32_t* hist) {
+  const int tid = threadIdx.x;
+  const int mis = (int)(((uintptr_t)(row + c0) >> 2) & 3);
+  const int a0 = min(c1, c0 + ((4 - mis) & 3));
+  const int nv = (c1 - a0) >> 2;
+  const int t0 = a0 + 4 * nv;
+  if (tid < a0 - c0) atomicAdd(&hist[score_key(row[c0 + tid]) >> TK_SHIFT1], 1u);
+  if (tid < c1 - t0) atomicAdd(&hist[score_key(row[t0 + tid]) >> TK_SHIFT1], 1u);
+  const float4* v = (const float4*)(row + a0);
+  for (int i0 = 0; i0 < nv; i0 += 4 * TK_THREADS) {
+    float4 x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * TK_THREADS + tid;
+      if (i < nv) x[u] = v[i];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (i0 + u * TK_THREADS + tid < nv) {
+        atomicAdd(&hist[score_key(x[u].x) >> TK_SHIFT1], 1u);
+        atomicAdd(&hist[score_key(x[u].y) >> TK_SHIFT1], 1u);
+        atomicAdd(&hist[score_key(x[u].z) >> TK_SHIFT1], 1u);
+        atomicAdd(&hist[score_key(x[u].w) >> TK_SHIFT1], 1u);
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // finalize from an ordered candidate list held in LDS
 // ---------------------------------------------------------------------------
@@ -210,32 +242,53 @@ __device__ void select_row_streaming(const float* row, int n, int k, uint32_t d1
 
 // Ordered compaction of row[c0, c1): entries with top-12 key bits >= d1 go
 // to (dst_key, dst_pos) in position order.  Returns the count (all threads).
+// Thread t takes four consecutive values of each 4,096-value stretch; four
+// stretches are loaded before they are scanned, as float4 when row + c0 is
+// 16-byte aligned.
 __device__ uint32_t compact_chunk(const float* row, int c0, int c1, uint32_t d1, uint32_t* dst_key,
                                   int32_t* dst_pos, uint32_t cap, ScanShared& ss) {
   const int tid = threadIdx.x;
+  const bool vec = (((uintptr_t)(row + c0)) & 15) == 0;
+  constexpr int STRETCH = 4 * TK_THREADS;
   uint32_t base = 0;
-  for (int t0 = c0; t0 < c1; t0 += 4 * TK_THREADS) {
-    uint32_t u[4];
-    uint32_t f = 0;
+  for (int t0 = c0; t0 < c1; t0 += 4 * STRETCH) {
+    uint32_t u[4][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int s = t0 + tid * 4 + i;
-      u[i] = s < c1 ? score_key(row[s]) : 0u;
-      if (s < c1 && (u[i] >> TK_SHIFT1) >= d1) f |= 1u << i;
-    }
-    uint32_t p = block_exclusive_scan(__builtin_popcount(f), ss.wsum, &ss.total);
+    for (int it = 0; it < 4; ++it) {
+      const int s0 = t0 + it * STRETCH + tid * 4;
+      if (vec && s0 + 3 < c1) {
+        const float4 x = *(const float4*)(row + s0);
+        u[it][0] = score_key(x.x);
+        u[it][1] = score_key(x.y);
+        u[it][2] = score_key(x.z);
+        u[it][3] = score_key(x.w);
+      } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (f & (1u << i)) {
-        const uint32_t slot = base + p++;
-        if (slot < cap) {
-          dst_key[slot] = u[i];
-          dst_pos[slot] = t0 + tid * 4 + i;
-        }
+        for (int j = 0; j < 4; ++j) u[it][j] = s0 + j < c1 ? score_key(row[s0 + j]) : 0u;
       }
     }
-    base += ss.total;
-    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int s0 = t0 + it * STRETCH + tid * 4;
+      if (t0 + it * STRETCH >= c1) break;  // uniform
+      uint32_t f = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (s0 + j < c1 && (u[it][j] >> TK_SHIFT1) >= d1) f |= 1u << j;
+      uint32_t p = block_exclusive_scan(__builtin_popcount(f), ss.wsum, &ss.total);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (f & (1u << j)) {
+          const uint32_t slot = base + p++;
+          if (slot < cap) {
+            dst_key[slot] = u[it][j];
+            dst_pos[slot] = s0 + j;
+          }
+        }
+      }
+      base += ss.total;
+      __syncthreads();
+    }
   }
   return base;
 }
@@ -265,7 +318,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_kernel(BatchDev b, const 
   const float* row = scores + (int64_t)q * ld;
   for (int i = tid; i < TK_BINS1; i += TK_THREADS) sm.hist1[i] = 0;
   __syncthreads();
-  for (int s = tid; s < n; s += TK_THREADS) atomicAdd(&sm.hist1[score_key(row[s]) >> TK_SHIFT1], 1u);
+  hist_range(row, 0, n, sm.hist1);
   __syncthreads();
   int d1;
   uint32_t above;
@@ -305,7 +358,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_hist_kernel(BatchDev b, const
   for (int i = tid; i < TK_BINS1; i += TK_THREADS) hist[i] = 0;
   __syncthreads();
   const float* row = scores + (int64_t)q * ld;
-  for (int s = c0 + tid; s < c1; s += TK_THREADS) atomicAdd(&hist[score_key(row[s]) >> TK_SHIFT1], 1u);
+  hist_range(row, c0, c1, hist);
   __syncthreads();
   uint32_t* gh = ws.hist + (int64_t)q * TK_BINS1;
   for (int i = tid; i < TK_BINS1; i += TK_THREADS)

@@ -153,6 +153,24 @@ def test_topk_many_rows(B):
         assert np.array_equal(idx[i], ref), f"row {i}: selection differs"
 
 
+@pytest.mark.parametrize("nrows", [5, 290])
+def test_topk_unaligned_rows(B, nrows):
+    """Row strides that are not a multiple of four floats: every row but the
+    first starts off a 16-byte boundary, so the vector passes take their
+    scalar head and tail paths (few rows: split path; many: one per row)."""
+    rng = np.random.default_rng(32 + nrows)
+    rows = []
+    for i in range(nrows):
+        n = int(rng.integers(2049, 40001)) if i % 3 else int(rng.integers(1, 5000))
+        rows.append(rng.integers(0, 60, n).astype(np.float32) if i % 2 else rng.standard_normal(n).astype(np.float32))
+    L = max(len(r) for r in rows)
+    idx, cnt = _topk_gpu(B, rows, 2048, ld=L + 3)
+    for i, r in enumerate(rows):
+        ref, m = oracle.topk(r.astype(np.float64), 2048)
+        assert cnt[i] == m, f"row {i}"
+        assert np.array_equal(idx[i], ref), f"row {i}: selection differs"
+
+
 def test_topk_on_indexer_scores(B):
     w = wl.make_decode([2048, 2049, 5000, 33000], "bf16", 1, seed=24)
     t = w.to_torch(DEV)
