@@ -49,19 +49,19 @@ struct KeyTile {
   u32x4 v[8];  // [key block kb][contraction step s] at v[kb*4 + s]
 };
 
-__global__ __launch_bounds__(IDX_DEC_THREADS) void idx_decode_bf16(
-    BatchDev b, const uint16_t* __restrict__ qI, const float* __restrict__ w,
-    const uint16_t* __restrict__ kI, float* __restrict__ scores, int64_t ld, int chunk, ZeroSpans z) {
-  const int q = blockIdx.y;
-  if (blockIdx.x == 0) zero_query_spans(z, q, threadIdx.x, IDX_DEC_THREADS);
-  const QueryRange r = query_range(b, q);
-  const int base = blockIdx.x * chunk;
-  if (base >= r.n) return;
-  const int end = min(base + chunk, r.n);
+// Scores of query q's keys [base, end): the four waves of the workgroup
+// take interleaved 32-key steps, each wave keeping four steps of loads in
+// flight.  Waves are independent (no LDS, no barriers).
+__device__ __forceinline__ void idx_decode_range(const BatchDev& b, const uint16_t* __restrict__ qI,
+                                                 const float* __restrict__ w, const uint16_t* __restrict__ kI,
+                                                 float* __restrict__ scores, int64_t ld, int q, int64_t row0,
+                                                 int base, int end) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int c16 = lane & 15;  // A row (head within block) / B column (key within block)
   const int g = lane >> 4;    // which 8 of each 32 contraction slots
+  int k0 = base + wave * IDX_DEC_STEP;
+  if (k0 >= end) return;
 
   // A operand: head hb*16 + c16, contraction slots s*32 + 8g + [0,8).
   bf16x8 a[2][4];
@@ -78,22 +78,22 @@ __global__ __launch_bounds__(IDX_DEC_THREADS) void idx_decode_bf16(
 #pragma unroll
     for (int i = 0; i < 4; ++i) wr[hb][i] = w[(int64_t)q * HI + hb * 16 + 4 * g + i];
 
-  const uint16_t* kb = kI + r.row0 * DI + g * 8;
+  const uint16_t* kb = kI + row0 * DI + g * 8;
   float* out = scores + (int64_t)q * ld;
   const int last = end - 1;
   constexpr int WSTEP = IDX_DEC_WAVES * IDX_DEC_STEP;
 
-  // Keys past the chunk end re-read the chunk's last row (a cache hit), so
-  // every load is unconditional and three stages stay in flight.
-  auto load = [&](KeyTile& kt, int k0) {
+  // Keys past the range end re-read its last row (a cache hit), so every
+  // load is unconditional and four stages stay in flight.
+  auto load = [&](KeyTile& kt, int k) {
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
-      const uint16_t* p = kb + (int64_t)min(k0 + kb2 * 16 + c16, last) * DI;
+      const uint16_t* p = kb + (int64_t)min(k + kb2 * 16 + c16, last) * DI;
 #pragma unroll
       for (int st = 0; st < 4; ++st) kt.v[kb2 * 4 + st] = load16_nt(p + st * 32);
     }
   };
-  auto score = [&](const KeyTile& kt, int k0) {
+  auto score = [&](const KeyTile& kt, int k) {
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
       f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
@@ -111,27 +111,106 @@ __global__ __launch_bounds__(IDX_DEC_THREADS) void idx_decode_bf16(
       }
       part += __shfl_xor(part, 16);
       part += __shfl_xor(part, 32);
-      const int key = k0 + kb2 * 16 + c16;
+      const int key = k + kb2 * 16 + c16;
       if (g == 0 && key < end) out[key] = part;
     }
   };
 
-  int k0 = base + wave * IDX_DEC_STEP;
-  if (k0 >= end) return;
-  KeyTile t0, t1, t2;
+  KeyTile t0, t1, t2, t3;
   load(t0, k0);
   load(t1, k0 + WSTEP);
+  load(t2, k0 + 2 * WSTEP);
   while (true) {
-    load(t2, k0 + 2 * WSTEP);
+    load(t3, k0 + 3 * WSTEP);
     score(t0, k0);
     if (k0 + WSTEP >= end) break;
-    load(t0, k0 + 3 * WSTEP);
+    load(t0, k0 + 4 * WSTEP);
     score(t1, k0 + WSTEP);
     if (k0 + 2 * WSTEP >= end) break;
-    load(t1, k0 + 4 * WSTEP);
+    load(t1, k0 + 5 * WSTEP);
     score(t2, k0 + 2 * WSTEP);
-    k0 += 3 * WSTEP;
+    if (k0 + 3 * WSTEP >= end) break;
+    load(t2, k0 + 6 * WSTEP);
+    score(t3, k0 + 3 * WSTEP);
+    k0 += 4 * WSTEP;
     if (k0 >= end) break;
+  }
+}
+
+// Grid (chunks, queries): workgroup (c, q) scores keys [c*chunk, (c+1)*chunk)
+// of query q.  Used for batches of many queries.
+__global__ __launch_bounds__(IDX_DEC_THREADS) void idx_decode_bf16(
+    BatchDev b, const uint16_t* __restrict__ qI, const float* __restrict__ w,
+    const uint16_t* __restrict__ kI, float* __restrict__ scores, int64_t ld, int chunk, ZeroSpans z) {
+  const int q = blockIdx.y;
+  if (blockIdx.x == 0) zero_query_spans(z, q, threadIdx.x, IDX_DEC_THREADS);
+  const QueryRange r = query_range(b, q);
+  const int base = blockIdx.x * chunk;
+  if (base >= r.n) return;
+  idx_decode_range(b, qI, w, kI, scores, ld, q, r.row0, base, min(base + chunk, r.n));
+}
+
+// Balanced decode: the batch's keys, laid end to end in query order, are
+// cut into gridDim.x equal ranges, one per workgroup, so ragged lengths
+// cost no imbalance and every workgroup streams a long range.  Each
+// workgroup first forms the prefix sums of the candidate counts itself.
+constexpr int IDX_BAL_MAXQ = 1024;
+constexpr int IDX_BAL_GRID = 512;
+
+__global__ __launch_bounds__(IDX_DEC_THREADS) void idx_decode_bf16_bal(
+    BatchDev b, const uint16_t* __restrict__ qI, const float* __restrict__ w,
+    const uint16_t* __restrict__ kI, float* __restrict__ scores, int64_t ld, ZeroSpans z) {
+  __shared__ int64_t pre[IDX_BAL_MAXQ + 1];
+  __shared__ int64_t wtot[IDX_DEC_WAVES];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  for (int q = blockIdx.x; q < b.nq; q += gridDim.x) zero_query_spans(z, q, tid, IDX_DEC_THREADS);
+  // candidate counts -> exclusive prefix sums in pre[0..nq]
+  constexpr int PER = IDX_BAL_MAXQ / IDX_DEC_THREADS;
+  int64_t cnt[PER];
+  int64_t mine = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int q = tid * PER + i;
+    cnt[i] = q < b.nq ? (int64_t)query_range(b, q).n : 0;
+    mine += cnt[i];
+  }
+  int64_t x = mine;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wtot[wave] = x;
+  __syncthreads();
+  int64_t before = 0;
+  for (int v = 0; v < wave; ++v) before += wtot[v];
+  int64_t run = before + x - mine;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int q = tid * PER + i;
+    if (q <= b.nq) pre[q] = run;
+    run += cnt[i];
+  }
+  __syncthreads();
+  const int64_t T = pre[b.nq];
+  const int64_t lo = T * blockIdx.x / gridDim.x;
+  const int64_t hi = T * (blockIdx.x + 1) / gridDim.x;
+  if (lo >= hi) return;
+  // first query whose keys end after lo
+  int qa = 0, qb = b.nq - 1;
+  while (qa < qb) {
+    const int m = (qa + qb) >> 1;
+    if (pre[m + 1] > lo) qb = m;
+    else qa = m + 1;
+  }
+  for (int q = qa; q < b.nq && pre[q] < hi; ++q) {
+    const int64_t s0 = max(lo, pre[q]) - pre[q];
+    const int64_t s1 = min(hi, pre[q + 1]) - pre[q];
+    if (s0 >= s1) continue;
+    const int s = b.q_seq[q];
+    idx_decode_range(b, qI, w, kI, scores, ld, q, b.seq_row0[s], (int)s0, (int)s1);
   }
 }
 
@@ -299,6 +378,9 @@ hipError_t launch_index_score(const BatchDev& b, int dtype, const void* qI, cons
     dim3 grid((b.max_len + PF_KC - 1) / PF_KC, (b.nq + PF_QB - 1) / PF_QB);
     hipLaunchKernelGGL(idx_prefill_bf16, grid, dim3(PF_THREADS), 0, st, b, (const uint16_t*)qI, w,
                        (const uint16_t*)kI, scores, ld);
+  } else if (b.nq <= IDX_BAL_MAXQ) {
+    hipLaunchKernelGGL(idx_decode_bf16_bal, dim3(IDX_BAL_GRID), dim3(IDX_DEC_THREADS), 0, st, b,
+                       (const uint16_t*)qI, w, (const uint16_t*)kI, scores, ld, z);
   } else {
     const int chunk = decode_chunk(b.nq, b.max_len);
     dim3 grid((b.max_len + chunk - 1) / chunk, b.nq);

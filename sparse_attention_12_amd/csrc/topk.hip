@@ -242,53 +242,50 @@ __device__ void select_row_streaming(const float* row, int n, int k, uint32_t d1
 
 // Ordered compaction of row[c0, c1): entries with top-12 key bits >= d1 go
 // to (dst_key, dst_pos) in position order.  Returns the count (all threads).
-// Thread t takes four consecutive values of each 4,096-value stretch; four
-// stretches are loaded before they are scanned, as float4 when row + c0 is
-// 16-byte aligned.
+// Thread t takes the 16 consecutive values [16t, 16t + 16) of each
+// 16,384-value stretch (four float4 loads when row + c0 is 16-byte
+// aligned), so one block scan orders a whole stretch.
+constexpr int TK_RUN = 16;
+constexpr int TK_STRETCH = TK_RUN * TK_THREADS;
+
 __device__ uint32_t compact_chunk(const float* row, int c0, int c1, uint32_t d1, uint32_t* dst_key,
                                   int32_t* dst_pos, uint32_t cap, ScanShared& ss) {
   const int tid = threadIdx.x;
   const bool vec = (((uintptr_t)(row + c0)) & 15) == 0;
-  constexpr int STRETCH = 4 * TK_THREADS;
   uint32_t base = 0;
-  for (int t0 = c0; t0 < c1; t0 += 4 * STRETCH) {
-    uint32_t u[4][4];
+  for (int t0 = c0; t0 < c1; t0 += TK_STRETCH) {
+    const int s0 = t0 + tid * TK_RUN;
+    uint32_t u[TK_RUN];
+    if (vec && s0 + TK_RUN <= c1) {
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int s0 = t0 + it * STRETCH + tid * 4;
-      if (vec && s0 + 3 < c1) {
-        const float4 x = *(const float4*)(row + s0);
-        u[it][0] = score_key(x.x);
-        u[it][1] = score_key(x.y);
-        u[it][2] = score_key(x.z);
-        u[it][3] = score_key(x.w);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) u[it][j] = s0 + j < c1 ? score_key(row[s0 + j]) : 0u;
+      for (int i = 0; i < TK_RUN / 4; ++i) {
+        const float4 x = *(const float4*)(row + s0 + 4 * i);
+        u[4 * i + 0] = score_key(x.x);
+        u[4 * i + 1] = score_key(x.y);
+        u[4 * i + 2] = score_key(x.z);
+        u[4 * i + 3] = score_key(x.w);
       }
+    } else {
+#pragma unroll
+      for (int j = 0; j < TK_RUN; ++j) u[j] = s0 + j < c1 ? score_key(row[s0 + j]) : 0u;
     }
+    uint32_t f = 0;
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int s0 = t0 + it * STRETCH + tid * 4;
-      if (t0 + it * STRETCH >= c1) break;  // uniform
-      uint32_t f = 0;
+    for (int j = 0; j < TK_RUN; ++j)
+      if (s0 + j < c1 && (u[j] >> TK_SHIFT1) >= d1) f |= 1u << j;
+    uint32_t p = block_exclusive_scan(__builtin_popcount(f), ss.wsum, &ss.total);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (s0 + j < c1 && (u[it][j] >> TK_SHIFT1) >= d1) f |= 1u << j;
-      uint32_t p = block_exclusive_scan(__builtin_popcount(f), ss.wsum, &ss.total);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (f & (1u << j)) {
-          const uint32_t slot = base + p++;
-          if (slot < cap) {
-            dst_key[slot] = u[it][j];
-            dst_pos[slot] = s0 + j;
-          }
+    for (int j = 0; j < TK_RUN; ++j) {
+      if (f & (1u << j)) {
+        const uint32_t slot = base + p++;
+        if (slot < cap) {
+          dst_key[slot] = u[j];
+          dst_pos[slot] = s0 + j;
         }
       }
-      base += ss.total;
-      __syncthreads();
     }
+    base += ss.total;
+    __syncthreads();
   }
   return base;
 }

@@ -67,6 +67,24 @@ def test_index_score_decode_exact(B, dtype):
         assert np.all(np.isnan(sc[qi, n:])), f"query {qi}: columns beyond the candidates were written"
 
 
+def test_index_score_decode_many_queries(B):
+    """Over 1,024 decode queries: the one-workgroup-per-chunk grid (smaller
+    batches cut the concatenated keys into equal ranges instead)."""
+    rng = np.random.default_rng(22)
+    lens = rng.integers(1, 1500, 1100).tolist()
+    w = wl.make_decode(lens, "bf16", 1, seed=22)
+    t = w.to_torch(DEV)
+    scores = torch.full((w.nq, w.max_len), float("nan"), device=DEV)
+    B.dsa_index_score(_batch(B, w, t), t["qI"], t["w"], t["kI"], scores)
+    torch.cuda.synchronize()
+    sc = scores.cpu().numpy()
+    for qi in (0, 1, 517, 1023, 1024, 1099):
+        n = lens[qi]
+        assert np.array_equal(sc[qi, :n].astype(np.float64), _oracle_scores(w, qi)), f"query {qi} (L={n})"
+    filled = ~np.isnan(sc)
+    assert np.array_equal(filled.sum(axis=1), np.array(lens)), "every candidate scored, nothing else written"
+
+
 @pytest.mark.parametrize("cache,first,nq", [(3000, 2900, 70), (5000, 10, 64), (9000, 8960, 40)])
 def test_index_score_prefill_exact(B, cache, first, nq):
     w = wl.make_prefill(cache, first, nq, "bf16", seed=22)
