@@ -36,25 +36,30 @@ constexpr int TK_LEVEL_BITS = 11;       // fallback levels over 64-bit keys
 // ---------------------------------------------------------------------------
 // block-wide helpers (1024 threads; every thread must call them)
 // ---------------------------------------------------------------------------
+// Inclusive prefix sum over the 64 lanes of a wave with data-parallel
+// primitives (DPP lane moves, no LDS round trips): shifts of 1, 2, 4 and 8
+// within each row of 16 lanes, then each row adds the total of the rows
+// before it (row broadcasts of lanes 15 and 31).  Lanes with no source lane
+// receive 0.
+__device__ inline uint32_t wave_inclusive_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1, 3
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2, 3
+  return x;
+}
+
 __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_inclusive_scan(v);
   if (lane == 63) wsum[wave] = x;
   __syncthreads();
   if (wave == 0) {
     const uint32_t s = lane < TK_WAVES ? wsum[lane] : 0u;
-    uint32_t t = s;
-#pragma unroll
-    for (int o = 1; o < TK_WAVES; o <<= 1) {
-      const uint32_t y = __shfl_up(t, o);
-      if (lane >= o) t += y;
-    }
+    const uint32_t t = wave_inclusive_scan(s);
     if (lane < TK_WAVES) wsum[lane] = t - s;
     if (lane == TK_WAVES - 1) *total = t;
   }
