@@ -509,21 +509,34 @@ __global__ __launch_bounds__(CMB_THREADS) void mla_combine(MlaParams p) {
   const int64_t stride = (int64_t)p.n_layers * p.b.nq * H;  // slots between splits
   const int64_t slot0 = (int64_t)layer * p.b.nq * H + qh;
   float mx = -INFINITY;
+#pragma unroll 4
   for (int i = 0; i < p.nsplit; ++i) mx = fmaxf(mx, p.part_ml[(slot0 + i * stride) * 2]);
   f32x4 acc[VS / 4];
 #pragma unroll
   for (int v = 0; v < VS / 4; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
   float den = 0.0f;
-  if (mx != -INFINITY) {
-    for (int i = 0; i < p.nsplit; ++i) {
-      const int64_t slot = slot0 + i * stride;
+  // four splits at a time, every load of a batch issued before any is used;
+  // an empty split (max -inf) weighs 0
+  constexpr int CB = 4;
+  for (int i0 = 0; i0 < p.nsplit; i0 += CB) {
+    float wgt[CB], sum[CB];
+    f32x4 val[CB][VS / 4];
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+      const bool ok = i0 + c < p.nsplit;
+      const int64_t slot = slot0 + (int64_t)(ok ? i0 + c : 0) * stride;
       const float mi = p.part_ml[slot * 2];
-      if (mi == -INFINITY) continue;
-      const float wgt = exp2f(mi - mx);
-      den += wgt * p.part_ml[slot * 2 + 1];
+      sum[c] = p.part_ml[slot * 2 + 1];
+      wgt[c] = (!ok || mi == -INFINITY) ? 0.0f : exp2f(mi - mx);
       const f32x4* pa = (const f32x4*)(p.part_acc + slot * DC) + part;
 #pragma unroll
-      for (int v = 0; v < VS / 4; ++v) acc[v] += wgt * pa[32 * v];
+      for (int v = 0; v < VS / 4; ++v) val[c][v] = pa[32 * v];
+    }
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+      den += wgt[c] * sum[c];
+#pragma unroll
+      for (int v = 0; v < VS / 4; ++v) acc[v] += wgt[c] * val[c][v];
     }
   }
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;
