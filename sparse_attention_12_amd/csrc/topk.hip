@@ -378,16 +378,48 @@ __global__ __launch_bounds__(TK_THREADS) void topk_gather_kernel(BatchDev b, con
   if (r.n <= k || c0 >= r.n) return;
   const int c1 = min(c0 + TK_CHUNK, r.n);
   const int tid = threadIdx.x;
+  // this thread's GR consecutive scores, read before the histogram so the
+  // two round trips overlap
+  constexpr int GR = TK_CHUNK / TK_THREADS;
+  static_assert(GR % 4 == 0, "whole float4 runs");
+  const float* row = scores + (int64_t)q * ld;
+  const int s0 = c0 + tid * GR;
+  uint32_t u[GR];
+  if ((((uintptr_t)(row + s0)) & 15) == 0 && s0 + GR <= c1) {
+#pragma unroll
+    for (int i = 0; i < GR / 4; ++i) {
+      const float4 x = *(const float4*)(row + s0 + 4 * i);
+      u[4 * i + 0] = score_key(x.x);
+      u[4 * i + 1] = score_key(x.y);
+      u[4 * i + 2] = score_key(x.z);
+      u[4 * i + 3] = score_key(x.w);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < GR; ++j) u[j] = s0 + j < c1 ? score_key(row[s0 + j]) : 0u;
+  }
   const uint32_t* gh = ws.hist + (int64_t)q * TK_BINS1;
   for (int i = tid; i < TK_BINS1; i += TK_THREADS) hist[i] = gh[i];
   __syncthreads();
   int d1;
   uint32_t above;
   find_bucket(hist, TK_BINS1, (uint32_t)k, ss, &d1, &above);
+  // ordered compaction of the chunk: one block scan
+  uint32_t f = 0;
+#pragma unroll
+  for (int j = 0; j < GR; ++j)
+    if (s0 + j < c1 && (u[j] >> TK_SHIFT1) >= (uint32_t)d1) f |= 1u << j;
+  uint32_t slot = block_exclusive_scan(__builtin_popcount(f), ss.wsum, &ss.total);
   const int64_t lbase = ((int64_t)q * ws.nchunk + c) * TK_CHUNK;
-  const uint32_t got = compact_chunk(scores + (int64_t)q * ld, c0, c1, (uint32_t)d1, ws.lkey + lbase,
-                                     ws.lpos + lbase, TK_CHUNK, ss);
-  if (tid == 0) ws.cnt[(int64_t)q * ws.nchunk + c] = got;
+#pragma unroll
+  for (int j = 0; j < GR; ++j) {
+    if (f & (1u << j)) {
+      ws.lkey[lbase + slot] = u[j];
+      ws.lpos[lbase + slot] = s0 + j;
+      ++slot;
+    }
+  }
+  if (tid == 0) ws.cnt[(int64_t)q * ws.nchunk + c] = ss.total;
 }
 
 struct FinalShared {
@@ -410,7 +442,10 @@ __global__ __launch_bounds__(TK_THREADS) void topk_final_kernel(BatchDev b, cons
     if (tid == 0 && count) count[q] = n;
     return;
   }
+  // the histogram and the per-chunk list lengths are read together
   const uint32_t* gh = ws.hist + (int64_t)q * TK_BINS1;
+  const int nch = (n + TK_CHUNK - 1) / TK_CHUNK;
+  const uint32_t mine = tid < nch ? ws.cnt[(int64_t)q * ws.nchunk + tid] : 0u;
   for (int i = tid; i < TK_BINS1; i += TK_THREADS) sm.hist1[i] = gh[i];
   __syncthreads();
   int d1;
@@ -418,25 +453,37 @@ __global__ __launch_bounds__(TK_THREADS) void topk_final_kernel(BatchDev b, cons
   find_bucket(sm.hist1, TK_BINS1, (uint32_t)k, sm.list.ss, &d1, &above);
   const uint32_t need = (uint32_t)k - above;
   const uint32_t total = above + sm.hist1[d1];
-  const int nch = (n + TK_CHUNK - 1) / TK_CHUNK;
   if (total <= (uint32_t)TK_FCAP) {
     // concatenate the per-chunk lists in chunk (= position) order: offsets
-    // by a block scan, then every entry copied in one parallel pass
-    const uint32_t mine = tid < nch ? ws.cnt[(int64_t)q * ws.nchunk + tid] : 0u;
+    // by a block scan, then every entry copied in one parallel pass with all
+    // of a thread's reads in flight together
     const uint32_t o = block_exclusive_scan(mine, sm.list.ss.wsum, &sm.list.ss.total);
     if (tid < nch) sm.off[tid] = o;
     __syncthreads();
     const int64_t lq = (int64_t)q * ws.nchunk * TK_CHUNK;
-    for (uint32_t e = tid; e < total; e += TK_THREADS) {
+    constexpr int PER = (TK_FCAP + TK_THREADS - 1) / TK_THREADS;
+    uint32_t kv[PER];
+    int32_t pv[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const uint32_t e = tid + i * TK_THREADS;
       int lo = 0, hi = nch - 1;  // last chunk whose offset is <= e
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (sm.off[mid] <= e) lo = mid;
         else hi = mid - 1;
       }
-      const int64_t src = lq + (int64_t)lo * TK_CHUNK + (e - sm.off[lo]);
-      sm.list.ukey[e] = ws.lkey[src];
-      sm.list.pos[e] = ws.lpos[src];
+      const int64_t src = lq + (int64_t)lo * TK_CHUNK + (e < total ? e - sm.off[lo] : 0);
+      kv[i] = ws.lkey[src];
+      pv[i] = ws.lpos[src];
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const uint32_t e = tid + i * TK_THREADS;
+      if (e < total) {
+        sm.list.ukey[e] = kv[i];
+        sm.list.pos[e] = pv[i];
+      }
     }
     __syncthreads();
     finalize_list(sm.list, (int)total, (uint32_t)d1, need, out);
