@@ -154,7 +154,8 @@ def main():
         achieved = tr["indexer"]["bytes"] / (idx_ms / 1e3) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=None,
-                    kernel="idx_decode_bf16", per_launch=tr["indexer"]["bytes"], per_launch_unit="B")
+                    kernel="idx_decode_bf16_bal" if w.nq <= 1024 else "idx_decode_bf16",
+                    per_launch=tr["indexer"]["bytes"], per_launch_unit="B")
     else:
         achieved = tr["indexer"]["flop"] / (idx_ms / 1e3) / 1e12
         roof = dict(bound="alu", achieved=round(achieved, 3), peak=FP32_VALU_PEAK_TFLOPS, unit="TFLOP/s",
