@@ -57,6 +57,31 @@ __device__ inline QueryRange query_range(const BatchDev& b, int q) {
 
 __device__ inline float bf16_to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
 
+// Reductions over lanes l, l^16, l^32, l^48 (the four 16-lane rows of a
+// wave) with gfx950's row swaps (v_permlane16_swap / v_permlane32_swap):
+// pure VALU, no LDS round trip.  Each swap of x with itself leaves, in every
+// lane, the values of the two rows being paired, so the pair's max or sum
+// needs no lane select.
+__device__ inline float rows4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Sum over lanes l and l^32 (the two halves of a wave).
+__device__ inline float halves_sum(float x) {
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__device__ inline float rows4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Two floats -> packed bf16 pair (low half = a), rounded to nearest even by
 // the gfx950 conversion instruction (v_cvt_pk_bf16_f32).
 typedef __bf16 hw_bf16x2 __attribute__((ext_vector_type(2)));

@@ -109,8 +109,7 @@ __device__ __forceinline__ void idx_decode_range(const BatchDev& b, const uint16
         part = fmaf(wr[0][i], fmaxf(acc0[i], 0.0f), part);
         part = fmaf(wr[1][i], fmaxf(acc1[i], 0.0f), part);
       }
-      part += __shfl_xor(part, 16);
-      part += __shfl_xor(part, 32);
+      part = rows4_sum(part);
       const int key = k + kb2 * 16 + c16;
       if (g == 0 && key < end) out[key] = part;
     }
@@ -333,7 +332,7 @@ __global__ __launch_bounds__(PF_THREADS) void idx_prefill_bf16(
       float part = 0.0f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) part = fmaf(wq[8 * (i >> 2) + (i & 3)], fmaxf(acc[i], 0.0f), part);
-      part += __shfl_xor(part, 32);
+      part = halves_sum(part);
       const int key = k0 + col;
       if (half == 0 && key < nj[j])
         scores[(int64_t)(qg0 + wave * PF_QPW + j) * ld + key] = part;

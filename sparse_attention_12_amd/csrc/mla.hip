@@ -186,21 +186,21 @@ __device__ __forceinline__ void mla_partial_logits(const uint8_t* tile, const bf
 
 // Online softmax over the tile's logits and O^T += V_tile^T . P^T for this
 // wave's 256 latent columns.
-__device__ __forceinline__ void mla_softmax_pv(MlaTileState& st, const uint8_t* tile, const f32x4 (&s)[2], const int* sel_l,
-                                               int t0, int d, int n16, int g, float scale_log2) {
+// valid: bit j set when the tile's position j is a kept position.
+__device__ __forceinline__ void mla_softmax_pv(MlaTileState& st, const uint8_t* tile, const f32x4 (&s)[2], uint32_t valid,
+                                               int d, int n16, int g, float scale_log2) {
   float x[8];
   float tmax = -INFINITY;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bool ok = sel_l[t0 + 16 * mb + 4 * g + i] >= 0;
+      const bool ok = (valid >> (16 * mb + 4 * g + i)) & 1u;
       const float v = ok ? s[mb][i] * scale_log2 : -INFINITY;
       x[mb * 4 + i] = v;
       tmax = fmaxf(tmax, v);
     }
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  tmax = rows4_max(tmax);
   const bool resc = tmax > st.m_run + MLA_RESCALE_SLACK;
   if (__any(resc)) {
     const float alpha = resc ? __builtin_amdgcn_exp2f(st.m_run - tmax) : 1.0f;
@@ -366,6 +366,9 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_bf16_kernel(MlaParams p) {
     // unconditional (a clamped, harmless re-read at the end), so that the
     // wait counts below need not merge two control paths
     mla_rows(rows, sel_l, min(it + 3, ntiles - 1), lane, wave_u);
+    // validity of the tile's 32 positions, read now and folded into a mask
+    // after the logits (the read's latency hides behind them)
+    const int vpos = sel_l[it * MLA_TILE + (lane & 31)];
     f32x4 s[2];
     __builtin_amdgcn_sched_barrier(0);
     mla_partial_logits(cur, qf, d, n16, g, s);
@@ -376,7 +379,8 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_bf16_kernel(MlaParams p) {
     barrier_no_fence();
     s[0] += xpart[wave_u ^ 4][lane][0];
     s[1] += xpart[wave_u ^ 4][lane][1];
-    mla_softmax_pv(st, cur, s, sel_l, it * MLA_TILE, d, n16, g, p.scale_log2);
+    const uint32_t valid = (uint32_t)__ballot(vpos >= 0);
+    mla_softmax_pv(st, cur, s, valid, d, n16, g, p.scale_log2);
   };
   for (int it = 0; it < ntiles; it += 3) {
     step(it, tile0, tile2);
@@ -387,9 +391,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_bf16_kernel(MlaParams p) {
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // every gather has landed before the LDS is released
 
-  float l_part = st.l_part;
-  l_part += __shfl_xor(l_part, 16);
-  l_part += __shfl_xor(l_part, 32);
+  const float l_part = rows4_sum(st.l_part);
   const int64_t qh = (int64_t)q * H + head;
   const int col0 = d * (DC / 2);
   if (p.nsplit == 1) {
