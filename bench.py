@@ -6,6 +6,7 @@ the C ABI, with all inputs resident in HBM: the fused decode entry for decode
 batches, the three calls in turn for a prefill chunk.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 0..4] [--no-cpu]
+                  [--index-dtype fp8]
 
 The default workload is the decode batch of 64 sequences at 32,768 positions
 (bf16).  `roofline` describes the dominant kernel (the indexer): algorithmic
@@ -28,6 +29,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
+FP8_MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 matrix, published
 FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector, published
 
 
@@ -38,6 +40,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--index-dtype", choices=["bf16", "fp8"], default=None,
+                    help="store the indexer's query and keys in this type (default: the workload's)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the run, copy a device buffer of this size (for counter calibration)")
@@ -65,6 +69,18 @@ def measured_traffic(kernel: str, workload: str):
     return rec["bytes_per_launch"]
 
 
+def indexer_kernel(w) -> str:
+    """The indexer kernel the library launches for this batch (same rules as
+    its dispatch: prefill-shaped bf16 batches use the blocked matrix kernel,
+    up to 1,024 decode queries the balanced range kernel)."""
+    if w.index_dtype == "f32":
+        return "idx_decode_f32"
+    if w.index_dtype == "bf16" and w.nseq == 1 and w.nq >= 32:
+        return "idx_prefill_bf16"
+    t = "fp8" if w.index_dtype == "fp8" else "bf16"
+    return f"idx_decode_{t}_bal" if w.nq <= 1024 else f"idx_decode_{t}"
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -81,7 +97,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t_gen = time.time()
-    w = workloads.config(args.config)
+    w = workloads.config(args.config, args.index_dtype)
     print(f"[bench] workload {w.name}: nq={w.nq} layers={w.n_layers} max_len={w.max_len} "
           f"(generated in {time.time() - t_gen:.1f}s)", file=sys.stderr, flush=True)
     t = w.to_torch(dev)
@@ -143,19 +159,20 @@ def main():
           f"indexer {idx_ms:.4f} ms, top-k {tk_ms:.4f} ms, one-layer MLA {mla_ms:.4f} ms",
           file=sys.stderr, flush=True)
 
-    tr = costmodel.path_traffic(w.seq_len, w.q_seq, w.q_pos, w.dtype, L, k)
+    tr = costmodel.path_traffic(w.seq_len, w.q_seq, w.q_pos, w.dtype, L, k, index_dtype=w.index_dtype)
     value = w.nq / (ms_per_step / 1e3)
-    if w.kind == "prefill":
+    kname = indexer_kernel(w)
+    if w.kind == "prefill" and w.index_dtype != "f32":
+        peak = FP8_MFMA_PEAK_TFLOPS if w.index_dtype == "fp8" else BF16_MFMA_PEAK_TFLOPS
         achieved = tr["indexer"]["flop"] / (idx_ms / 1e3) / 1e12
-        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=BF16_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(achieved / BF16_MFMA_PEAK_TFLOPS, 4), traffic=None,
-                    kernel="idx_prefill_bf16", per_launch=tr["indexer"]["flop"], per_launch_unit="FLOP")
-    elif w.dtype == "bf16":
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
+                    frac=round(achieved / peak, 4), traffic=None,
+                    kernel=kname, per_launch=tr["indexer"]["flop"], per_launch_unit="FLOP")
+    elif w.index_dtype != "f32":
         achieved = tr["indexer"]["bytes"] / (idx_ms / 1e3) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=None,
-                    kernel="idx_decode_bf16_bal" if w.nq <= 1024 else "idx_decode_bf16",
-                    per_launch=tr["indexer"]["bytes"], per_launch_unit="B")
+                    kernel=kname, per_launch=tr["indexer"]["bytes"], per_launch_unit="B")
     else:
         achieved = tr["indexer"]["flop"] / (idx_ms / 1e3) / 1e12
         roof = dict(bound="alu", achieved=round(achieved, 3), peak=FP32_VALU_PEAK_TFLOPS, unit="TFLOP/s",
@@ -191,7 +208,8 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded; integer indexer inputs in [-3,3], weights in [1,4], N(0,1) queries and cache)",
         "config": {"workload": w.name, "queries": w.nq, "sequences": w.nseq, "max_context": w.max_len,
-                   "layers_sharing_selection": L, "topk": k, "kind": w.kind},
+                   "layers_sharing_selection": L, "topk": k, "kind": w.kind,
+                   "indexer_dtype": w.index_dtype},
         "roofline": roof,
         "cpu_baseline": cpu,
         "path": {"algorithmic_bytes": tr["path_bytes"], "algorithmic_flop": tr["path_flop"],

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 1
+#define DSA_ABI_VERSION 2
 
 #define DSA_INDEX_HEADS 32  /* indexer heads                          */
 #define DSA_INDEX_DIM 128   /* indexer head width                     */
@@ -75,7 +75,15 @@ typedef enum {
   DSA_ERR_HIP = -7          /* the HIP runtime reported an error                  */
 } dsa_status_t;
 
-typedef enum { DSA_F32 = 0, DSA_BF16 = 1 } dsa_dtype_t;
+/*
+ * Element types.  DSA_FP8_E4M3 is for the indexer's inputs only (q_idx and
+ * k_idx; w_idx stays float32): the concept page's 1M-token serving
+ * scenario keeps the indexer keys in FP8.  It is the OCP 8-bit E4M3 encoding (sign,
+ * 4 exponent bits with bias 7, 3 mantissa bits; 0x7F/0xFF are NaN, no
+ * infinities, largest finite 448) with no scale factor: the caller stores
+ * values already scaled.  Products are exact in float32 and summed in float32.
+ */
+typedef enum { DSA_F32 = 0, DSA_BF16 = 1, DSA_FP8_E4M3 = 2 } dsa_dtype_t;
 
 /*
  * A batch of queries over one or more sequences.
@@ -116,6 +124,7 @@ const char* dsa_last_error(void);
 
 /*
  * Indexer scores ("Where to look" / "Sparse attention"; formula above).
+ *   dtype  DSA_F32, DSA_BF16 or DSA_FP8_E4M3 (q_idx and k_idx)
  *   q_idx  [nq][32][128] dtype      w_idx [nq][32] float32
  *   k_idx  [rows][128]   dtype      (row seq_row0[s] + p is position p)
  *   scores [nq][ld]      float32    column s < n_cand(q) receives I[q][s];
@@ -146,6 +155,7 @@ int32_t dsa_topk(const dsa_batch_t* batch, const float* scores, int64_t ld, int3
 
 /*
  * Sparse MLA read of one layer ("What to keep", "Sparse attention").
+ *   dtype, out_dtype  DSA_F32 or DSA_BF16
  *   q   [nq][64][576] dtype    absorbed query: 512 latent-space + 64 rotary
  *   kv  [rows][576]   dtype    cache rows (512 latent, 64 rotary key)
  *   idx [nq][k]       int32    selected positions; entries outside
@@ -168,8 +178,10 @@ int32_t mla_sparse_attend(const dsa_batch_t* batch, int32_t dtype, const void* q
  * page: 28 layers reuse the selection of the most recent layer that ran its
  * indexer).  Runs the indexer and the top-k once, then the sparse MLA read
  * of n_layers layers, each with its own query and cache, over that one
- * selection.  Arguments as in the three calls above; per-layer arrays come
- * as HOST tables of n_layers device pointers:
+ * selection.  Arguments as in the three calls above; index_dtype is the
+ * indexer's dtype (q_idx, k_idx) and dtype that of every layer's query and
+ * cache rows.  Per-layer arrays come as HOST tables of n_layers device
+ * pointers:
  *   q_l[l]   [nq][64][576] dtype    kv_l[l] [rows][576] dtype
  *   out_l[l] [nq][64][512] out_dtype  lse_l[l] [nq][64] float32 (lse_l or
  *   any entry may be NULL)
@@ -178,9 +190,9 @@ int32_t mla_sparse_attend(const dsa_batch_t* batch, int32_t dtype, const void* q
  */
 size_t dsa_mla_decode_fused_workspace_size(int32_t nq, int32_t max_len, int32_t k,
                                            int32_t n_layers);
-int32_t dsa_mla_decode_fused(const dsa_batch_t* batch, int32_t dtype, const void* q_idx,
+int32_t dsa_mla_decode_fused(const dsa_batch_t* batch, int32_t index_dtype, const void* q_idx,
                              const float* w_idx, const void* k_idx, int32_t k, int32_t n_layers,
-                             const void* const* q_l, const void* const* kv_l,
+                             int32_t dtype, const void* const* q_l, const void* const* kv_l,
                              void* const* out_l, float* const* lse_l, int32_t out_dtype,
                              float scale, int32_t* idx_out, void* ws, size_t ws_bytes,
                              void* stream);

@@ -16,7 +16,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdsa_mla.so")
 
-DSA_F32, DSA_BF16 = 0, 1
+DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
 INDEX_HEADS, INDEX_DIM, HEADS, LATENT, ROPE, ROW, TOPK_MAX = 32, 128, 64, 512, 64, 576, 2048
 
 EXPORTS = [
@@ -57,7 +57,7 @@ def _load() -> ctypes.CDLL:
     lib.mla_sparse_attend.restype = i32
     lib.dsa_mla_decode_fused_workspace_size.argtypes = [i32, i32, i32, i32]
     lib.dsa_mla_decode_fused_workspace_size.restype = sz
-    lib.dsa_mla_decode_fused.argtypes = [bp, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, i32,
+    lib.dsa_mla_decode_fused.argtypes = [bp, i32, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, i32,
                                          ctypes.c_float, vp, vp, sz, vp]
     lib.dsa_mla_decode_fused.restype = i32
     return lib
@@ -82,11 +82,18 @@ def _p(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+_FP8_TYPES = tuple(getattr(torch, n) for n in ("float8_e4m3fn",) if hasattr(torch, n))
+
+
 def _dt(t: torch.Tensor) -> int:
+    """Library dtype code of a tensor.  FP8 E4M3 (OCP) inputs of the indexer
+    may come as torch.float8_e4m3fn or as their uint8 bit patterns."""
     if t.dtype == torch.bfloat16:
         return DSA_BF16
     if t.dtype == torch.float32:
         return DSA_F32
+    if t.dtype == torch.uint8 or t.dtype in _FP8_TYPES:
+        return DSA_FP8_E4M3
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
@@ -178,6 +185,7 @@ def dsa_mla_decode_fused(batch: Batch, q_idx, w_idx, k_idx, k: int, q_l: Sequenc
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     cv = lambda a: None if a is None else ctypes.cast(a, ctypes.c_void_p)
     _check(lib.dsa_mla_decode_fused(batch.ref, _dt(q_idx), _p(q_idx), _p(w_idx), _p(k_idx), k, n,
-                                    cv(qa), cv(kva), cv(oa), cv(la), _dt(out_l[0]), scale, _p(idx_out),
+                                    _dt(q_l[0]), cv(qa), cv(kva), cv(oa), cv(la), _dt(out_l[0]), scale,
+                                    _p(idx_out),
                                     _p(ws), wsb, _stream(stream)), "dsa_mla_decode_fused")
     return out_l

@@ -139,12 +139,15 @@ ATTEND_MACS = HEADS * (LATENT + ROPE + LATENT)          # 69,632 per attended po
 
 
 def elem_bytes(dtype: str) -> int:
-    return {"f32": 4, "bf16": 2}[dtype]
+    return {"f32": 4, "bf16": 2, "fp8": 1}[dtype]
 
 
 def path_traffic(seq_len, q_seq, q_pos, dtype: str, n_layers: int = 1, k: int = TOPK,
-                 out_bytes: int = 4) -> dict:
+                 out_bytes: int = 4, index_dtype: str = "") -> dict:
     """Algorithmic bytes and FLOP of one pass of the read over a batch.
+
+    dtype is the storage of the attention query and cache rows; index_dtype
+    that of the indexer's query and keys ("" = dtype).
 
     Candidates of a query: its own position and every earlier one within the
     cache, n = min(q_pos + 1, seq_len).  Key rows and cache rows are counted
@@ -155,6 +158,7 @@ def path_traffic(seq_len, q_seq, q_pos, dtype: str, n_layers: int = 1, k: int = 
     q_seq = np.asarray(q_seq, np.int64)
     q_pos = np.asarray(q_pos, np.int64)
     es = elem_bytes(dtype)
+    ei = elem_bytes(index_dtype or dtype)
     nq = int(q_seq.shape[0])
     n_cand = np.maximum(0, np.minimum(q_pos + 1, seq_len[q_seq]))
     n_sel = np.minimum(n_cand, k)
@@ -162,9 +166,9 @@ def path_traffic(seq_len, q_seq, q_pos, dtype: str, n_layers: int = 1, k: int = 
     key_rows = np.zeros(seq_len.shape[0], np.int64)
     np.maximum.at(key_rows, q_seq, n_cand)
     row_d = LATENT + ROPE
-    idx_q_bytes = nq * (INDEXER_HEADS * INDEXER_DIM * es + INDEXER_HEADS * 4)
+    idx_q_bytes = nq * (INDEXER_HEADS * INDEXER_DIM * ei + INDEXER_HEADS * 4)
     indexer = dict(
-        key_bytes=int(key_rows.sum()) * INDEXER_DIM * es,
+        key_bytes=int(key_rows.sum()) * INDEXER_DIM * ei,
         q_bytes=idx_q_bytes,
         score_bytes=int(n_cand.sum()) * 4,
         flop=2 * SCORE_MACS * int(n_cand.sum()),

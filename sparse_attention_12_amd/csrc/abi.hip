@@ -60,6 +60,13 @@ int check_dtype(int32_t dt, const char* what) {
   return DSA_OK;
 }
 
+// The indexer also takes FP8 E4M3 inputs.
+int check_index_dtype(int32_t dt, const char* what) {
+  if (dt != DSA_F32 && dt != DSA_BF16 && dt != DSA_FP8_E4M3)
+    return fail(DSA_ERR_DTYPE, "%s = %d is not DSA_F32, DSA_BF16 or DSA_FP8_E4M3", what, dt);
+  return DSA_OK;
+}
+
 int check_k(int32_t k) {
   if (k < 1) return fail(DSA_ERR_SHAPE, "k = %d < 1", k);
   if (k > DSA_TOPK_MAX) return fail(DSA_ERR_UNSUPPORTED, "k = %d > %d", k, DSA_TOPK_MAX);
@@ -97,7 +104,7 @@ int32_t dsa_index_score(const dsa_batch_t* batch, int32_t dtype, const void* q_i
   dsa::BatchDev b;
   int st = check_batch(batch, &b);
   if (st) return st;
-  if ((st = check_dtype(dtype, "dtype"))) return st;
+  if ((st = check_index_dtype(dtype, "dtype"))) return st;
   if (b.nq == 0) return DSA_OK;
   REQUIRE_PTR(q_idx);
   REQUIRE_PTR(w_idx);
@@ -193,14 +200,15 @@ size_t dsa_mla_decode_fused_workspace_size(int32_t nq, int32_t max_len, int32_t 
   return fused_parts(nq, max_len, k, n_layers, &a, &c, &d);
 }
 
-int32_t dsa_mla_decode_fused(const dsa_batch_t* batch, int32_t dtype, const void* q_idx, const float* w_idx,
-                             const void* k_idx, int32_t k, int32_t n_layers, const void* const* q_l,
-                             const void* const* kv_l, void* const* out_l, float* const* lse_l,
-                             int32_t out_dtype, float scale, int32_t* idx_out, void* ws, size_t ws_bytes,
-                             void* stream) {
+int32_t dsa_mla_decode_fused(const dsa_batch_t* batch, int32_t index_dtype, const void* q_idx,
+                             const float* w_idx, const void* k_idx, int32_t k, int32_t n_layers,
+                             int32_t dtype, const void* const* q_l, const void* const* kv_l,
+                             void* const* out_l, float* const* lse_l, int32_t out_dtype, float scale,
+                             int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
   dsa::BatchDev b;
   int st = check_batch(batch, &b);
   if (st) return st;
+  if ((st = check_index_dtype(index_dtype, "index_dtype"))) return st;
   if ((st = check_dtype(dtype, "dtype"))) return st;
   if ((st = check_dtype(out_dtype, "out_dtype"))) return st;
   if ((st = check_k(k))) return st;
@@ -234,7 +242,7 @@ int32_t dsa_mla_decode_fused(const dsa_batch_t* batch, int32_t dtype, const void
   dsa::ZeroSpans z;
   z.s[0] = dsa::topk_zero_span(base + off_topk, b.nq, b.max_len);
   z.s[1] = dsa::ZeroSpan{nullptr, 0, 0};
-  if ((st = hip_status(dsa::launch_index_score(b, dtype, q_idx, w_idx, k_idx, scores, b.max_len, s, &z),
+  if ((st = hip_status(dsa::launch_index_score(b, index_dtype, q_idx, w_idx, k_idx, scores, b.max_len, s, &z),
                        "fused: index score launch")))
     return st;
   if ((st = hip_status(dsa::launch_topk(b, scores, b.max_len, k, idx, nullptr, base + off_topk,

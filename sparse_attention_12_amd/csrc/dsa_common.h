@@ -20,6 +20,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));  // 32 fp8 operand bytes
 
 // Device copy of the host batch descriptor (passed by value to kernels).
 struct BatchDev {

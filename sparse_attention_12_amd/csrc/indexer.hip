@@ -136,17 +136,121 @@ __device__ __forceinline__ void idx_decode_range(const BatchDev& b, const uint16
   }
 }
 
+// ---------------------------------------------------------------------------
+// decode, fp8 (OCP E4M3 queries and keys, the pages' indexer storage)
+// ---------------------------------------------------------------------------
+// v_mfma_f32_16x16x128_f8f6f4: 16 heads on M (two blocks for 32 heads), 16
+// keys on N, the whole 128-wide contraction in one product.  Lane (c, g)
+// holds 32 operand bytes; its contraction slots are taken as key bytes
+// [16g, 16g+16) and [64+16g, 64+16g+16) (the query uses the same slots), so
+// each load instruction reads 64 contiguous bytes of each of 16 keys.
+constexpr int IDX8_STEP = 64;  // keys per pipeline stage and wave (4 key blocks)
+
+struct KeyTile8 {
+  u32x4 v[8];  // [key block kb][half] at v[kb*2 + half]
+};
+
+__device__ __forceinline__ i32x8 cat32(u32x4 lo, u32x4 hi) {
+  return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__device__ __forceinline__ void idx_decode_range_f8(const BatchDev& b, const uint8_t* __restrict__ qI,
+                                                    const float* __restrict__ w, const uint8_t* __restrict__ kI,
+                                                    float* __restrict__ scores, int64_t ld, int q, int64_t row0,
+                                                    int base, int end) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int c16 = lane & 15;
+  const int g = lane >> 4;
+  int k0 = base + wave * IDX8_STEP;
+  if (k0 >= end) return;
+  i32x8 a[2];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    const uint8_t* qrow = qI + ((int64_t)q * HI + hb * 16 + c16) * DI;
+    a[hb] = cat32(load16(qrow + 16 * g), load16(qrow + 64 + 16 * g));
+  }
+  float wr[2][4];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wr[hb][i] = w[(int64_t)q * HI + hb * 16 + 4 * g + i];
+
+  const uint8_t* kb = kI + row0 * DI + 16 * g;
+  float* out = scores + (int64_t)q * ld;
+  const int last = end - 1;
+  constexpr int WSTEP = IDX_DEC_WAVES * IDX8_STEP;
+  auto load = [&](KeyTile8& kt, int k) {
+#pragma unroll
+    for (int kb4 = 0; kb4 < 4; ++kb4) {
+      const uint8_t* p = kb + (int64_t)min(k + kb4 * 16 + c16, last) * DI;
+      kt.v[kb4 * 2 + 0] = load16_nt(p);
+      kt.v[kb4 * 2 + 1] = load16_nt(p + 64);
+    }
+  };
+  auto score = [&](const KeyTile8& kt, int k) {
+#pragma unroll
+    for (int kb4 = 0; kb4 < 4; ++kb4) {
+      const i32x8 bk = cat32(kt.v[kb4 * 2], kt.v[kb4 * 2 + 1]);
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      // format 0 = FP8 E4M3 for both operands, no block scaling
+      const f32x4 acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[0], bk, zero, 0, 0, 0, 0, 0, 0);
+      const f32x4 acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[1], bk, zero, 0, 0, 0, 0, 0, 0);
+      float part = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        part = fmaf(wr[0][i], fmaxf(acc0[i], 0.0f), part);
+        part = fmaf(wr[1][i], fmaxf(acc1[i], 0.0f), part);
+      }
+      part = rows4_sum(part);
+      const int key = k + kb4 * 16 + c16;
+      if (g == 0 && key < end) out[key] = part;
+    }
+  };
+
+  KeyTile8 t0, t1, t2, t3;
+  load(t0, k0);
+  load(t1, k0 + WSTEP);
+  load(t2, k0 + 2 * WSTEP);
+  while (true) {
+    load(t3, k0 + 3 * WSTEP);
+    score(t0, k0);
+    if (k0 + WSTEP >= end) break;
+    load(t0, k0 + 4 * WSTEP);
+    score(t1, k0 + WSTEP);
+    if (k0 + 2 * WSTEP >= end) break;
+    load(t1, k0 + 5 * WSTEP);
+    score(t2, k0 + 2 * WSTEP);
+    if (k0 + 3 * WSTEP >= end) break;
+    load(t2, k0 + 6 * WSTEP);
+    score(t3, k0 + 3 * WSTEP);
+    k0 += 4 * WSTEP;
+    if (k0 >= end) break;
+  }
+}
+
+// Scores of keys [base, end) of query q in the given storage.
+template <bool FP8>
+__device__ __forceinline__ void idx_decode_any(const BatchDev& b, const void* qI, const float* w, const void* kI,
+                                               float* scores, int64_t ld, int q, int64_t row0, int base, int end) {
+  if (FP8)
+    idx_decode_range_f8(b, (const uint8_t*)qI, w, (const uint8_t*)kI, scores, ld, q, row0, base, end);
+  else
+    idx_decode_range(b, (const uint16_t*)qI, w, (const uint16_t*)kI, scores, ld, q, row0, base, end);
+}
+
 // Grid (chunks, queries): workgroup (c, q) scores keys [c*chunk, (c+1)*chunk)
 // of query q.  Used for batches of many queries.
-__global__ __launch_bounds__(IDX_DEC_THREADS) void idx_decode_bf16(
-    BatchDev b, const uint16_t* __restrict__ qI, const float* __restrict__ w,
-    const uint16_t* __restrict__ kI, float* __restrict__ scores, int64_t ld, int chunk, ZeroSpans z) {
+template <bool FP8>
+__device__ __forceinline__ void idx_decode_chunked(BatchDev b, const void* __restrict__ qI, const float* __restrict__ w,
+                                                   const void* __restrict__ kI, float* __restrict__ scores,
+                                                   int64_t ld, int chunk, ZeroSpans z) {
   const int q = blockIdx.y;
   if (blockIdx.x == 0) zero_query_spans(z, q, threadIdx.x, IDX_DEC_THREADS);
   const QueryRange r = query_range(b, q);
   const int base = blockIdx.x * chunk;
   if (base >= r.n) return;
-  idx_decode_range(b, qI, w, kI, scores, ld, q, r.row0, base, min(base + chunk, r.n));
+  idx_decode_any<FP8>(b, qI, w, kI, scores, ld, q, r.row0, base, min(base + chunk, r.n));
 }
 
 // Balanced decode: the batch's keys, laid end to end in query order, are
@@ -156,9 +260,10 @@ __global__ __launch_bounds__(IDX_DEC_THREADS) void idx_decode_bf16(
 constexpr int IDX_BAL_MAXQ = 1024;
 constexpr int IDX_BAL_GRID = 512;
 
-__global__ __launch_bounds__(IDX_DEC_THREADS) void idx_decode_bf16_bal(
-    BatchDev b, const uint16_t* __restrict__ qI, const float* __restrict__ w,
-    const uint16_t* __restrict__ kI, float* __restrict__ scores, int64_t ld, ZeroSpans z) {
+template <bool FP8>
+__device__ __forceinline__ void idx_decode_bal(BatchDev b, const void* __restrict__ qI, const float* __restrict__ w,
+                                               const void* __restrict__ kI, float* __restrict__ scores, int64_t ld,
+                                               ZeroSpans z) {
   __shared__ int64_t pre[IDX_BAL_MAXQ + 1];
   __shared__ int64_t wtot[IDX_DEC_WAVES];
   const int tid = threadIdx.x;
@@ -209,8 +314,30 @@ __global__ __launch_bounds__(IDX_DEC_THREADS) void idx_decode_bf16_bal(
     const int64_t s1 = min(hi, pre[q + 1]) - pre[q];
     if (s0 >= s1) continue;
     const int s = b.q_seq[q];
-    idx_decode_range(b, qI, w, kI, scores, ld, q, b.seq_row0[s], (int)s0, (int)s1);
+    idx_decode_any<FP8>(b, qI, w, kI, scores, ld, q, b.seq_row0[s], (int)s0, (int)s1);
   }
+}
+
+// One kernel per storage type, so profiles name what ran.
+__global__ __launch_bounds__(IDX_DEC_THREADS) void idx_decode_bf16_bal(BatchDev b, const void* qI, const float* w,
+                                                                       const void* kI, float* scores, int64_t ld,
+                                                                       ZeroSpans z) {
+  idx_decode_bal<false>(b, qI, w, kI, scores, ld, z);
+}
+__global__ __launch_bounds__(IDX_DEC_THREADS) void idx_decode_fp8_bal(BatchDev b, const void* qI, const float* w,
+                                                                      const void* kI, float* scores, int64_t ld,
+                                                                      ZeroSpans z) {
+  idx_decode_bal<true>(b, qI, w, kI, scores, ld, z);
+}
+__global__ __launch_bounds__(IDX_DEC_THREADS) void idx_decode_bf16(BatchDev b, const void* qI, const float* w,
+                                                                   const void* kI, float* scores, int64_t ld, int chunk,
+                                                                   ZeroSpans z) {
+  idx_decode_chunked<false>(b, qI, w, kI, scores, ld, chunk, z);
+}
+__global__ __launch_bounds__(IDX_DEC_THREADS) void idx_decode_fp8(BatchDev b, const void* qI, const float* w,
+                                                                  const void* kI, float* scores, int64_t ld, int chunk,
+                                                                  ZeroSpans z) {
+  idx_decode_chunked<true>(b, qI, w, kI, scores, ld, chunk, z);
 }
 
 // ---------------------------------------------------------------------------
@@ -371,20 +498,28 @@ hipError_t launch_index_score(const BatchDev& b, int dtype, const void* qI, cons
     dim3 grid((b.max_len + IDX_F32_THREADS - 1) / IDX_F32_THREADS, b.nq);
     hipLaunchKernelGGL(idx_decode_f32, grid, dim3(IDX_F32_THREADS), 0, st, b, (const float*)qI, w,
                        (const float*)kI, scores, ld, z);
-  } else if (b.nseq == 1 && b.nq >= PF_QB) {
+  } else if (dtype == 1 && b.nseq == 1 && b.nq >= PF_QB) {
     hipError_t e = launch_zero(z, b.nq, st);
     if (e != hipSuccess) return e;
     dim3 grid((b.max_len + PF_KC - 1) / PF_KC, (b.nq + PF_QB - 1) / PF_QB);
     hipLaunchKernelGGL(idx_prefill_bf16, grid, dim3(PF_THREADS), 0, st, b, (const uint16_t*)qI, w,
                        (const uint16_t*)kI, scores, ld);
   } else if (b.nq <= IDX_BAL_MAXQ) {
-    hipLaunchKernelGGL(idx_decode_bf16_bal, dim3(IDX_BAL_GRID), dim3(IDX_DEC_THREADS), 0, st, b,
-                       (const uint16_t*)qI, w, (const uint16_t*)kI, scores, ld, z);
+    if (dtype == 2)
+      hipLaunchKernelGGL(idx_decode_fp8_bal, dim3(IDX_BAL_GRID), dim3(IDX_DEC_THREADS), 0, st, b, qI, w, kI,
+                         scores, ld, z);
+    else
+      hipLaunchKernelGGL(idx_decode_bf16_bal, dim3(IDX_BAL_GRID), dim3(IDX_DEC_THREADS), 0, st, b, qI, w, kI,
+                         scores, ld, z);
   } else {
     const int chunk = decode_chunk(b.nq, b.max_len);
     dim3 grid((b.max_len + chunk - 1) / chunk, b.nq);
-    hipLaunchKernelGGL(idx_decode_bf16, grid, dim3(IDX_DEC_THREADS), 0, st, b,
-                       (const uint16_t*)qI, w, (const uint16_t*)kI, scores, ld, chunk, z);
+    if (dtype == 2)
+      hipLaunchKernelGGL(idx_decode_fp8, grid, dim3(IDX_DEC_THREADS), 0, st, b, qI, w, kI, scores, ld,
+                         chunk, z);
+    else
+      hipLaunchKernelGGL(idx_decode_bf16, grid, dim3(IDX_DEC_THREADS), 0, st, b, qI, w, kI, scores, ld,
+                         chunk, z);
   }
   return hipGetLastError();
 }

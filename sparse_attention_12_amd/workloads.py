@@ -15,8 +15,10 @@ Recipe (one ``numpy.random.default_rng(seed)`` stream, drawn in this order):
      with ``split_kv`` the latent block [rows,512] is drawn before the rotary
      block [rows,64] and the two are concatenated).
 Normal draws are float32 and are rounded once to bf16 (round to nearest even)
-when the workload is bf16; integer draws are exact in either precision.
-Decode queries sit at the last position of their sequence.
+when the workload is bf16; integer draws are exact in either precision and
+also in FP8 E4M3, in which the indexer's qI and kI may be stored
+(``index_dtype="fp8"``, as uint8 bit patterns).  Decode queries sit at the
+last position of their sequence.
 """
 from __future__ import annotations
 
@@ -57,11 +59,64 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
+# --------------------------------------------------------------------------
+# FP8 E4M3 storage helpers (OCP 8-bit floating point, E4M3: exponent bias 7,
+# no infinities, S.1111.111 is NaN, largest finite 448; format conversion only)
+# --------------------------------------------------------------------------
+
+
+def _e4m3_table() -> np.ndarray:
+    b = np.arange(256, dtype=np.int64)
+    sign = np.where(b >> 7, -1.0, 1.0)
+    e = (b >> 3) & 15
+    m = (b & 7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    v = sign * mag
+    v[(b & 0x7F) == 0x7F] = np.nan
+    return v.astype(np.float32)
+
+
+E4M3_VALUES = _e4m3_table()
+
+
+def e4m3_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen E4M3 bit patterns (uint8) to float32 exactly."""
+    return E4M3_VALUES[np.ascontiguousarray(b, dtype=np.uint8)]
+
+
+def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to E4M3 (nearest, ties to even; magnitudes above 448
+    saturate to 448, NaN gives 0x7F); returns uint8 bit patterns."""
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    nan = np.isnan(x)
+    neg = np.signbit(x)
+    a = np.minimum(np.abs(np.where(nan, 0.0, x)), 448.0)
+    # quantum of the binade of a (subnormals share the quantum 2^-9)
+    _, ex = np.frexp(a)
+    e = np.maximum(ex - 1, -6)
+    q = np.exp2(e - 3.0)
+    r = np.round(a / q) * q                      # numpy rounds half to even
+    r = np.minimum(r, 448.0)
+    _, ex = np.frexp(r)
+    e = ex - 1
+    normal = r >= 2.0 ** -6
+    field_e = np.where(normal, e + 7, 0)
+    field_m = np.where(normal, r / np.exp2(np.where(normal, e, 0)) * 8.0 - 8.0, r * 512.0)
+    bits = (field_e.astype(np.int64) << 3) | np.rint(field_m).astype(np.int64)
+    bits = np.where(neg, bits | 0x80, bits)
+    bits = np.where(nan, 0x7F, bits)
+    return bits.astype(np.uint8)
+
+
 def _small_int_bits(values: np.ndarray, dtype: str) -> np.ndarray:
-    """Store small integers exactly as float32 or bf16 bits."""
+    """Store small integers exactly as float32, bf16 bits or E4M3 bits."""
     if dtype == "f32":
         return values.astype(np.float32)
-    lut = f32_to_bf16_bits(np.arange(-128, 128, dtype=np.float32))
+    if dtype == "fp8":
+        assert int(np.abs(values).max(initial=0)) <= 16, "integers above 16 are not exact in E4M3"
+        lut = f32_to_e4m3_bits(np.arange(-128, 128, dtype=np.float32))
+    else:
+        lut = f32_to_bf16_bits(np.arange(-128, 128, dtype=np.float32))
     return lut[values.astype(np.int16) + 128]
 
 
@@ -86,7 +141,8 @@ def _normal(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
 class Workload:
     name: str
     kind: str                 # "decode" or "prefill"
-    dtype: str                # "f32" or "bf16" (storage of qI, kI, q, kv)
+    dtype: str                # "f32" or "bf16" (storage of q, kv; and of qI, kI
+                              # unless index_dtype says otherwise)
     n_layers: int
     seq_len: np.ndarray       # int32 [nseq]
     seq_row0: np.ndarray      # int64 [nseq]  first cache row of each sequence
@@ -100,6 +156,11 @@ class Workload:
     k: int = TOPK
     tau: float = TAU
     seed: int = 0
+    index_dtype: str = ""     # storage of qI, kI: "f32", "bf16" or "fp8" ("" = dtype)
+
+    def __post_init__(self):
+        if not self.index_dtype:
+            self.index_dtype = self.dtype
 
     @property
     def nq(self) -> int:
@@ -118,15 +179,20 @@ class Workload:
         return int(self.kI.shape[0])
 
     def widen(self, a: np.ndarray) -> np.ndarray:
-        """float32 view of a stored array (exact for bf16)."""
-        return bf16_bits_to_f32(a) if self.dtype == "bf16" else np.ascontiguousarray(a, np.float32)
+        """float32 view of a stored array (exact for bf16 and E4M3 bits)."""
+        if a.dtype == np.uint16:
+            return bf16_bits_to_f32(a)
+        if a.dtype == np.uint8:
+            return e4m3_bits_to_f32(a)
+        return np.ascontiguousarray(a, np.float32)
 
     def seq_rows(self, a: np.ndarray, s: int) -> np.ndarray:
         r0 = int(self.seq_row0[s])
         return a[r0:r0 + int(self.seq_len[s])]
 
     def to_torch(self, device):
-        """Device tensors of every array (bf16 bits reinterpreted as torch.bfloat16)."""
+        """Device tensors of every array (bf16 bits reinterpreted as torch.bfloat16;
+        E4M3 bits stay torch.uint8, which the binding passes as FP8 E4M3)."""
         import torch
 
         def t(a):
@@ -151,15 +217,17 @@ def _layout(lens: np.ndarray):
 
 def make_decode(lens, dtype: str = "bf16", n_layers: int = 1, seed: int = 0,
                 name: Optional[str] = None, split_kv: bool = False,
-                rng: Optional[np.random.Generator] = None) -> Workload:
+                rng: Optional[np.random.Generator] = None,
+                index_dtype: Optional[str] = None) -> Workload:
     """Decode batch: one query per sequence, at its last position."""
     rng = rng if rng is not None else np.random.default_rng(seed)
+    idt = index_dtype or dtype
     lens = np.asarray(lens, np.int32)
     nq = len(lens)
     row0, rows = _layout(lens)
-    qI = _small_int_bits(rng.integers(-3, 4, size=(nq, HI, DI), dtype=np.int8), dtype)
+    qI = _small_int_bits(rng.integers(-3, 4, size=(nq, HI, DI), dtype=np.int8), idt)
     w = rng.integers(1, 5, size=(nq, HI), dtype=np.int8).astype(np.float32)
-    kI = _small_int_bits(rng.integers(-3, 4, size=(rows, DI), dtype=np.int8), dtype)
+    kI = _small_int_bits(rng.integers(-3, 4, size=(rows, DI), dtype=np.int8), idt)
     qs, kvs = [], []
     for _ in range(n_layers):
         qs.append(_normal(rng, (nq, H, D), dtype))
@@ -173,25 +241,28 @@ def make_decode(lens, dtype: str = "bf16", n_layers: int = 1, seed: int = 0,
     return Workload(
         name=name or f"decode_b{nq}_{dtype}", kind="decode", dtype=dtype, n_layers=n_layers,
         seq_len=lens, seq_row0=row0, q_seq=np.arange(nq, dtype=np.int32),
-        q_pos=(lens - 1).astype(np.int32), qI=qI, w=w, kI=kI, q=qs, kv=kvs, seed=seed)
+        q_pos=(lens - 1).astype(np.int32), qI=qI, w=w, kI=kI, q=qs, kv=kvs, seed=seed,
+        index_dtype=idt)
 
 
 def make_prefill(cache_len: int, first_pos: int, nq: int, dtype: str = "bf16",
-                 seed: int = 0, name: Optional[str] = None) -> Workload:
+                 seed: int = 0, name: Optional[str] = None,
+                 index_dtype: Optional[str] = None) -> Workload:
     """Causal prefill chunk: nq consecutive queries of one sequence."""
     rng = np.random.default_rng(seed)
+    idt = index_dtype or dtype
     lens = np.asarray([cache_len], np.int32)
     row0, rows = _layout(lens)
-    qI = _small_int_bits(rng.integers(-3, 4, size=(nq, HI, DI), dtype=np.int8), dtype)
+    qI = _small_int_bits(rng.integers(-3, 4, size=(nq, HI, DI), dtype=np.int8), idt)
     w = rng.integers(1, 5, size=(nq, HI), dtype=np.int8).astype(np.float32)
-    kI = _small_int_bits(rng.integers(-3, 4, size=(rows, DI), dtype=np.int8), dtype)
+    kI = _small_int_bits(rng.integers(-3, 4, size=(rows, DI), dtype=np.int8), idt)
     q = _normal(rng, (nq, H, D), dtype)
     kv = _normal(rng, (rows, D), dtype)
     return Workload(
         name=name or f"prefill_{nq}q_{dtype}", kind="prefill", dtype=dtype, n_layers=1,
         seq_len=lens, seq_row0=row0, q_seq=np.zeros(nq, np.int32),
         q_pos=(first_pos + np.arange(nq)).astype(np.int32), qI=qI, w=w, kI=kI,
-        q=[q], kv=[kv], seed=seed)
+        q=[q], kv=[kv], seed=seed, index_dtype=idt)
 
 
 def ragged_lengths(rng: np.random.Generator, b: int, lo: int, hi: int, forced=(1024, 2048, 2049)):
@@ -219,19 +290,23 @@ CONFIG_NAMES = {
 }
 
 
-def config(i: int) -> Workload:
+def config(i: int, index_dtype: Optional[str] = None) -> Workload:
+    """Workload i; index_dtype="fp8" stores its indexer inputs in E4M3 (the
+    same integer draws, so scores and selections are unchanged)."""
     seed = 1000 + i
     name = CONFIG_NAMES[i]
+    if index_dtype == "fp8":
+        name = name + "_fp8index"
     if i == 0:
-        return make_decode([4096], "f32", 1, seed, name, split_kv=True)
+        return make_decode([4096], "f32", 1, seed, name, split_kv=True, index_dtype=index_dtype)
     if i == 1:
-        return make_decode([32768] * 64, "bf16", 1, seed, name)
+        return make_decode([32768] * 64, "bf16", 1, seed, name, index_dtype=index_dtype)
     if i == 2:
         rng = np.random.default_rng(seed)
         lens = ragged_lengths(rng, 16, 1024, 131072)
-        return make_decode(lens, "bf16", 4, seed, name, rng=rng)
+        return make_decode(lens, "bf16", 4, seed, name, rng=rng, index_dtype=index_dtype)
     if i == 3:
-        return make_prefill(65536, 63488, 2048, "bf16", seed, name)
+        return make_prefill(65536, 63488, 2048, "bf16", seed, name, index_dtype=index_dtype)
     if i == 4:
-        return make_decode([1 << 20] * 4, "bf16", 1, seed, name)
+        return make_decode([1 << 20] * 4, "bf16", 1, seed, name, index_dtype=index_dtype)
     raise KeyError(i)

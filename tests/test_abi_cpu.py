@@ -33,7 +33,7 @@ def lib():
     l.mla_sparse_attend.argtypes = [vp, i32, vp, vp, vp, i32, ctypes.c_float, vp, i32, vp, vp, sz, vp]
     l.mla_sparse_attend_workspace_size.argtypes = [i32, i32, i32]
     l.mla_sparse_attend_workspace_size.restype = sz
-    l.dsa_mla_decode_fused.argtypes = [vp, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, i32,
+    l.dsa_mla_decode_fused.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, i32,
                                        ctypes.c_float, vp, vp, sz, vp]
     l.dsa_mla_decode_fused_workspace_size.argtypes = [i32, i32, i32, i32]
     l.dsa_mla_decode_fused_workspace_size.restype = sz
@@ -65,7 +65,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.dsa_abi_version() == 1
+    assert lib.dsa_abi_version() == 2
     for st in (OK, NULL, SHAPE, DTYPE, ALIGN, WORKSPACE, UNSUPPORTED, -7):
         assert lib.dsa_status_string(st)
     assert b"unknown" in lib.dsa_status_string(42)
@@ -78,6 +78,10 @@ def test_index_score_validation(lib):
     assert lib.dsa_index_score(ctypes.byref(_batch(max_len=0)), 1, A, A, A, A, 100, None) == SHAPE
     assert lib.dsa_index_score(ctypes.byref(_batch(nq=-1)), 1, A, A, A, A, 100, None) == SHAPE
     assert lib.dsa_index_score(ctypes.byref(b), 7, A, A, A, A, 100, None) == DTYPE
+    assert lib.dsa_index_score(ctypes.byref(b), 3, A, A, A, A, 100, None) == DTYPE
+    # FP8 E4M3 (2) is an indexer dtype: validation goes on to the pointers
+    assert lib.dsa_index_score(ctypes.byref(b), 2, None, A, A, A, 100, None) == NULL
+    assert lib.dsa_index_score(ctypes.byref(b), 2, A, A, A, A, 99, None) == SHAPE
     assert lib.dsa_index_score(ctypes.byref(b), 1, None, A, A, A, 100, None) == NULL
     assert lib.dsa_index_score(ctypes.byref(b), 1, MIS, A, A, A, 100, None) == ALIGN
     assert lib.dsa_index_score(ctypes.byref(b), 1, A, A, A, None, 100, None) == NULL
@@ -135,10 +139,15 @@ def test_fused_validation(lib):
     need = lib.dsa_mla_decode_fused_workspace_size(2, 100, 2048, 2)
     assert need >= 2 * 100 * 4 + 2 * 2048 * 4
 
-    def call(n_layers=2, q=tab, kv=tab, out=tab, k=2048, ws=A, wsb=need):
+    def call(n_layers=2, q=tab, kv=tab, out=tab, k=2048, ws=A, wsb=need, idt=1, dt=1, odt=0):
         c = lambda t: ctypes.cast(t, ctypes.c_void_p) if t is not None else None
-        return lib.dsa_mla_decode_fused(ctypes.byref(b), 1, A, A, A, k, n_layers, c(q), c(kv), c(out), None, 0,
-                                        0.07, None, ws, wsb, None)
+        return lib.dsa_mla_decode_fused(ctypes.byref(b), idt, A, A, A, k, n_layers, dt, c(q), c(kv), c(out),
+                                        None, odt, 0.07, None, ws, wsb, None)
+
+    assert call(idt=5) == DTYPE
+    assert call(dt=2) == DTYPE          # FP8 is for the indexer's inputs only
+    assert call(odt=2) == DTYPE
+    assert call(idt=2, ws=None) == WORKSPACE   # FP8 indexer accepted, fails later
 
     assert call(n_layers=0) == SHAPE
     assert call(n_layers=17) == UNSUPPORTED

@@ -85,3 +85,8 @@ def test_path_traffic_units():
     # short context: every position selected
     t = cm.path_traffic([1000], [0], [999], "f32")
     assert t["mla_layer"]["positions"] == 1000
+    # FP8 E4M3 indexer: one byte per key element; the cache rows stay bf16
+    t = cm.path_traffic([32768], [0], [32767], "bf16", index_dtype="fp8")
+    assert t["indexer"]["key_bytes"] == 32768 * 128
+    assert t["indexer"]["q_bytes"] == 32 * 128 + 32 * 4
+    assert t["mla_layer"]["row_bytes_unique"] == 2048 * 1152

@@ -52,9 +52,9 @@ def _oracle_scores(w, qi):
 DECODE_LENS = [1, 31, 32, 33, 100, 2047, 2048, 2049, 4097, 9000, 16385]
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_index_score_decode_exact(B, dtype):
-    w = wl.make_decode(DECODE_LENS, dtype, 1, seed=21)
+@pytest.mark.parametrize("dtype,idt", [("bf16", "bf16"), ("f32", "f32"), ("bf16", "fp8")])
+def test_index_score_decode_exact(B, dtype, idt):
+    w = wl.make_decode(DECODE_LENS, dtype, 1, seed=21, index_dtype=idt)
     t = w.to_torch(DEV)
     ld = w.max_len + 5
     scores = torch.full((w.nq, ld), float("nan"), device=DEV)
@@ -67,12 +67,13 @@ def test_index_score_decode_exact(B, dtype):
         assert np.all(np.isnan(sc[qi, n:])), f"query {qi}: columns beyond the candidates were written"
 
 
-def test_index_score_decode_many_queries(B):
+@pytest.mark.parametrize("idt", ["bf16", "fp8"])
+def test_index_score_decode_many_queries(B, idt):
     """Over 1,024 decode queries: the one-workgroup-per-chunk grid (smaller
     batches cut the concatenated keys into equal ranges instead)."""
     rng = np.random.default_rng(22)
     lens = rng.integers(1, 1500, 1100).tolist()
-    w = wl.make_decode(lens, "bf16", 1, seed=22)
+    w = wl.make_decode(lens, "bf16", 1, seed=22, index_dtype=idt)
     t = w.to_torch(DEV)
     scores = torch.full((w.nq, w.max_len), float("nan"), device=DEV)
     B.dsa_index_score(_batch(B, w, t), t["qI"], t["w"], t["kI"], scores)
@@ -85,9 +86,10 @@ def test_index_score_decode_many_queries(B):
     assert np.array_equal(filled.sum(axis=1), np.array(lens)), "every candidate scored, nothing else written"
 
 
+@pytest.mark.parametrize("idt", ["bf16", "fp8"])
 @pytest.mark.parametrize("cache,first,nq", [(3000, 2900, 70), (5000, 10, 64), (9000, 8960, 40)])
-def test_index_score_prefill_exact(B, cache, first, nq):
-    w = wl.make_prefill(cache, first, nq, "bf16", seed=22)
+def test_index_score_prefill_exact(B, cache, first, nq, idt):
+    w = wl.make_prefill(cache, first, nq, "bf16", seed=22, index_dtype=idt)
     t = w.to_torch(DEV)
     scores = torch.full((w.nq, cache), float("nan"), device=DEV)
     B.dsa_index_score(_batch(B, w, t), t["qI"], t["w"], t["kI"], scores)
@@ -99,6 +101,80 @@ def test_index_score_prefill_exact(B, cache, first, nq):
         assert ref.shape[0] == n
         assert np.array_equal(sc[qi, :n].astype(np.float64), ref), f"query {qi}"
         assert np.all(np.isnan(sc[qi, n:]))
+
+
+FINITE_E4M3 = np.array([b for b in range(256) if (b & 0x7F) != 0x7F], np.uint8)
+
+
+def _fp8_scores(B, lens, qI, kI, w_):
+    """Indexer scores of one decode query per sequence from raw E4M3 bytes."""
+    nq = len(lens)
+    row0 = np.concatenate([[0], np.cumsum(lens[:-1])]).astype(np.int64)
+    L = np.array(lens, np.int32)
+    batch = B.Batch(torch.arange(nq, dtype=torch.int32, device=DEV), torch.from_numpy(L - 1).to(DEV),
+                    torch.from_numpy(L).to(DEV), torch.from_numpy(row0).to(DEV), max(lens))
+    scores = torch.full((nq, max(lens)), float("nan"), device=DEV)
+    B.dsa_index_score(batch, torch.from_numpy(qI).to(DEV), torch.from_numpy(w_).to(DEV),
+                      torch.from_numpy(kI).to(DEV), scores)
+    torch.cuda.synchronize()
+    return scores.cpu().numpy().astype(np.float64), row0
+
+
+def test_index_score_fp8_every_code_exact(B):
+    """Every finite E4M3 code (subnormals, +-448, signed zeros) is read as the
+    OCP encoding, bit-exact.  Query 0 has one-hot heads (+-1 at one element
+    each) over keys drawn from all codes; query 1 has one-hot keys (+-1) under
+    heads drawn from all codes.  With unit weights each score is a sum of 32
+    E4M3 values, all multiples of 2^-9 below 32 x 448 < 2^14, so float32
+    holds every partial sum exactly and the result must equal the oracle."""
+    rng = np.random.default_rng(23)
+    lens = [700, 1500]
+    rows = sum(lens)
+    qI = np.zeros((2, 32, 128), np.uint8)
+    kI = rng.choice(FINITE_E4M3, size=(rows, 128))
+    pick = rng.integers(0, 128, 32)
+    qI[0, np.arange(32), pick] = rng.choice(np.array([0x38, 0xB8], np.uint8), 32)
+    qI[1] = rng.choice(FINITE_E4M3, size=(32, 128))
+    one = rng.integers(0, 128, lens[1])
+    kI[lens[0]:] = 0
+    kI[lens[0] + np.arange(lens[1]), one] = rng.choice(np.array([0x38, 0xB8], np.uint8), lens[1])
+    w_ = np.ones((2, 32), np.float32)
+    sc, row0 = _fp8_scores(B, lens, qI, kI, w_)
+    qf, kf = wl.e4m3_bits_to_f32(qI), wl.e4m3_bits_to_f32(kI)
+    # every code was exercised
+    assert len(np.unique(kI[:lens[0]][:, pick])) == len(FINITE_E4M3)
+    assert len(np.unique(qI[1])) == len(FINITE_E4M3)
+    for qi, n in enumerate(lens):
+        ref = oracle.index_score(qf[qi], w_[qi], kf[row0[qi]:row0[qi] + n])
+        assert np.array_equal(sc[qi, :n], ref), f"query {qi}"
+
+
+def test_index_score_fp8_full_range(B):
+    """Random codes over the whole E4M3 range in q and k and normal weights.
+    Products of two E4M3 values are exact, but the matrix core sums the 128
+    products of a head at an internal precision that AMD does not specify bit
+    by bit, so the bar is relative to the sum of absolute terms,
+    sum_h |w_h| sum_i |q_hi k_i|: 2^-14 of it (fp32 rounding alone gives
+    about 2^-17; a mis-read code or a dropped product is far larger).  The
+    last query and its keys use only subnormals and the two lowest binades,
+    where a flushed subnormal would exceed the bar."""
+    rng = np.random.default_rng(24)
+    lens = [3, 700, 2100, 500]
+    rows = sum(lens)
+    qI = rng.choice(FINITE_E4M3, size=(len(lens), 32, 128))
+    kI = rng.choice(FINITE_E4M3, size=(rows, 128))
+    tiny = FINITE_E4M3[(FINITE_E4M3 & 0x78) <= 0x10]
+    qI[-1] = rng.choice(tiny, size=(32, 128))
+    kI[rows - lens[-1]:] = rng.choice(tiny, size=(lens[-1], 128))
+    w_ = rng.standard_normal((len(lens), 32)).astype(np.float32)
+    sc, row0 = _fp8_scores(B, lens, qI, kI, w_)
+    qf, kf = wl.e4m3_bits_to_f32(qI), wl.e4m3_bits_to_f32(kI)
+    for qi, n in enumerate(lens):
+        k = kf[row0[qi]:row0[qi] + n].astype(np.float64)
+        ref = oracle.index_score(qf[qi], w_[qi], kf[row0[qi]:row0[qi] + n])
+        mag = np.abs(w_[qi]).astype(np.float64) @ (np.abs(qf[qi]).astype(np.float64) @ np.abs(k.T))
+        err = np.abs(sc[qi, :n] - ref)
+        assert np.all(err <= 2.0 ** -14 * mag), f"query {qi}: worst {np.max(err / mag):.3e}"
 
 
 # ----------------------------------------------------------------------------
@@ -292,12 +368,13 @@ def test_mla_bf16_output(B):
 # ----------------------------------------------------------------------------
 
 
-@pytest.mark.parametrize("dtype,lens,layers", [
-    ("bf16", [1024, 2048, 2049, 3333, 40000], 4),
-    ("f32", [700, 4096], 2),
+@pytest.mark.parametrize("dtype,idt,lens,layers", [
+    ("bf16", "bf16", [1024, 2048, 2049, 3333, 40000], 4),
+    ("f32", "f32", [700, 4096], 2),
+    ("bf16", "fp8", [1500, 2049, 9000], 2),
 ])
-def test_fused_decode(B, dtype, lens, layers):
-    w = wl.make_decode(lens, dtype, layers, seed=30)
+def test_fused_decode(B, dtype, idt, lens, layers):
+    w = wl.make_decode(lens, dtype, layers, seed=30, index_dtype=idt)
     t = w.to_torch(DEV)
     outs = [torch.empty((w.nq, 64, 512), device=DEV) for _ in range(layers)]
     lses = [torch.empty((w.nq, 64), device=DEV) for _ in range(layers)]
