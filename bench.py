@@ -71,13 +71,14 @@ def measured_traffic(kernel: str, workload: str):
 
 def indexer_kernel(w) -> str:
     """The indexer kernel the library launches for this batch (same rules as
-    its dispatch: prefill-shaped bf16 batches use the blocked matrix kernel,
-    up to 1,024 decode queries the balanced range kernel)."""
+    its dispatch: batches of one sequence with 32 or more queries use the
+    blocked matrix kernel, up to 1,024 decode queries the balanced range
+    kernel)."""
     if w.index_dtype == "f32":
         return "idx_decode_f32"
-    if w.index_dtype == "bf16" and w.nseq == 1 and w.nq >= 32:
-        return "idx_prefill_bf16"
     t = "fp8" if w.index_dtype == "fp8" else "bf16"
+    if w.nseq == 1 and w.nq >= 32:
+        return f"idx_prefill_{t}"
     return f"idx_decode_{t}_bal" if w.nq <= 1024 else f"idx_decode_{t}"
 
 

@@ -469,6 +469,100 @@ __global__ __launch_bounds__(PF_THREADS) void idx_prefill_bf16(
 }
 
 // ---------------------------------------------------------------------------
+// prefill, fp8: 32 queries of one sequence per workgroup
+// ---------------------------------------------------------------------------
+// v_mfma_f32_32x32x64_f8f6f4: 32 heads on M, 32 keys on N, two products for
+// the 128-wide contraction.  Lane (col, half) holds 32 operand bytes per
+// product; its contraction slots are taken as bytes [64*half, 64*half + 64)
+// of the row (first product the lower 32, second the upper 32), the same for
+// query and key, so each lane reads 64 contiguous bytes of one key.
+constexpr int PF8_TK = 64;  // keys per LDS tile (two 32-key products)
+
+__global__ __launch_bounds__(PF_THREADS) void idx_prefill_fp8(
+    BatchDev b, const uint8_t* __restrict__ qI, const float* __restrict__ w,
+    const uint8_t* __restrict__ kI, float* __restrict__ scores, int64_t ld) {
+  // Key tile: 64 keys x 8 chunks of 16 B; chunk c of key k sits at slot
+  // k*8 + (c ^ ((k >> 1) & 7)), so the 16 keys a quarter-wave reads fall on
+  // 16 distinct 16-byte bank groups.
+  __shared__ u32x4 ktile[2][PF8_TK * 8];
+  __shared__ float wl[PF_QB * HI];
+  __shared__ int ncand[PF_QB];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 31;
+  const int half = lane >> 5;
+  const int qg0 = blockIdx.y * PF_QB;
+  const int kbase = blockIdx.x * PF_KC;
+
+  if (tid < PF_QB) {
+    const int qi = qg0 + tid;
+    ncand[tid] = qi < b.nq ? query_range(b, qi).n : 0;
+  }
+  for (int i = tid; i < PF_QB * HI; i += PF_THREADS) {
+    const int qi = qg0 + i / HI;
+    wl[i] = qi < b.nq ? w[(int64_t)qg0 * HI + i] : 0.0f;
+  }
+  __syncthreads();
+  int nmax = 0;
+#pragma unroll
+  for (int j = 0; j < PF_QB; ++j) nmax = max(nmax, ncand[j]);
+  const int kend = min(kbase + PF_KC, nmax);
+  if (kbase >= kend) return;
+  const int64_t row0 = b.seq_row0[0];
+
+  i32x8 a[PF_QPW][2];
+  int nj[PF_QPW];
+#pragma unroll
+  for (int j = 0; j < PF_QPW; ++j) {
+    const int ql = wave * PF_QPW + j;
+    const int qc = min(qg0 + ql, b.nq - 1);
+    const uint8_t* qrow = qI + ((int64_t)qc * HI + col) * DI + half * 64;
+    a[j][0] = cat32(load16(qrow), load16(qrow + 16));
+    a[j][1] = cat32(load16(qrow + 32), load16(qrow + 48));
+    nj[j] = ncand[ql];
+  }
+
+  const int lk = tid >> 3;   // key of the tile this thread stages
+  const int lc = tid & 7;    // its 16-byte chunk
+  const int lslot = lk * 8 + (lc ^ ((lk >> 1) & 7));
+  const uint8_t* kb = kI + row0 * DI + lc * 16;
+  u32x4 pre = load16_nt(kb + (int64_t)min(kbase + lk, kend - 1) * DI);
+  int buf = 0;
+  for (int k0 = kbase; k0 < kend; k0 += PF8_TK) {
+    ktile[buf][lslot] = pre;
+    __syncthreads();
+    if (k0 + PF8_TK < kend) pre = load16_nt(kb + (int64_t)min(k0 + PF8_TK + lk, kend - 1) * DI);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int kk = sub * 32 + col;
+      const int sw = (kk >> 1) & 7;
+      const u32x4* krow = &ktile[buf][kk * 8];
+      const i32x8 b0 = cat32(krow[(4 * half + 0) ^ sw], krow[(4 * half + 1) ^ sw]);
+      const i32x8 b1 = cat32(krow[(4 * half + 2) ^ sw], krow[(4 * half + 3) ^ sw]);
+      const int kt0 = k0 + sub * 32;
+#pragma unroll
+      for (int j = 0; j < PF_QPW; ++j) {
+        if (kt0 >= nj[j]) continue;
+        f32x16 acc = {};
+        // format 0 = FP8 E4M3 for both operands, no block scaling
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[j][0], b0, acc, 0, 0, 0, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[j][1], b1, acc, 0, 0, 0, 0, 0, 0);
+        const float* wq = wl + (wave * PF_QPW + j) * HI + 4 * half;
+        float part = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) part = fmaf(wq[8 * (i >> 2) + (i & 3)], fmaxf(acc[i], 0.0f), part);
+        part = halves_sum(part);
+        const int key = kt0 + col;
+        if (half == 0 && key < nj[j])
+          scores[(int64_t)(qg0 + wave * PF_QPW + j) * ld + key] = part;
+      }
+    }
+    buf ^= 1;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
 // Keys per decode workgroup: the largest power of two in [512, 4096] that
@@ -498,12 +592,16 @@ hipError_t launch_index_score(const BatchDev& b, int dtype, const void* qI, cons
     dim3 grid((b.max_len + IDX_F32_THREADS - 1) / IDX_F32_THREADS, b.nq);
     hipLaunchKernelGGL(idx_decode_f32, grid, dim3(IDX_F32_THREADS), 0, st, b, (const float*)qI, w,
                        (const float*)kI, scores, ld, z);
-  } else if (dtype == 1 && b.nseq == 1 && b.nq >= PF_QB) {
+  } else if (b.nseq == 1 && b.nq >= PF_QB) {
     hipError_t e = launch_zero(z, b.nq, st);
     if (e != hipSuccess) return e;
     dim3 grid((b.max_len + PF_KC - 1) / PF_KC, (b.nq + PF_QB - 1) / PF_QB);
-    hipLaunchKernelGGL(idx_prefill_bf16, grid, dim3(PF_THREADS), 0, st, b, (const uint16_t*)qI, w,
-                       (const uint16_t*)kI, scores, ld);
+    if (dtype == 2)
+      hipLaunchKernelGGL(idx_prefill_fp8, grid, dim3(PF_THREADS), 0, st, b, (const uint8_t*)qI, w,
+                         (const uint8_t*)kI, scores, ld);
+    else
+      hipLaunchKernelGGL(idx_prefill_bf16, grid, dim3(PF_THREADS), 0, st, b, (const uint16_t*)qI, w,
+                         (const uint16_t*)kI, scores, ld);
   } else if (b.nq <= IDX_BAL_MAXQ) {
     if (dtype == 2)
       hipLaunchKernelGGL(idx_decode_fp8_bal, dim3(IDX_BAL_GRID), dim3(IDX_DEC_THREADS), 0, st, b, qI, w, kI,
