@@ -476,12 +476,12 @@ __global__ __launch_bounds__(PF_THREADS) void idx_prefill_bf16(
 // product; its contraction slots are taken as bytes [64*half, 64*half + 64)
 // of the row (first product the lower 32, second the upper 32), the same for
 // query and key, so each lane reads 64 contiguous bytes of one key.
-constexpr int PF8_TK = 64;  // keys per LDS tile (two 32-key products)
+constexpr int PF8_TK = 256;  // keys per LDS tile (eight 32-key products)
 
 __global__ __launch_bounds__(PF_THREADS) void idx_prefill_fp8(
     BatchDev b, const uint8_t* __restrict__ qI, const float* __restrict__ w,
     const uint8_t* __restrict__ kI, float* __restrict__ scores, int64_t ld) {
-  // Key tile: 64 keys x 8 chunks of 16 B; chunk c of key k sits at slot
+  // Key tile: 256 keys x 8 chunks of 16 B; chunk c of key k sits at slot
   // k*8 + (c ^ ((k >> 1) & 7)), so the 16 keys a quarter-wave reads fall on
   // 16 distinct 16-byte bank groups.
   __shared__ u32x4 ktile[2][PF8_TK * 8];
@@ -489,7 +489,7 @@ __global__ __launch_bounds__(PF_THREADS) void idx_prefill_fp8(
   __shared__ int ncand[PF_QB];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31;
   const int half = lane >> 5;
   const int qg0 = blockIdx.y * PF_QB;
@@ -512,6 +512,7 @@ __global__ __launch_bounds__(PF_THREADS) void idx_prefill_fp8(
   const int64_t row0 = b.seq_row0[0];
 
   i32x8 a[PF_QPW][2];
+  float wr[PF_QPW][16];
   int nj[PF_QPW];
 #pragma unroll
   for (int j = 0; j < PF_QPW; ++j) {
@@ -521,41 +522,62 @@ __global__ __launch_bounds__(PF_THREADS) void idx_prefill_fp8(
     a[j][0] = cat32(load16(qrow), load16(qrow + 16));
     a[j][1] = cat32(load16(qrow + 32), load16(qrow + 48));
     nj[j] = ncand[ql];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) wr[j][i] = wl[ql * HI + 4 * half + 8 * (i >> 2) + (i & 3)];
   }
 
-  const int lk = tid >> 3;   // key of the tile this thread stages
+  constexpr int TK = PF8_TK;
+  constexpr int NR = TK * 8 / PF_THREADS;  // 16-byte chunks each thread stages
+  const int lk = tid >> 3;   // key of the tile this thread stages (plus r*PF_THREADS/8)
   const int lc = tid & 7;    // its 16-byte chunk
   const int lslot = lk * 8 + (lc ^ ((lk >> 1) & 7));
   const uint8_t* kb = kI + row0 * DI + lc * 16;
-  u32x4 pre = load16_nt(kb + (int64_t)min(kbase + lk, kend - 1) * DI);
-  int buf = 0;
-  for (int k0 = kbase; k0 < kend; k0 += PF8_TK) {
-    ktile[buf][lslot] = pre;
-    __syncthreads();
-    if (k0 + PF8_TK < kend) pre = load16_nt(kb + (int64_t)min(k0 + PF8_TK + lk, kend - 1) * DI);
+  u32x4 pre[NR];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
+  for (int r = 0; r < NR; ++r) pre[r] = load16_nt(kb + (int64_t)min(kbase + lk + (PF_THREADS / 8) * r, kend - 1) * DI);
+  // one buffer resource per query over exactly its candidate columns: a
+  // store at a column >= n_cand (or from the upper half-wave, which holds no
+  // result) lies outside it and is dropped without a branch
+  __amdgpu_buffer_rsrc_t srs[PF_QPW];
+#pragma unroll
+  for (int j = 0; j < PF_QPW; ++j) {
+    const int n = __builtin_amdgcn_readfirstlane(nj[j]);
+    srs[j] = __builtin_amdgcn_make_buffer_rsrc(scores + (int64_t)(qg0 + wave * PF_QPW + j) * ld, (short)0,
+                                               (int)((uint32_t)n * 4u), 0x00020000);
+  }
+  int buf = 0;
+  for (int k0 = kbase; k0 < kend; k0 += TK) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) ktile[buf][lslot + r * PF_THREADS] = pre[r];
+    __syncthreads();
+    // next tile (clamped, so the last iteration re-reads an in-range key)
+#pragma unroll
+    for (int r = 0; r < NR; ++r) pre[r] = load16_nt(kb + (int64_t)min(k0 + TK + lk + (PF_THREADS / 8) * r, kend - 1) * DI);
+    const int nsub = min(TK / 32, (kend - k0 + 31) / 32);
+    for (int sub = 0; sub < nsub; ++sub) {
       const int kk = sub * 32 + col;
       const int sw = (kk >> 1) & 7;
       const u32x4* krow = &ktile[buf][kk * 8];
       const i32x8 b0 = cat32(krow[(4 * half + 0) ^ sw], krow[(4 * half + 1) ^ sw]);
       const i32x8 b1 = cat32(krow[(4 * half + 2) ^ sw], krow[(4 * half + 3) ^ sw]);
-      const int kt0 = k0 + sub * 32;
+      // all queries of the wave, branch-free, so the products of one query
+      // overlap the epilogue of another
+      f32x16 acc[PF_QPW];
 #pragma unroll
       for (int j = 0; j < PF_QPW; ++j) {
-        if (kt0 >= nj[j]) continue;
-        f32x16 acc = {};
+        const f32x16 z = {};
         // format 0 = FP8 E4M3 for both operands, no block scaling
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[j][0], b0, acc, 0, 0, 0, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[j][1], b1, acc, 0, 0, 0, 0, 0, 0);
-        const float* wq = wl + (wave * PF_QPW + j) * HI + 4 * half;
+        acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[j][0], b0, z, 0, 0, 0, 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[j][1], b1, acc[j], 0, 0, 0, 0, 0, 0);
+      }
+      const int soff = half ? (int)0x80000000u : (k0 + sub * 32 + col) * 4;
+#pragma unroll
+      for (int j = 0; j < PF_QPW; ++j) {
         float part = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) part = fmaf(wq[8 * (i >> 2) + (i & 3)], fmaxf(acc[i], 0.0f), part);
+        for (int i = 0; i < 16; ++i) part = fmaf(wr[j][i], fmaxf(acc[j][i], 0.0f), part);
         part = halves_sum(part);
-        const int key = kt0 + col;
-        if (half == 0 && key < nj[j])
-          scores[(int64_t)(qg0 + wave * PF_QPW + j) * ld + key] = part;
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, part), srs[j], soff, 0, 0);
       }
     }
     buf ^= 1;
