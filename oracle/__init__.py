@@ -58,7 +58,7 @@ def _load():
         lib.oracle_index_score.restype = None
         lib.oracle_topk.argtypes = [f64p, ctypes.c_int64, ctypes.c_int64, i32p]
         lib.oracle_topk.restype = ctypes.c_int64
-        lib.oracle_mla_attend.argtypes = [f32p, f32p, i32p, ctypes.c_int64,
+        lib.oracle_mla_attend.argtypes = [f32p, f32p, i32p, ctypes.c_int64, ctypes.c_int32,
                                           ctypes.c_double, f64p, f64p]
         lib.oracle_mla_attend.restype = None
         lib.oracle_dims.argtypes = [i32p]
@@ -113,16 +113,21 @@ def topk(scores, k: int):
 
 
 def mla_attend(q, kv, sel, tau: float):
-    """Sparse MLA of one query: q [64,576], kv [rows,576], sel int32 [m] -> (o [64,512], lse [64])."""
+    """Sparse MLA of one query: q [64,W], kv [rows,W], sel int32 [m] -> (o [64,512], lse [64]).
+
+    W = 576 (512 latent + 64 rotary) or 512 for a layer without rotary
+    encoding (every fourth layer on the concept page keeps the latent alone).
+    """
     q, kv = _f32(q), _f32(kv)
     sel = np.ascontiguousarray(np.asarray(sel, np.int32))
-    assert q.shape == (H, D) and kv.ndim == 2 and kv.shape[1] == D
+    width = q.shape[-1]
+    assert width in (D, DC) and q.shape == (H, width) and kv.ndim == 2 and kv.shape[1] == width
     if sel.size and sel.max() >= kv.shape[0]:
         raise IndexError("selected position outside the cache rows")
     o = np.empty((H, DC), np.float64)
     lse = np.empty(H, np.float64)
     _load().oracle_mla_attend(_ptr(q, ctypes.c_float), _ptr(kv, ctypes.c_float),
-                              _ptr(sel, ctypes.c_int32), sel.shape[0], float(tau),
+                              _ptr(sel, ctypes.c_int32), sel.shape[0], width - DC, float(tau),
                               _ptr(o, ctypes.c_double), _ptr(lse, ctypes.c_double))
     return o, lse
 
@@ -154,3 +159,59 @@ def decode_query(qI, w, kI_seq, q_layers, kv_layers, n_cand: int, k: int, tau: f
         outs.append(o)
         lses.append(lse)
     return idx, m, outs, lses
+
+
+# ----------------------------------------------------------------------------
+# The model's layer schedule and one decode step over it
+# ----------------------------------------------------------------------------
+
+LAYERS = 72
+
+
+def layer_plan(n_layers: int = LAYERS):
+    """Per layer l < n_layers: (runs_indexer, rope, kv_source).
+
+    Rules of the concept page's list of changes to the DeepSeek recipe:
+      * every fourth layer (l = 3, 7, 11, ...) has no rotary encoding;
+      * from layer 39 on, those layers read layer 35's latent instead of
+        keeping their own (every layer that shares a cache is rotary-free,
+        and so is layer 35);
+      * 28 layers reuse the selection of the most recent layer that ran its
+        indexer.  Which ones (reading of the summary page's DSA paragraph):
+        from layer 16 on, in every group of four layers (16-19, 20-23, ...)
+        the middle two reuse the selection of the group's first layer, and
+        the first and last run their own indexer.
+    """
+    plan = []
+    for l in range(n_layers):
+        rope = (l + 1) % 4 != 0
+        kv_source = 35 if (l >= 39 and not rope) else l
+        reuses = l >= 16 and l % 4 in (1, 2)
+        plan.append((not reuses, rope, kv_source))
+    return plan
+
+
+def decode_layers(plan, qI_l, w_l, kI_l, q_l, kv_l, n_cand: int, k: int, tau: float):
+    """One query through the attention read of every layer of `plan`.
+
+    A layer that runs its indexer selects from its own indexer query, head
+    weights and keys (qI_l[l] [32,128], w_l[l] [32], kI_l[l] [rows,128]); a
+    layer that reuses takes the selection of the most recent layer that ran
+    its indexer.  Layer l attends with its query q_l[l] ([64,576], or
+    [64,512] without rotary encoding) over the cache of layer
+    plan[l].kv_source (kv_l[source] [rows,576 or 512]).
+    Returns ([idx of each layer], [o], [lse]).
+    """
+    idx_l, outs, lses = [], [], []
+    idx = m = None
+    for l, (runs, rope, src) in enumerate(plan):
+        if runs:
+            _, idx, m = select_query(qI_l[l], w_l[l], kI_l[l], n_cand, k)
+        if idx is None:
+            raise ValueError("the first layer must run its indexer")
+        o, lse = mla_attend(q_l[l], kv_l[src], idx[:m], tau)
+        idx_l.append(idx)
+        outs.append(o)
+        lses.append(lse)
+    return idx_l, outs, lses
+

@@ -30,7 +30,10 @@
  *   - the MLA read is in absorbed form: the 576-wide query is dotted with the
  *     576-wide cache row (512 latent + 64 rotary), the value is the 512-wide
  *     latent, the logit is scaled by tau, and the softmax runs over the
- *     selected positions only.
+ *     selected positions only;
+ *   - a layer without rotary encoding (every fourth layer, [ML4-concepts]
+ *     list of changes and "Cache": such a layer keeps the 512-value latent
+ *     alone) reads 512-wide rows, and its logit is the 512-wide dot product.
  *
  * All arithmetic is in IEEE double.  Inputs arrive as float (bf16 inputs are
  * widened exactly by the caller).  No blocking, fusion or reordering beyond
@@ -130,23 +133,26 @@ int64_t oracle_topk(const double* scores, int64_t n, int64_t k, int32_t* idx_out
 
 /*
  * Sparse MLA read of one query over a selected set ([ML4-concepts] "What to
- * keep", "Where to look", "Sparse attention"; absorbed form, reading above):
+ * keep", "Where to look", "Sparse attention"; absorbed form, reading above),
+ * with rotary width R = 64 (R = 0 for a layer without rotary encoding) and
+ * row width W = 512 + R:
  *   l[h][j] = tau * ( sum_{d<512} q[h][d]     * kv[sel_j][d]
- *                   + sum_{d<64}  q[h][512+d] * kv[sel_j][512+d] )
+ *                   + sum_{d<R}   q[h][512+d] * kv[sel_j][512+d] )
  *   M_h = max_j l[h][j];  Z_h = sum_j exp(l[h][j] - M_h)
  *   o[h][e] = sum_j exp(l[h][j] - M_h) / Z_h * kv[sel_j][e]    (e < 512)
  *   lse[h] = M_h + ln Z_h
- * q: [64][576]; kv: cache rows of the sequence, row p = position p, [.][576];
+ * q: [64][W]; kv: cache rows of the sequence, row p = position p, [.][W];
  * sel: m positions (any order; entries < 0 are skipped); o: [64][512];
  * lse: [64].  With no selected position, o = 0 and lse = -inf.
  * Parallel over heads for timing only.
  */
 void oracle_mla_attend(const float* q, const float* kv, const int32_t* sel, int64_t m,
-                       double tau, double* o, double* lse) {
+                       int32_t rope, double tau, double* o, double* lse) {
+  const int64_t W = ORC_DC + rope;
   int h;
 #pragma omp parallel for schedule(static)
   for (h = 0; h < ORC_H; ++h) {
-    const float* qh = q + (int64_t)h * ORC_D;
+    const float* qh = q + (int64_t)h * W;
     double* oh = o + (int64_t)h * ORC_DC;
     double* logit = (double*)malloc((size_t)(m > 0 ? m : 1) * sizeof(double));
     for (int e = 0; e < ORC_DC; ++e) oh[e] = 0.0;
@@ -154,11 +160,11 @@ void oracle_mla_attend(const float* q, const float* kv, const int32_t* sel, int6
     int64_t used = 0;
     for (int64_t j = 0; j < m; ++j) {
       if (sel[j] < 0) continue;
-      const float* row = kv + (int64_t)sel[j] * ORC_D;
-      double latent = 0.0, rope = 0.0;
+      const float* row = kv + (int64_t)sel[j] * W;
+      double latent = 0.0, rot = 0.0;
       for (int d = 0; d < ORC_DC; ++d) latent += (double)qh[d] * (double)row[d];
-      for (int d = 0; d < ORC_DR; ++d) rope += (double)qh[ORC_DC + d] * (double)row[ORC_DC + d];
-      logit[j] = tau * (latent + rope);
+      for (int d = 0; d < rope; ++d) rot += (double)qh[ORC_DC + d] * (double)row[ORC_DC + d];
+      logit[j] = tau * (latent + rot);
       if (logit[j] > mx) mx = logit[j];
       ++used;
     }
@@ -172,7 +178,7 @@ void oracle_mla_attend(const float* q, const float* kv, const int32_t* sel, int6
       if (sel[j] >= 0) z += exp(logit[j] - mx);
     for (int64_t j = 0; j < m; ++j) {
       if (sel[j] < 0) continue;
-      const float* row = kv + (int64_t)sel[j] * ORC_D;
+      const float* row = kv + (int64_t)sel[j] * W;
       double p = exp(logit[j] - mx) / z;
       for (int e = 0; e < ORC_DC; ++e) oh[e] += p * (double)row[e];
     }

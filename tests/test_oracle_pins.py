@@ -5,7 +5,9 @@ Each test ties one oracle function to mathematics or to a figure of the
 ReLU, a head/weight index mismatch, a transposed operand, a wrong tie-break,
 a softmax normalised over the wrong set) fails at least one of them.
 """
+import json
 import math
+import os
 
 import numpy as np
 import pytest
@@ -292,3 +294,115 @@ def test_decode_selection_shared_across_layers():
     sc = oracle.index_score(w.qI[0], w.w[0], w.kI)
     order = np.lexsort((np.arange(3000), -sc))[:2048]
     assert np.array_equal(np.sort(order), idx)
+
+
+# ----------------------------------------------------------------------------
+# layers without rotary encoding, the layer schedule, a decode step over it
+# ----------------------------------------------------------------------------
+
+
+def _sdpa_w(q, kv, tau):
+    """torch's library attention in float64 with keys = the whole row and
+    values = its first 512 entries, for any row width."""
+    Q = torch.from_numpy(q.astype(np.float64))[None, None]
+    K = torch.from_numpy(kv.astype(np.float64))[None, None]
+    V = torch.from_numpy(kv[:, :DC].astype(np.float64))[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(Q, K, V, scale=tau)[0, 0].numpy()
+
+
+def test_mla_without_rotary_part_equals_library_attention():
+    """A layer without rotary encoding keeps the 512-value latent alone
+    (concept page, list of changes and "Cache"): its read is dense softmax
+    attention over 512-wide rows when every position is kept."""
+    rng = np.random.default_rng(31)
+    n = 900
+    q = rng.standard_normal((H, DC)).astype(np.float32)
+    kv = rng.standard_normal((n, DC)).astype(np.float32)
+    o, lse = oracle.mla_attend(q, kv, np.arange(n, dtype=np.int32), TAU)
+    np.testing.assert_allclose(o, _sdpa_w(q, kv, TAU), rtol=1e-10, atol=1e-12)
+    from scipy.special import logsumexp
+    np.testing.assert_allclose(lse, logsumexp(TAU * (q.astype(np.float64) @ kv.astype(np.float64).T), axis=1),
+                               rtol=1e-12)
+
+
+def test_mla_without_rotary_part_equals_zero_rotary_query():
+    """The 512-wide read equals the 576-wide read with a zero rotary query,
+    whatever the rotary keys hold."""
+    rng = np.random.default_rng(32)
+    n = 400
+    q = rng.standard_normal((H, DC)).astype(np.float32)
+    kv = rng.standard_normal((n, DC)).astype(np.float32)
+    sel = np.sort(rng.choice(n, 150, replace=False)).astype(np.int32)
+    q576 = np.concatenate([q, np.zeros((H, DR), np.float32)], axis=1)
+    kv576 = np.concatenate([kv, rng.standard_normal((n, DR)).astype(np.float32) * 5], axis=1)
+    o1, l1 = oracle.mla_attend(q, kv, sel, TAU)
+    o2, l2 = oracle.mla_attend(q576, kv576, sel, TAU)
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(l1, l2, rtol=1e-12)
+
+
+def _page_figures():
+    fx = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_arithmetic.json")))
+    return {f["name"]: f["value"] for f in fx["figures"]}
+
+
+def test_layer_plan_reproduces_the_pages_counts():
+    """The schedule built from the page's rules reproduces every count the
+    page prints about it (tests/golden/pages_arithmetic.json)."""
+    fig = _page_figures()
+    plan = oracle.layer_plan()
+    assert len(plan) == fig["layers"] == 72
+    assert sum(r for r, _, _ in plan) == fig["indexer_layers"] == 44
+    assert sum(not r for r, _, _ in plan) == 28
+    own = [(l, rope) for l, (_, rope, src) in enumerate(plan) if src == l]
+    assert sum(rope for _, rope in own) == fig["owning_rope_layers"] == 54
+    assert sum(not rope for _, rope in own) == fig["owning_nope_layers"] == 9
+    assert sum(512 + (64 if rope else 0) for _, rope in own) == fig["cached_values_per_position"] == 35712
+    readers = [l for l, (_, _, src) in enumerate(plan) if src != l]
+    assert readers == list(range(39, 72, 4)) and len(readers) == 9
+    assert 512 * len(readers) == fig["values_saved_by_cache_sharing"] == 4608
+    # every layer that shares a cache is rotary-free, and so is its source
+    assert all(not plan[l][1] and not plan[plan[l][2]][1] for l in readers)
+    # 54 rotary layers, 18 without
+    assert sum(rope for _, rope, _ in plan) == 54
+
+
+def test_layer_plan_selection_runs():
+    """Reusing layers come in runs of two after an indexer layer, from layer
+    16 on, and every run (the indexer layer and its reusers) is rotary."""
+    plan = oracle.layer_plan()
+    runs, cur = [], None
+    for l, (r, rope, _) in enumerate(plan):
+        if r:
+            cur = [l]
+            runs.append(cur)
+        else:
+            cur.append(l)
+    shared = [x for x in runs if len(x) > 1]
+    assert shared == [[g, g + 1, g + 2] for g in range(16, 72, 4)]
+    assert all(plan[l][1] for x in shared for l in x)
+    assert all(len(x) == 1 for x in runs if x[0] < 16)
+
+
+def test_decode_layers_follows_the_plan():
+    """A decode step over a schedule: reusing layers carry the selection of
+    the most recent indexer layer, a cache-sharing layer reads its source's
+    rows, and a rotary-free layer reads 512-wide rows."""
+    rng = np.random.default_rng(33)
+    n = 3000
+    plan = oracle.layer_plan(44)                      # layers 0..43: runs, layer 35, readers 39 and 43
+    width = [576 if rope else 512 for _, rope, _ in plan]
+    qI = [rng.integers(-3, 4, (32, 128)).astype(np.float32) for _ in plan]
+    w = [rng.integers(1, 5, 32).astype(np.float32) for _ in plan]
+    kI = [rng.integers(-3, 4, (n, 128)).astype(np.float32) for _ in plan]
+    q = [rng.standard_normal((H, wd)).astype(np.float32) for wd in width]
+    kv = [rng.standard_normal((n, wd)).astype(np.float32) for wd in width]
+    idx_l, outs, lses = oracle.decode_layers(plan, qI, w, kI, q, kv, n, 2048, TAU)
+    for l, (runs, rope, src) in enumerate(plan):
+        last = max(j for j in range(l + 1) if plan[j][0])
+        ref_idx, m = oracle.topk(oracle.index_score(qI[last], w[last], kI[last]), 2048)
+        assert np.array_equal(idx_l[l], ref_idx)
+        o, lse = oracle.mla_attend(q[l], kv[src], ref_idx[:m], TAU)
+        assert np.array_equal(outs[l], o) and np.array_equal(lses[l], lse)
+    assert plan[39][2] == 35 and plan[43][2] == 35 and not plan[35][1]
+    assert np.array_equal(idx_l[17], idx_l[16]) and np.array_equal(idx_l[18], idx_l[16])
