@@ -16,16 +16,22 @@
  *     2,048, and a softmax normalised over the kept positions alone; its cost
  *     figures (32 x 128 multiply-adds per scored position, 64 x (512 + 64 +
  *     512) per attended one) fix the shapes below.
+ *   - the change list: every fourth layer has no rotary encoding (its rows
+ *     hold the 512-value latent alone), from layer 39 on those layers read
+ *     layer 35's latent, and 28 layers reuse the selection of the most
+ *     recent layer that ran its indexer ("Cache" counts the result).
  * The page's display formula for the score was lost; this library computes
  *   I[q][s] = sum_{h<32} w[q][h] * max(0, sum_{d<128} qI[q][h][d] * kI[s][d])
- * and the absorbed-form MLA read
- *   l[h][j] = scale * (q[h][0:576] . kv[S_j][0:576]),  p = softmax_j(l) over S,
+ * and the absorbed-form MLA read, with row width W = 512 + rope_dim
+ * (rope_dim = 64, or 0 in a layer without rotary encoding):
+ *   l[h][j] = scale * (q[h][0:W] . kv[S_j][0:W]),  p = softmax_j(l) over S,
  *   o[h][:] = sum_j p[h][j] * kv[S_j][0:512],  lse[h] = log sum_j exp(l[h][j]).
  *
  * Conventions shared by every entry point
  *   - Every array argument is a DEVICE pointer owned by the caller, except
- *     the dsa_batch_t struct itself and the per-layer pointer tables of the
- *     fused call, which are HOST memory read during the call only.
+ *     the dsa_batch_t struct itself, the layer plans and the per-layer
+ *     pointer tables of the multi-layer calls, which are HOST memory read
+ *     during the call only.
  *   - The library never allocates, frees or synchronises.  Work is enqueued
  *     on `stream` (a hipStream_t; NULL = the default stream) and the call
  *     returns at once; results are ready when the stream reaches them.
@@ -33,11 +39,12 @@
  *     validated on the host before anything is enqueued; a validation error
  *     enqueues nothing.  A failed launch returns DSA_ERR_HIP.  The message of
  *     the last error on the calling thread is in dsa_last_error().
- *   - Dtypes: DSA_BF16 (bf16 storage, fp32 accumulation) or DSA_F32.  One
- *     `dtype` covers the indexer query/keys and the MLA query/cache rows;
- *     indexer weights, scores and log-sum-exp are always float32.
+ *   - Dtypes: DSA_BF16 (bf16 storage, fp32 accumulation) or DSA_F32; the
+ *     indexer's query and keys may also be DSA_FP8_E4M3.  Indexer weights,
+ *     scores and log-sum-exp are always float32.
  *   - Alignment: every pointer 16-byte aligned.  Row strides are fixed:
- *     indexer keys 128 elements, cache rows 576 (512 latent then 64 rotary).
+ *     indexer keys 128 elements, cache rows 512 + rope_dim (512 latent, then
+ *     the rotary key if any).
  *   - Entries are re-entrant; calls that share a workspace race unless they
  *     are ordered on one stream.
  */
@@ -51,7 +58,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 2
+#define DSA_ABI_VERSION 3
 
 #define DSA_INDEX_HEADS 32  /* indexer heads                          */
 #define DSA_INDEX_DIM 128   /* indexer head width                     */
@@ -61,6 +68,7 @@ extern "C" {
 #define DSA_ROW 576         /* cache row = latent + rotary key        */
 #define DSA_TOPK_MAX 2048   /* largest supported k (the pages' 2,048) */
 #define DSA_MAX_LAYERS 16   /* largest n_layers of the fused call     */
+#define DSA_ML4_LAYERS 72   /* decoder layers of Mistral Large 4      */
 #define DSA_MAX_LEN 3728270 /* longest sequence: its 1,152-byte bf16
                                cache rows are addressed with 32 bits   */
 
@@ -156,8 +164,10 @@ int32_t dsa_topk(const dsa_batch_t* batch, const float* scores, int64_t ld, int3
 /*
  * Sparse MLA read of one layer ("What to keep", "Sparse attention").
  *   dtype, out_dtype  DSA_F32 or DSA_BF16
- *   q   [nq][64][576] dtype    absorbed query: 512 latent-space + 64 rotary
- *   kv  [rows][576]   dtype    cache rows (512 latent, 64 rotary key)
+ *   rope_dim   DSA_ROPE (64), or 0 for a layer without rotary encoding;
+ *              W = 512 + rope_dim (other values: DSA_ERR_SHAPE)
+ *   q   [nq][64][W]   dtype    absorbed query: 512 latent-space (+ 64 rotary)
+ *   kv  [rows][W]     dtype    cache rows (512 latent (+ 64 rotary key))
  *   idx [nq][k]       int32    selected positions; entries outside
  *                              [0, n_cand(q)) (e.g. the -1 padding) are skipped
  *   scale                      logit scale (the harness uses 1/sqrt(192))
@@ -168,7 +178,7 @@ int32_t dsa_topk(const dsa_batch_t* batch, const float* scores, int64_t ld, int3
  *   1 <= k <= 2,048.  ws: mla_sparse_attend_workspace_size(nq, k, 1) bytes.
  */
 size_t mla_sparse_attend_workspace_size(int32_t nq, int32_t k, int32_t n_layers);
-int32_t mla_sparse_attend(const dsa_batch_t* batch, int32_t dtype, const void* q, const void* kv,
+int32_t mla_sparse_attend(const dsa_batch_t* batch, int32_t dtype, int32_t rope_dim, const void* q, const void* kv,
                           const int32_t* idx, int32_t k, float scale, void* out,
                           int32_t out_dtype, float* lse, void* ws, size_t ws_bytes,
                           void* stream);
@@ -179,10 +189,10 @@ int32_t mla_sparse_attend(const dsa_batch_t* batch, int32_t dtype, const void* q
  * indexer).  Runs the indexer and the top-k once, then the sparse MLA read
  * of n_layers layers, each with its own query and cache, over that one
  * selection.  Arguments as in the three calls above; index_dtype is the
- * indexer's dtype (q_idx, k_idx) and dtype that of every layer's query and
- * cache rows.  Per-layer arrays come as HOST tables of n_layers device
- * pointers:
- *   q_l[l]   [nq][64][576] dtype    kv_l[l] [rows][576] dtype
+ * indexer's dtype (q_idx, k_idx), dtype and rope_dim those of every layer's
+ * query and cache rows.  Per-layer arrays come as HOST tables of n_layers
+ * device pointers (two layers may name the same cache):
+ *   q_l[l]   [nq][64][W] dtype      kv_l[l] [rows][W] dtype
  *   out_l[l] [nq][64][512] out_dtype  lse_l[l] [nq][64] float32 (lse_l or
  *   any entry may be NULL)
  *   idx_out  [nq][k] int32 (may be NULL): the shared selection.
@@ -192,10 +202,69 @@ size_t dsa_mla_decode_fused_workspace_size(int32_t nq, int32_t max_len, int32_t 
                                            int32_t n_layers);
 int32_t dsa_mla_decode_fused(const dsa_batch_t* batch, int32_t index_dtype, const void* q_idx,
                              const float* w_idx, const void* k_idx, int32_t k, int32_t n_layers,
-                             int32_t dtype, const void* const* q_l, const void* const* kv_l,
-                             void* const* out_l, float* const* lse_l, int32_t out_dtype,
-                             float scale, int32_t* idx_out, void* ws, size_t ws_bytes,
-                             void* stream);
+                             int32_t dtype, int32_t rope_dim, const void* const* q_l,
+                             const void* const* kv_l, void* const* out_l, float* const* lse_l,
+                             int32_t out_dtype, float scale, int32_t* idx_out, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/*
+ * Layer schedule (concept page, change list and layer map).  For each layer:
+ *   runs_indexer  1: the layer scores and selects with its own indexer;
+ *                 0: it reuses the selection of the most recent layer that
+ *                 ran its indexer (layer 0 must run one);
+ *   rope_dim      DSA_ROPE, or 0 for a layer without rotary encoding;
+ *   kv_source     the layer whose cache it reads: itself, or an earlier
+ *                 layer that owns its cache and has the same rope_dim
+ *                 (a layer never reads a cache built with another
+ *                 positional scheme).
+ * dsa_ml4_layer_plan fills plan[0 .. n_layers) with Mistral Large 4's
+ * schedule (1 <= n_layers <= DSA_ML4_LAYERS; fewer layers take the first
+ * ones): no rotary encoding in layers l with (l + 1) % 4 == 0; from layer 39
+ * those layers read layer 35's cache; from layer 16, in every group of four
+ * layers the middle two reuse the selection of the group's first layer
+ * (this reading of the pages gives the 44 indexer layers, 28 reusing layers
+ * and 35,712 cached values per position that the concept page prints).
+ * plan is HOST memory.
+ */
+typedef struct dsa_layer_plan {
+  int32_t runs_indexer;
+  int32_t rope_dim;
+  int32_t kv_source;
+} dsa_layer_plan_t;
+
+int32_t dsa_ml4_layer_plan(int32_t n_layers, dsa_layer_plan_t* plan);
+
+/*
+ * Decode read over a stack of layers under a schedule: for each layer in
+ * order, run the indexer and the top-k if the plan says so, then the sparse
+ * MLA read over the current selection, reading the cache of the layer's
+ * kv_source.  Consecutive layers that share a selection and a rope_dim run
+ * as one MLA launch (up to DSA_MAX_LAYERS layers).  HOST tables of n_layers
+ * device pointers:
+ *   q_idx_l[l] [nq][32][128] index_dtype, w_idx_l[l] [nq][32] float32,
+ *   k_idx_l[l] [rows][128] index_dtype    read for indexer layers only
+ *                                          (other entries may be NULL);
+ *   q_l[l]     [nq][64][W_l] dtype         W_l = 512 + plan[l].rope_dim;
+ *   kv_l[l]    [rows][W_l] dtype           read for layers that own their
+ *                                          cache (kv_source == l); layer l
+ *                                          reads kv_l[plan[l].kv_source];
+ *   out_l[l]   [nq][64][512] out_dtype;   lse_l (or an entry) may be NULL;
+ *   idx_l      may be NULL; idx_l[l] (may be NULL) [nq][k] int32 receives
+ *              the selection made at indexer layer l.
+ *   1 <= n_layers <= DSA_ML4_LAYERS.
+ *   ws: dsa_mla_decode_layers_workspace_size(nq, max_len, k, n_layers, plan).
+ * An invalid plan (first layer not an indexer layer, rope_dim not 0 or 64,
+ * kv_source after the layer, not owning its cache or with another rope_dim)
+ * is DSA_ERR_SHAPE; the size query then returns 0.
+ */
+size_t dsa_mla_decode_layers_workspace_size(int32_t nq, int32_t max_len, int32_t k, int32_t n_layers,
+                                            const dsa_layer_plan_t* plan);
+int32_t dsa_mla_decode_layers(const dsa_batch_t* batch, int32_t n_layers, const dsa_layer_plan_t* plan,
+                              int32_t index_dtype, const void* const* q_idx_l,
+                              const float* const* w_idx_l, const void* const* k_idx_l, int32_t k,
+                              int32_t dtype, const void* const* q_l, const void* const* kv_l,
+                              void* const* out_l, float* const* lse_l, int32_t out_dtype, float scale,
+                              int32_t* const* idx_l, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

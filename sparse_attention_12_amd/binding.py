@@ -23,7 +23,16 @@ EXPORTS = [
     "dsa_abi_version", "dsa_status_string", "dsa_last_error", "dsa_index_score",
     "dsa_topk_workspace_size", "dsa_topk", "mla_sparse_attend_workspace_size",
     "mla_sparse_attend", "dsa_mla_decode_fused_workspace_size", "dsa_mla_decode_fused",
+    "dsa_ml4_layer_plan", "dsa_mla_decode_layers_workspace_size", "dsa_mla_decode_layers",
 ]
+ML4_LAYERS = 72
+
+
+class LayerPlan(ctypes.Structure):
+    """One layer of a schedule: whether it runs its indexer, its rotary
+    width (64 or 0) and the layer whose cache it reads."""
+    _fields_ = [("runs_indexer", ctypes.c_int32), ("rope_dim", ctypes.c_int32),
+                ("kv_source", ctypes.c_int32)]
 
 
 class DsaBatch(ctypes.Structure):
@@ -53,13 +62,21 @@ def _load() -> ctypes.CDLL:
     lib.dsa_topk.restype = i32
     lib.mla_sparse_attend_workspace_size.argtypes = [i32, i32, i32]
     lib.mla_sparse_attend_workspace_size.restype = sz
-    lib.mla_sparse_attend.argtypes = [bp, i32, vp, vp, vp, i32, ctypes.c_float, vp, i32, vp, vp, sz, vp]
+    lib.mla_sparse_attend.argtypes = [bp, i32, i32, vp, vp, vp, i32, ctypes.c_float, vp, i32, vp, vp, sz, vp]
     lib.mla_sparse_attend.restype = i32
     lib.dsa_mla_decode_fused_workspace_size.argtypes = [i32, i32, i32, i32]
     lib.dsa_mla_decode_fused_workspace_size.restype = sz
-    lib.dsa_mla_decode_fused.argtypes = [bp, i32, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, i32,
+    lib.dsa_mla_decode_fused.argtypes = [bp, i32, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, i32,
                                          ctypes.c_float, vp, vp, sz, vp]
     lib.dsa_mla_decode_fused.restype = i32
+    pp = ctypes.POINTER(LayerPlan)
+    lib.dsa_ml4_layer_plan.argtypes = [i32, pp]
+    lib.dsa_ml4_layer_plan.restype = i32
+    lib.dsa_mla_decode_layers_workspace_size.argtypes = [i32, i32, i32, i32, pp]
+    lib.dsa_mla_decode_layers_workspace_size.restype = sz
+    lib.dsa_mla_decode_layers.argtypes = [bp, i32, pp, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, i32,
+                                          ctypes.c_float, vp, vp, sz, vp]
+    lib.dsa_mla_decode_layers.restype = i32
     return lib
 
 
@@ -159,12 +176,20 @@ def mla_sparse_attend_workspace_size(nq: int, k: int, n_layers: int = 1) -> int:
     return int(lib.mla_sparse_attend_workspace_size(nq, k, n_layers))
 
 
+def _rope(q, kv=None) -> int:
+    """Rotary width of a layer from its query's row width (576 or 512)."""
+    rope = int(q.shape[-1]) - LATENT
+    if kv is not None and int(kv.shape[-1]) != int(q.shape[-1]):
+        raise ValueError(f"query rows are {q.shape[-1]} wide but cache rows {kv.shape[-1]}")
+    return rope
+
+
 def mla_sparse_attend(batch: Batch, q, kv, idx, k: int, scale: float, out, lse=None, ws=None,
                       stream=None):
     ws = _workspace(ws, mla_sparse_attend_workspace_size(batch.nq, k, 1), q)
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib.mla_sparse_attend(batch.ref, _dt(q), _p(q), _p(kv), _p(idx), k, scale, _p(out), _dt(out),
-                                 _p(lse), _p(ws), wsb, _stream(stream)), "mla_sparse_attend")
+    _check(lib.mla_sparse_attend(batch.ref, _dt(q), _rope(q, kv), _p(q), _p(kv), _p(idx), k, scale, _p(out),
+                                 _dt(out), _p(lse), _p(ws), wsb, _stream(stream)), "mla_sparse_attend")
     return out
 
 
@@ -185,7 +210,51 @@ def dsa_mla_decode_fused(batch: Batch, q_idx, w_idx, k_idx, k: int, q_l: Sequenc
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     cv = lambda a: None if a is None else ctypes.cast(a, ctypes.c_void_p)
     _check(lib.dsa_mla_decode_fused(batch.ref, _dt(q_idx), _p(q_idx), _p(w_idx), _p(k_idx), k, n,
-                                    _dt(q_l[0]), cv(qa), cv(kva), cv(oa), cv(la), _dt(out_l[0]), scale,
-                                    _p(idx_out),
+                                    _dt(q_l[0]), _rope(q_l[0], kv_l[0]), cv(qa), cv(kva), cv(oa), cv(la),
+                                    _dt(out_l[0]), scale, _p(idx_out),
                                     _p(ws), wsb, _stream(stream)), "dsa_mla_decode_fused")
     return out_l
+
+
+def _plan_array(plan):
+    arr = (LayerPlan * len(plan))()
+    for i, p in enumerate(plan):
+        arr[i] = LayerPlan(int(p[0]), int(p[1]), int(p[2]))
+    return arr
+
+
+def dsa_ml4_layer_plan(n_layers: int = ML4_LAYERS):
+    """Mistral Large 4's schedule as a list of (runs_indexer, rope_dim, kv_source)."""
+    arr = (LayerPlan * max(n_layers, 1))()
+    _check(lib.dsa_ml4_layer_plan(n_layers, arr), "dsa_ml4_layer_plan")
+    return [(bool(p.runs_indexer), int(p.rope_dim), int(p.kv_source)) for p in arr[:n_layers]]
+
+
+def dsa_mla_decode_layers_workspace_size(nq: int, max_len: int, k: int, plan) -> int:
+    return int(lib.dsa_mla_decode_layers_workspace_size(nq, max_len, k, len(plan), _plan_array(plan)))
+
+
+def dsa_mla_decode_layers(batch: Batch, plan, qI_l: Sequence, w_l: Sequence, kI_l: Sequence, k: int,
+                          q_l: Sequence, kv_l: Sequence, out_l: Sequence, scale: float,
+                          lse_l: Optional[Sequence] = None, idx_l: Optional[Sequence] = None, ws=None,
+                          stream=None):
+    """Decode read over a stack of layers under `plan` (list of
+    (runs_indexer, rope_dim, kv_source)).  Per-layer sequences may hold None
+    where the library does not read the entry (indexer inputs of reusing
+    layers, caches of layers that read another layer's cache)."""
+    n = len(plan)
+    arr = ctypes.c_void_p * n
+    tab = lambda ts: arr(*[(0 if t is None else t.data_ptr()) for t in ts])
+    first = next(t for t in qI_l if t is not None)
+    ws = _workspace(ws, dsa_mla_decode_layers_workspace_size(batch.nq, batch.max_len, k, plan), first)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    cv = lambda a: None if a is None else ctypes.cast(a, ctypes.c_void_p)
+    tabs = [tab(qI_l), tab(w_l), tab(kI_l), tab(q_l), tab(kv_l), tab(out_l)]
+    la = None if lse_l is None else tab(lse_l)
+    ia = None if idx_l is None else tab(idx_l)
+    _check(lib.dsa_mla_decode_layers(batch.ref, n, _plan_array(plan), _dt(first), cv(tabs[0]), cv(tabs[1]),
+                                     cv(tabs[2]), k, _dt(q_l[0]), cv(tabs[3]), cv(tabs[4]), cv(tabs[5]), cv(la),
+                                     _dt(out_l[0]), scale, cv(ia), _p(ws), wsb, _stream(stream)),
+           "dsa_mla_decode_layers")
+    return out_l
+

@@ -67,6 +67,12 @@ int check_index_dtype(int32_t dt, const char* what) {
   return DSA_OK;
 }
 
+int check_rope(int32_t rope_dim) {
+  if (rope_dim != 0 && rope_dim != DSA_ROPE)
+    return fail(DSA_ERR_SHAPE, "rope_dim = %d is neither 0 nor %d", rope_dim, DSA_ROPE);
+  return DSA_OK;
+}
+
 int check_k(int32_t k) {
   if (k < 1) return fail(DSA_ERR_SHAPE, "k = %d < 1", k);
   if (k > DSA_TOPK_MAX) return fail(DSA_ERR_UNSUPPORTED, "k = %d > %d", k, DSA_TOPK_MAX);
@@ -152,13 +158,14 @@ static int check_mla_layer(const void* q, const void* kv, const void* out) {
   return DSA_OK;
 }
 
-int32_t mla_sparse_attend(const dsa_batch_t* batch, int32_t dtype, const void* q, const void* kv,
+int32_t mla_sparse_attend(const dsa_batch_t* batch, int32_t dtype, int32_t rope_dim, const void* q, const void* kv,
                           const int32_t* idx, int32_t k, float scale, void* out, int32_t out_dtype,
                           float* lse, void* ws, size_t ws_bytes, void* stream) {
   dsa::BatchDev b;
   int st = check_batch(batch, &b);
   if (st) return st;
   if ((st = check_dtype(dtype, "dtype"))) return st;
+  if ((st = check_rope(rope_dim))) return st;
   if ((st = check_dtype(out_dtype, "out_dtype"))) return st;
   if ((st = check_k(k))) return st;
   if (b.nq == 0) return DSA_OK;
@@ -174,7 +181,8 @@ int32_t mla_sparse_attend(const dsa_batch_t* batch, int32_t dtype, const void* q
   L.kv[0] = kv;
   L.out[0] = out;
   L.lse[0] = lse;
-  return hip_status(dsa::launch_mla(b, dtype, L, 1, idx, k, scale, out_dtype, ws, ws_bytes, as_stream(stream)),
+  return hip_status(dsa::launch_mla(b, dtype, rope_dim, L, 1, idx, k, scale, out_dtype, ws, ws_bytes,
+                                    as_stream(stream)),
                     "mla_sparse_attend launch");
 }
 
@@ -200,9 +208,28 @@ size_t dsa_mla_decode_fused_workspace_size(int32_t nq, int32_t max_len, int32_t 
   return fused_parts(nq, max_len, k, n_layers, &a, &c, &d);
 }
 
+// Indexer scores, then top-k into idx, using the scores and top-k parts of
+// a fused-layout workspace; the indexer launch also clears the top-k
+// histograms, so the workspace needs no clearing by the caller.
+static int run_selection(const dsa::BatchDev& b, int32_t index_dtype, const void* q_idx, const float* w_idx,
+                         const void* k_idx, int32_t k, int32_t* idx, char* base, size_t off_topk, size_t off_mla,
+                         hipStream_t s) {
+  int st;
+  float* scores = (float*)base;
+  dsa::ZeroSpans z;
+  z.s[0] = dsa::topk_zero_span(base + off_topk, b.nq, b.max_len);
+  z.s[1] = dsa::ZeroSpan{nullptr, 0, 0};
+  if ((st = hip_status(dsa::launch_index_score(b, index_dtype, q_idx, w_idx, k_idx, scores, b.max_len, s, &z),
+                       "index score launch")))
+    return st;
+  return hip_status(dsa::launch_topk(b, scores, b.max_len, k, idx, nullptr, base + off_topk, off_mla - off_topk, s,
+                                     true),
+                    "top-k launch");
+}
+
 int32_t dsa_mla_decode_fused(const dsa_batch_t* batch, int32_t index_dtype, const void* q_idx,
                              const float* w_idx, const void* k_idx, int32_t k, int32_t n_layers,
-                             int32_t dtype, const void* const* q_l, const void* const* kv_l,
+                             int32_t dtype, int32_t rope_dim, const void* const* q_l, const void* const* kv_l,
                              void* const* out_l, float* const* lse_l, int32_t out_dtype, float scale,
                              int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
   dsa::BatchDev b;
@@ -210,6 +237,7 @@ int32_t dsa_mla_decode_fused(const dsa_batch_t* batch, int32_t index_dtype, cons
   if (st) return st;
   if ((st = check_index_dtype(index_dtype, "index_dtype"))) return st;
   if ((st = check_dtype(dtype, "dtype"))) return st;
+  if ((st = check_rope(rope_dim))) return st;
   if ((st = check_dtype(out_dtype, "out_dtype"))) return st;
   if ((st = check_k(k))) return st;
   if (n_layers < 1) return fail(DSA_ERR_SHAPE, "n_layers = %d < 1", n_layers);
@@ -234,24 +262,128 @@ int32_t dsa_mla_decode_fused(const dsa_batch_t* batch, int32_t index_dtype, cons
     return fail(DSA_ERR_WORKSPACE, "fused workspace: %zu bytes given, %zu needed", ws_bytes, need);
   if (!aligned16(ws)) return fail(DSA_ERR_ALIGN, "ws is not 16-byte aligned");
   char* base = (char*)ws;
-  float* scores = (float*)base;
   int32_t* idx = idx_out ? idx_out : (int32_t*)(base + off_idx);
   hipStream_t s = as_stream(stream);
-  // The indexer launch also clears the top-k histograms of this call, so
-  // the workspace needs no clearing by the caller and no launch of its own.
-  dsa::ZeroSpans z;
-  z.s[0] = dsa::topk_zero_span(base + off_topk, b.nq, b.max_len);
-  z.s[1] = dsa::ZeroSpan{nullptr, 0, 0};
-  if ((st = hip_status(dsa::launch_index_score(b, index_dtype, q_idx, w_idx, k_idx, scores, b.max_len, s, &z),
-                       "fused: index score launch")))
-    return st;
-  if ((st = hip_status(dsa::launch_topk(b, scores, b.max_len, k, idx, nullptr, base + off_topk,
-                                        off_mla - off_topk, s, true),
-                       "fused: top-k launch")))
-    return st;
-  return hip_status(dsa::launch_mla(b, dtype, L, n_layers, idx, k, scale, out_dtype, base + off_mla,
+  if ((st = run_selection(b, index_dtype, q_idx, w_idx, k_idx, k, idx, base, off_topk, off_mla, s))) return st;
+  return hip_status(dsa::launch_mla(b, dtype, rope_dim, L, n_layers, idx, k, scale, out_dtype, base + off_mla,
                                     need - off_mla, s),
                     "fused: MLA launch");
+}
+
+int32_t dsa_ml4_layer_plan(int32_t n_layers, dsa_layer_plan_t* plan) {
+  if (plan == nullptr) return fail(DSA_ERR_NULL, "plan is NULL");
+  if (n_layers < 1 || n_layers > DSA_ML4_LAYERS)
+    return fail(DSA_ERR_SHAPE, "n_layers = %d outside [1, %d]", n_layers, DSA_ML4_LAYERS);
+  for (int l = 0; l < n_layers; ++l) {
+    const bool rotary = (l + 1) % 4 != 0;   // every fourth layer has no rotary encoding
+    plan[l].rope_dim = rotary ? DSA_ROPE : 0;
+    plan[l].kv_source = (!rotary && l >= 39) ? 35 : l;   // layer 35's latent, from layer 39 on
+    plan[l].runs_indexer = (l >= 16 && (l % 4 == 1 || l % 4 == 2)) ? 0 : 1;
+  }
+  return DSA_OK;
+}
+
+// Validates a plan; on success *max_group is the largest number of layers
+// one MLA launch covers (consecutive layers with one selection and one
+// rope_dim, at most DSA_MAX_LAYERS).
+static int check_plan(int32_t n_layers, const dsa_layer_plan_t* plan, int* max_group) {
+  if (plan == nullptr) return fail(DSA_ERR_NULL, "plan is NULL");
+  if (n_layers < 1 || n_layers > DSA_ML4_LAYERS)
+    return fail(DSA_ERR_SHAPE, "n_layers = %d outside [1, %d]", n_layers, DSA_ML4_LAYERS);
+  if (!plan[0].runs_indexer) return fail(DSA_ERR_SHAPE, "layer 0 does not run its indexer");
+  int group = 0, best = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    const dsa_layer_plan_t& p = plan[l];
+    if (p.rope_dim != 0 && p.rope_dim != DSA_ROPE)
+      return fail(DSA_ERR_SHAPE, "layer %d: rope_dim = %d is neither 0 nor %d", l, p.rope_dim, DSA_ROPE);
+    if (p.kv_source < 0 || p.kv_source > l)
+      return fail(DSA_ERR_SHAPE, "layer %d: kv_source = %d is not an earlier layer", l, p.kv_source);
+    const dsa_layer_plan_t& src = plan[p.kv_source];
+    if (src.kv_source != p.kv_source)
+      return fail(DSA_ERR_SHAPE, "layer %d: its kv_source %d does not own its cache", l, p.kv_source);
+    if (src.rope_dim != p.rope_dim)
+      return fail(DSA_ERR_SHAPE, "layer %d: kv_source %d has another rope_dim", l, p.kv_source);
+    const bool joins = l > 0 && !p.runs_indexer && p.rope_dim == plan[l - 1].rope_dim && group < DSA_MAX_LAYERS;
+    group = joins ? group + 1 : 1;
+    best = group > best ? group : best;
+  }
+  *max_group = best;
+  return DSA_OK;
+}
+
+size_t dsa_mla_decode_layers_workspace_size(int32_t nq, int32_t max_len, int32_t k, int32_t n_layers,
+                                            const dsa_layer_plan_t* plan) {
+  int group = 0;
+  if (nq <= 0 || max_len <= 0 || k <= 0 || check_plan(n_layers, plan, &group)) return 0;
+  size_t a, c, d;
+  return fused_parts(nq, max_len, k, group, &a, &c, &d);
+}
+
+int32_t dsa_mla_decode_layers(const dsa_batch_t* batch, int32_t n_layers, const dsa_layer_plan_t* plan,
+                              int32_t index_dtype, const void* const* q_idx_l, const float* const* w_idx_l,
+                              const void* const* k_idx_l, int32_t k, int32_t dtype, const void* const* q_l,
+                              const void* const* kv_l, void* const* out_l, float* const* lse_l, int32_t out_dtype,
+                              float scale, int32_t* const* idx_l, void* ws, size_t ws_bytes, void* stream) {
+  dsa::BatchDev b;
+  int st = check_batch(batch, &b);
+  if (st) return st;
+  int max_group = 0;
+  if ((st = check_plan(n_layers, plan, &max_group))) return st;
+  if ((st = check_index_dtype(index_dtype, "index_dtype"))) return st;
+  if ((st = check_dtype(dtype, "dtype"))) return st;
+  if ((st = check_dtype(out_dtype, "out_dtype"))) return st;
+  if ((st = check_k(k))) return st;
+  if (b.nq == 0) return DSA_OK;
+  if (!q_idx_l || !w_idx_l || !k_idx_l || !q_l || !kv_l || !out_l)
+    return fail(DSA_ERR_NULL, "a per-layer pointer table is NULL");
+  for (int l = 0; l < n_layers; ++l) {
+    if (plan[l].runs_indexer) {
+      const void* q_idx = q_idx_l[l];
+      const void* w_idx = w_idx_l[l];
+      const void* k_idx = k_idx_l[l];
+      REQUIRE_PTR(q_idx);
+      REQUIRE_PTR(w_idx);
+      REQUIRE_PTR(k_idx);
+      if (idx_l && idx_l[l] && !aligned16(idx_l[l])) return fail(DSA_ERR_ALIGN, "idx_l[%d] is not 16-byte aligned", l);
+    }
+    if ((st = check_mla_layer(q_l[l], kv_l[plan[l].kv_source], out_l[l]))) return st;
+  }
+  size_t off_idx, off_topk, off_mla;
+  const size_t need = fused_parts(b.nq, b.max_len, k, max_group, &off_idx, &off_topk, &off_mla);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "layers workspace: %zu bytes given, %zu needed", ws_bytes, need);
+  if (!aligned16(ws)) return fail(DSA_ERR_ALIGN, "ws is not 16-byte aligned");
+  char* base = (char*)ws;
+  hipStream_t s = as_stream(stream);
+  int32_t* idx = nullptr;
+  for (int l = 0; l < n_layers;) {
+    if (plan[l].runs_indexer) {
+      idx = (idx_l && idx_l[l]) ? idx_l[l] : (int32_t*)(base + off_idx);
+      if ((st = run_selection(b, index_dtype, q_idx_l[l], w_idx_l[l], k_idx_l[l], k, idx, base, off_topk, off_mla,
+                              s)))
+        return st;
+    }
+    // this layer and the following ones that reuse the same selection with
+    // the same rotary width: one MLA launch
+    int n = 1;
+    while (l + n < n_layers && n < DSA_MAX_LAYERS && !plan[l + n].runs_indexer &&
+           plan[l + n].rope_dim == plan[l].rope_dim)
+      ++n;
+    dsa::MlaLayers L;
+    memset(&L, 0, sizeof(L));
+    for (int j = 0; j < n; ++j) {
+      L.q[j] = q_l[l + j];
+      L.kv[j] = kv_l[plan[l + j].kv_source];
+      L.out[j] = out_l[l + j];
+      L.lse[j] = lse_l ? lse_l[l + j] : nullptr;
+    }
+    if ((st = hip_status(dsa::launch_mla(b, dtype, plan[l].rope_dim, L, n, idx, k, scale, out_dtype,
+                                         base + off_mla, need - off_mla, s),
+                         "layers: MLA launch")))
+      return st;
+    l += n;
+  }
+  return DSA_OK;
 }
 
 }  // extern "C"

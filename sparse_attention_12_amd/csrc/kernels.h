@@ -47,7 +47,8 @@ struct MlaLayers {
 };
 int mla_num_splits(int dtype, int nq, int k, int n_layers);
 size_t mla_workspace_bytes(int dtype, int nq, int k, int n_layers);
-hipError_t launch_mla(const BatchDev& b, int dtype, const MlaLayers& layers, int n_layers,
+// rope: rotary width of every layer's rows (DR, or 0 without rotary encoding).
+hipError_t launch_mla(const BatchDev& b, int dtype, int rope, const MlaLayers& layers, int n_layers,
                       const int32_t* idx, int k, float scale, int out_dtype, void* ws,
                       size_t ws_bytes, hipStream_t st);
 

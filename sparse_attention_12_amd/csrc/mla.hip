@@ -1,10 +1,12 @@
 // Sparse MLA read on gfx950 (concept page "Mistral Large 4", sections "What
 // to keep", "Where to look" and "Sparse attention").  For query q with
 // selected positions S (its row of idx), in absorbed form:
-//   l[h][j] = scale * q[h][0:576] . kv[S_j][0:576]
+//   l[h][j] = scale * q[h][0:W] . kv[S_j][0:W]
 //   o[h]    = sum_j softmax_j(l[h])[j] * kv[S_j][0:512]     (softmax over S only)
 //   lse[h]  = log sum_j exp(l[h][j])
-// 64 x (512 + 64 + 512) multiply-adds per selected position.
+// with row width W = 512 + R: R = 64 rotary values, or R = 0 in the layers
+// without rotary encoding (every fourth layer, list of changes on the same
+// page).  64 x (512 + R + 512) multiply-adds per selected position.
 //
 // bf16 kernel: one workgroup (4 waves) per (split of the selection, query,
 // layer); wave w owns heads 16w..16w+15.  Per tile of 32 positions the
@@ -69,20 +71,30 @@ __device__ inline void store_out4(const MlaParams& p, int layer, int64_t off, f3
 // flight while one is consumed.
 constexpr int MLA_THREADS = 512;
 constexpr int MLA_TILE = 32;                    // positions per tile
-constexpr int MLA_ROWB = D * 2;                 // 1,152 bytes per bf16 row
-constexpr int MLA_TILEB = MLA_TILE * MLA_ROWB;  // 36,864 bytes per tile
 constexpr int MLA_SPLIT_MAX = KMAX;
-constexpr int MLA_KSTEPS = D / 32 / 2;          // contraction steps per wave (9)
 constexpr int MLA_VBLK = DC / 16 / 2;           // 16-column value blocks per wave (16)
 constexpr float MLA_RESCALE_SLACK = 8.0f;       // log2 units
+
+// Row geometry for rotary width ROPE (64, or 0 without rotary encoding).
+template <int ROPE>
+struct MlaGeo {
+  static constexpr int W = DC + ROPE;                  // 576 or 512 values per row
+  static constexpr int ROWB = W * 2;                   // 1,152 or 1,024 bytes per bf16 row
+  static constexpr int TILEB = MLA_TILE * ROWB;        // 36,864 or 32,768 bytes per tile
+  static constexpr int KSTEPS = W / 32 / 2;            // contraction steps per wave (9 or 8)
+  static constexpr int BLOCKS = (ROWB / 128) * (MLA_TILE / 8);  // 1 KB gather blocks per tile (36 or 32)
+  static constexpr int WAVE_DMAS = (BLOCKS + MLA_THREADS / 64 - 1) / (MLA_THREADS / 64);  // 5 or 4
+  static_assert(WAVE_DMAS * (MLA_THREADS / 64) >= BLOCKS, "every block must be gathered");
+  static_assert(WAVE_DMAS <= 7, "wait counts below assume fewer than 16 gathers in flight");
+};
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-// LDS tile layout (36,864 bytes): nine column groups of 64 latent/rotary
-// values; group G holds rows 0..31 at 128 bytes each, and row r's logical
-// 16-byte chunk c (of the group's eight) sits at chunk slot c ^ (r & 7).
+// LDS tile layout: W/64 column groups of 64 latent/rotary values (nine for
+// 576-wide rows); group G holds rows 0..31 at 128 bytes each, and row r's
+// logical 16-byte chunk c (of the group's eight) sits at chunk slot c ^ (r & 7).
 // One gather instruction of a wave fills rows 8w'..8w'+7 of one group: 1 KB,
 // written in lane order.
 constexpr int MLA_GROUPB = MLA_TILE * 128;  // 4,096 bytes per column group
@@ -97,22 +109,23 @@ struct MlaTileState {
   float l_part;
 };
 
-// Gather tile t into LDS.  A tile is 36 blocks of 1 KB (column group i,
-// row octet o); every wave issues exactly MLA_WAVE_DMAS gather instructions
-// per tile -- blocks 5w .. 5w+4, where ids past the last block re-load block
-// 35's rows into a scratch slot -- so all waves keep the same number of
-// gathers in flight.  Within a block, lane l fetches row 8o + l/8, 16-byte
-// chunk ((l % 8) ^ (row & 7)) + 8i, landing at lane slot l.
-constexpr int MLA_BLOCKS = (D * 2 / 128) * (MLA_TILE / 8);  // 36
-constexpr int MLA_WAVE_DMAS = 5;
-static_assert(MLA_WAVE_DMAS * (MLA_THREADS / 64) >= MLA_BLOCKS, "every block must be gathered");
+// Gather tile t into LDS.  A tile is BLOCKS blocks of 1 KB (column group
+// i, row octet o); every wave issues exactly WAVE_DMAS gather instructions
+// per tile -- blocks WAVE_DMAS*w .. WAVE_DMAS*w + WAVE_DMAS-1, where ids past
+// the last block re-load the last block's rows into a scratch slot -- so all
+// waves keep the same number of gathers in flight.  Within a block, lane l
+// fetches row 8o + l/8, 16-byte chunk ((l % 8) ^ (row & 7)) + 8i, landing
+// at lane slot l.
 
 // Selected positions of the rows this lane gathers for tile t (read ahead of
 // the gathers, so no gather waits on an LDS read).
-__device__ __forceinline__ void mla_rows(int (&pos)[MLA_WAVE_DMAS], const int* sel_l, int t, int lane, int wave_u) {
+template <int ROPE>
+__device__ __forceinline__ void mla_rows(int (&pos)[MlaGeo<ROPE>::WAVE_DMAS], const int* sel_l, int t, int lane,
+                                         int wave_u) {
+  using G = MlaGeo<ROPE>;
 #pragma unroll
-  for (int jj = 0; jj < MLA_WAVE_DMAS; ++jj) {
-    const int blk = min(wave_u * MLA_WAVE_DMAS + jj, MLA_BLOCKS - 1);
+  for (int jj = 0; jj < G::WAVE_DMAS; ++jj) {
+    const int blk = min(wave_u * G::WAVE_DMAS + jj, G::BLOCKS - 1);
     pos[jj] = sel_l[t * MLA_TILE + (blk & 3) * 8 + (lane >> 3)];
   }
 }
@@ -120,25 +133,29 @@ __device__ __forceinline__ void mla_rows(int (&pos)[MLA_WAVE_DMAS], const int* s
 // The gathers are buffer loads with an LDS destination (MUBUF, not FLAT, so
 // the compiler keeps precise LDS wait counts around them) addressed from the
 // sequence's first row; sequences up to 2^32 bytes of rows are supported.
+template <int ROPE>
 __device__ __forceinline__ void mla_issue(uint8_t* buf, uint8_t* dummy, __amdgpu_buffer_rsrc_t kv,
-                                          const int (&pos)[MLA_WAVE_DMAS], int lane, int wave_u) {
+                                          const int (&pos)[MlaGeo<ROPE>::WAVE_DMAS], int lane, int wave_u) {
+  using G = MlaGeo<ROPE>;
 #pragma unroll
-  for (int jj = 0; jj < MLA_WAVE_DMAS; ++jj) {
-    const int id = wave_u * MLA_WAVE_DMAS + jj;
-    const int blk = min(id, MLA_BLOCKS - 1);
+  for (int jj = 0; jj < G::WAVE_DMAS; ++jj) {
+    const int id = wave_u * G::WAVE_DMAS + jj;
+    const int blk = min(id, G::BLOCKS - 1);
     const int gi = blk >> 2;
     const int oc = blk & 3;
     const int row = oc * 8 + (lane >> 3);
-    const uint32_t off = (uint32_t)max(pos[jj], 0) * (uint32_t)MLA_ROWB + (uint32_t)(gi * 8 + ((lane & 7) ^ (row & 7))) * 16u;
-    uint8_t* dst = id < MLA_BLOCKS ? buf + gi * MLA_GROUPB + oc * 1024 : dummy;
+    const uint32_t off = (uint32_t)max(pos[jj], 0) * (uint32_t)G::ROWB + (uint32_t)(gi * 8 + ((lane & 7) ^ (row & 7))) * 16u;
+    uint8_t* dst = id < G::BLOCKS ? buf + gi * MLA_GROUPB + oc * 1024 : dummy;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(kv, (lds_void*)dst, 16, off, 0, 0, 0);
   }
 }
 
 // Partial S^T (32 positions x 16 heads) over this wave's half of the
 // contraction; lane (n16, g) gets positions 16*mb + 4g + i of head n16.
-__device__ __forceinline__ void mla_partial_logits(const uint8_t* tile, const bf16x8 (&qf)[MLA_KSTEPS], int d, int n16,
-                                          int g, f32x4 (&s)[2]) {
+template <int ROPE>
+__device__ __forceinline__ void mla_partial_logits(const uint8_t* tile, const bf16x8 (&qf)[MlaGeo<ROPE>::KSTEPS], int d,
+                                                   int n16, int g, f32x4 (&s)[2]) {
+  constexpr int MLA_KSTEPS = MlaGeo<ROPE>::KSTEPS;
   // Row r's logical chunk 4t+g lies in column group t/2 at in-group chunk
   // 4*(t%2) + g.  Loads run two steps ahead; each block keeps two chains.
   const uint8_t* ev[2];
@@ -279,12 +296,16 @@ __device__ __forceinline__ void barrier_no_fence() {
   asm volatile("" ::: "memory");
 }
 
+template <int ROPE>
 __global__ __launch_bounds__(MLA_THREADS, 1) void mla_bf16_kernel(MlaParams p) {
+  using G = MlaGeo<ROPE>;
+  constexpr int MLA_KSTEPS = G::KSTEPS;
+  constexpr int MLA_WAVE_DMAS = G::WAVE_DMAS;
   // three distinct arrays, so that reads of one tile are known not to alias
   // the asynchronous gathers into the others
-  __shared__ __attribute__((aligned(16))) uint8_t tile0[MLA_TILEB];
-  __shared__ __attribute__((aligned(16))) uint8_t tile1[MLA_TILEB];
-  __shared__ __attribute__((aligned(16))) uint8_t tile2[MLA_TILEB];
+  __shared__ __attribute__((aligned(16))) uint8_t tile0[G::TILEB];
+  __shared__ __attribute__((aligned(16))) uint8_t tile1[G::TILEB];
+  __shared__ __attribute__((aligned(16))) uint8_t tile2[G::TILEB];
   __shared__ __attribute__((aligned(16))) uint8_t scratch_blk[1024];  // target of the filler gathers
   __shared__ int sel_l[MLA_SPLIT_MAX];
   __shared__ __attribute__((aligned(16))) f32x4 xpart[8][64][2];  // partial logits per wave
@@ -315,17 +336,17 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_bf16_kernel(MlaParams p) {
     }
   }
   // Q^T (this wave's heads and half of the contraction) as the B operand:
-  // head `head`, contraction slots (9d + tt)*32 + 8g + [0,8)
+  // head `head`, contraction slots (KSTEPS*d + tt)*32 + 8g + [0,8)
   bf16x8 qf[MLA_KSTEPS];
   {
-    const uint16_t* qp = (const uint16_t*)p.L.q[layer] + ((int64_t)q * H + head) * D + d * (D / 2) + g * 8;
+    const uint16_t* qp = (const uint16_t*)p.L.q[layer] + ((int64_t)q * H + head) * G::W + d * (G::W / 2) + g * 8;
 #pragma unroll
     for (int tt = 0; tt < MLA_KSTEPS; ++tt) qf[tt] = as_bf16x8(load16(qp + tt * 32));
   }
   // buffer resource over exactly this sequence's rows (raw addressing): a
   // gather outside them reads zeros and touches no memory
   const __amdgpu_buffer_rsrc_t kv = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const uint16_t*)p.L.kv[layer] + r.row0 * D), (short)0, (int)((uint32_t)r.n * (uint32_t)MLA_ROWB),
+      (void*)((const uint16_t*)p.L.kv[layer] + r.row0 * G::W), (short)0, (int)((uint32_t)r.n * (uint32_t)G::ROWB),
       0x00020000);
   MlaTileState st;
 #pragma unroll
@@ -339,14 +360,14 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_bf16_kernel(MlaParams p) {
   // of position -1, which the buffer range check turns into zeros without
   // a memory access), so the wait below is the same on every path.
   int rows[MLA_WAVE_DMAS];
-  mla_rows(rows, sel_l, 0, lane, wave_u);
-  mla_issue(tile0, scratch_blk, kv, rows, lane, wave_u);
-  mla_rows(rows, sel_l, 1, lane, wave_u);
-  mla_issue(tile1, scratch_blk, kv, rows, lane, wave_u);
-  mla_rows(rows, sel_l, min(2, max(ntiles, 1) - 1), lane, wave_u);
+  mla_rows<ROPE>(rows, sel_l, 0, lane, wave_u);
+  mla_issue<ROPE>(tile0, scratch_blk, kv, rows, lane, wave_u);
+  mla_rows<ROPE>(rows, sel_l, 1, lane, wave_u);
+  mla_issue<ROPE>(tile1, scratch_blk, kv, rows, lane, wave_u);
+  mla_rows<ROPE>(rows, sel_l, min(2, max(ntiles, 1) - 1), lane, wave_u);
   // Q (loaded before the gathers) must be in registers before the loop:
   // wait for it alone, leaving both tiles' gathers in flight
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * MLA_WAVE_DMAS));  // vmcnt(10)
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * MLA_WAVE_DMAS));  // vmcnt(2 * WAVE_DMAS)
   // From here on Q counts as computed, not loaded: otherwise the compiler
   // drains every gather before the loop because the loop reads registers
   // loaded outside it.
@@ -358,20 +379,20 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_bf16_kernel(MlaParams p) {
     // it+1 stay in flight); after the barrier the tile is complete and tile
     // it-1's buffer is free for tile it+2.
     if (it + 1 < ntiles)
-      __builtin_amdgcn_s_waitcnt(0x0075);  // vmcnt(5) lgkmcnt(0)
+      __builtin_amdgcn_s_waitcnt(0x0070 | MLA_WAVE_DMAS);  // vmcnt(WAVE_DMAS) lgkmcnt(0)
     else
       __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
     barrier_no_fence();
-    if (it + 2 < ntiles) mla_issue(nxt2, scratch_blk, kv, rows, lane, wave_u);
+    if (it + 2 < ntiles) mla_issue<ROPE>(nxt2, scratch_blk, kv, rows, lane, wave_u);
     // unconditional (a clamped, harmless re-read at the end), so that the
     // wait counts below need not merge two control paths
-    mla_rows(rows, sel_l, min(it + 3, ntiles - 1), lane, wave_u);
+    mla_rows<ROPE>(rows, sel_l, min(it + 3, ntiles - 1), lane, wave_u);
     // validity of the tile's 32 positions, read now and folded into a mask
     // after the logits (the read's latency hides behind them)
     const int vpos = sel_l[it * MLA_TILE + (lane & 31)];
     f32x4 s[2];
     __builtin_amdgcn_sched_barrier(0);
-    mla_partial_logits(cur, qf, d, n16, g, s);
+    mla_partial_logits<ROPE>(cur, qf, d, n16, g, s);
     __builtin_amdgcn_sched_barrier(0);
     xpart[wave_u][lane][0] = s[0];
     xpart[wave_u][lane][1] = s[1];
@@ -418,7 +439,9 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_bf16_kernel(MlaParams p) {
 constexpr int MLA32_THREADS = 256;
 constexpr int MLA32_TILE = 8;
 
+template <int ROPE>
 __global__ __launch_bounds__(MLA32_THREADS) void mla_f32_kernel(MlaParams p) {
+  constexpr int D = DC + ROPE;  // row width
   __shared__ __attribute__((aligned(16))) float tile[MLA32_TILE][D];
   __shared__ int vflag[MLA32_TILE];
   const int split = blockIdx.x;
@@ -432,7 +455,7 @@ __global__ __launch_bounds__(MLA32_THREADS) void mla_f32_kernel(MlaParams p) {
   const int j_end = min(j_begin + p.split_len, p.k);
   const float* kv = (const float*)p.L.kv[layer] + r.row0 * D;
   const int32_t* sel = p.idx + (int64_t)q * p.k;
-  constexpr int QS = D / 4;   // 144 contraction dims per thread
+  constexpr int QS = D / 4;   // 144 (or 128) contraction dims per thread
   constexpr int VS = DC / 4;  // 128 value dims per thread
   float qr[QS];
   {
@@ -575,7 +598,7 @@ size_t mla_workspace_bytes(int dtype, int nq, int k, int n_layers) {
   return slots * DC * sizeof(float) + slots * 2 * sizeof(float);
 }
 
-hipError_t launch_mla(const BatchDev& b, int dtype, const MlaLayers& layers, int n_layers,
+hipError_t launch_mla(const BatchDev& b, int dtype, int rope, const MlaLayers& layers, int n_layers,
                       const int32_t* idx, int k, float scale, int out_dtype, void* ws,
                       size_t ws_bytes, hipStream_t st) {
   if (b.nq == 0 || n_layers == 0) return hipSuccess;
@@ -599,10 +622,17 @@ hipError_t launch_mla(const BatchDev& b, int dtype, const MlaLayers& layers, int
     p.part_ml = (float*)ws + slots * DC;
   }
   dim3 grid(p.nsplit, b.nq, n_layers);
-  if (dtype == 0)
-    hipLaunchKernelGGL(mla_f32_kernel, grid, dim3(MLA32_THREADS), 0, st, p);
-  else
-    hipLaunchKernelGGL(mla_bf16_kernel, grid, dim3(MLA_THREADS), 0, st, p);
+  if (dtype == 0) {
+    if (rope)
+      hipLaunchKernelGGL(mla_f32_kernel<DR>, grid, dim3(MLA32_THREADS), 0, st, p);
+    else
+      hipLaunchKernelGGL(mla_f32_kernel<0>, grid, dim3(MLA32_THREADS), 0, st, p);
+  } else {
+    if (rope)
+      hipLaunchKernelGGL(mla_bf16_kernel<DR>, grid, dim3(MLA_THREADS), 0, st, p);
+    else
+      hipLaunchKernelGGL(mla_bf16_kernel<0>, grid, dim3(MLA_THREADS), 0, st, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
   hipLaunchKernelGGL(mla_combine, dim3(b.nq, n_layers, H / CMB_HEADS), dim3(CMB_THREADS), 0, st, p);

@@ -218,8 +218,9 @@ def _layout(lens: np.ndarray):
 def make_decode(lens, dtype: str = "bf16", n_layers: int = 1, seed: int = 0,
                 name: Optional[str] = None, split_kv: bool = False,
                 rng: Optional[np.random.Generator] = None,
-                index_dtype: Optional[str] = None) -> Workload:
-    """Decode batch: one query per sequence, at its last position."""
+                index_dtype: Optional[str] = None, rope_dim: int = DR) -> Workload:
+    """Decode batch: one query per sequence, at its last position.  With
+    rope_dim=0 the layers have no rotary part: q [nq,64,512], kv [rows,512]."""
     rng = rng if rng is not None else np.random.default_rng(seed)
     idt = index_dtype or dtype
     lens = np.asarray(lens, np.int32)
@@ -228,16 +229,17 @@ def make_decode(lens, dtype: str = "bf16", n_layers: int = 1, seed: int = 0,
     qI = _small_int_bits(rng.integers(-3, 4, size=(nq, HI, DI), dtype=np.int8), idt)
     w = rng.integers(1, 5, size=(nq, HI), dtype=np.int8).astype(np.float32)
     kI = _small_int_bits(rng.integers(-3, 4, size=(rows, DI), dtype=np.int8), idt)
+    width = DC + rope_dim
     qs, kvs = [], []
     for _ in range(n_layers):
-        qs.append(_normal(rng, (nq, H, D), dtype))
+        qs.append(_normal(rng, (nq, H, width), dtype))
     for _ in range(n_layers):
-        if split_kv:
+        if split_kv and rope_dim:
             lat = _normal(rng, (rows, DC), dtype)
-            rot = _normal(rng, (rows, DR), dtype)
+            rot = _normal(rng, (rows, rope_dim), dtype)
             kvs.append(np.ascontiguousarray(np.concatenate([lat, rot], axis=1)))
         else:
-            kvs.append(_normal(rng, (rows, D), dtype))
+            kvs.append(_normal(rng, (rows, width), dtype))
     return Workload(
         name=name or f"decode_b{nq}_{dtype}", kind="decode", dtype=dtype, n_layers=n_layers,
         seq_len=lens, seq_row0=row0, q_seq=np.arange(nq, dtype=np.int32),
@@ -263,6 +265,60 @@ def make_prefill(cache_len: int, first_pos: int, nq: int, dtype: str = "bf16",
         seq_len=lens, seq_row0=row0, q_seq=np.zeros(nq, np.int32),
         q_pos=(first_pos + np.arange(nq)).astype(np.int32), qI=qI, w=w, kI=kI,
         q=[q], kv=[kv], seed=seed, index_dtype=idt)
+
+
+@dataclasses.dataclass
+class LayerStack:
+    """Inputs of a decode step over a stack of layers under a schedule
+    (plan: list of (runs_indexer, rope, kv_source)).  Arrays a layer does not
+    own are None: indexer inputs of reusing layers, caches of layers that
+    read another layer's cache."""
+    base: Workload            # batch layout (lengths, rows, positions); its own arrays unused
+    plan: list
+    qI: List[Optional[np.ndarray]]
+    w: List[Optional[np.ndarray]]
+    kI: List[Optional[np.ndarray]]
+    q: List[np.ndarray]
+    kv: List[Optional[np.ndarray]]
+
+    def to_torch(self, device):
+        import torch
+
+        def t(a):
+            if a is None:
+                return None
+            x = torch.from_numpy(np.ascontiguousarray(a))
+            if a.dtype == np.uint16:
+                x = x.view(torch.bfloat16)
+            return x.to(device)
+
+        return dict(qI=[t(a) for a in self.qI], w=[t(a) for a in self.w], kI=[t(a) for a in self.kI],
+                    q=[t(a) for a in self.q], kv=[t(a) for a in self.kv])
+
+
+def make_layer_stack(lens, plan, dtype: str = "bf16", seed: int = 0,
+                     index_dtype: Optional[str] = None) -> LayerStack:
+    """Decode batch over the layers of `plan`: per layer, in layer order,
+    the indexer inputs (qI, w, kI) if it runs its indexer, its query (512 +
+    64 wide, or 512 without rotary part), its cache if it owns one."""
+    rng = np.random.default_rng(seed)
+    idt = index_dtype or dtype
+    base = make_decode(lens, dtype, 0, seed, "layer_stack", rng=np.random.default_rng(seed + 1), index_dtype=idt)
+    nq, rows = base.nq, base.rows
+    qI, w, kI, q, kv = [], [], [], [], []
+    for l, (runs, rope, src) in enumerate(plan):
+        width = DC + (DR if rope else 0)
+        if runs:
+            qI.append(_small_int_bits(rng.integers(-3, 4, size=(nq, HI, DI), dtype=np.int8), idt))
+            w.append(rng.integers(1, 5, size=(nq, HI), dtype=np.int8).astype(np.float32))
+            kI.append(_small_int_bits(rng.integers(-3, 4, size=(rows, DI), dtype=np.int8), idt))
+        else:
+            qI.append(None)
+            w.append(None)
+            kI.append(None)
+        q.append(_normal(rng, (nq, H, width), dtype))
+        kv.append(_normal(rng, (rows, width), dtype) if src == l else None)
+    return LayerStack(base=base, plan=list(plan), qI=qI, w=w, kI=kI, q=q, kv=kv)
 
 
 def ragged_lengths(rng: np.random.Generator, b: int, lo: int, hi: int, forced=(1024, 2048, 2049)):

@@ -30,13 +30,18 @@ def lib():
     l.dsa_topk.argtypes = [vp, vp, i64, i32, vp, vp, vp, sz, vp]
     l.dsa_topk_workspace_size.argtypes = [i32, i32, i32]
     l.dsa_topk_workspace_size.restype = sz
-    l.mla_sparse_attend.argtypes = [vp, i32, vp, vp, vp, i32, ctypes.c_float, vp, i32, vp, vp, sz, vp]
+    l.mla_sparse_attend.argtypes = [vp, i32, i32, vp, vp, vp, i32, ctypes.c_float, vp, i32, vp, vp, sz, vp]
     l.mla_sparse_attend_workspace_size.argtypes = [i32, i32, i32]
     l.mla_sparse_attend_workspace_size.restype = sz
-    l.dsa_mla_decode_fused.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, i32,
+    l.dsa_mla_decode_fused.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, i32,
                                        ctypes.c_float, vp, vp, sz, vp]
     l.dsa_mla_decode_fused_workspace_size.argtypes = [i32, i32, i32, i32]
     l.dsa_mla_decode_fused_workspace_size.restype = sz
+    l.dsa_ml4_layer_plan.argtypes = [i32, vp]
+    l.dsa_mla_decode_layers_workspace_size.argtypes = [i32, i32, i32, i32, vp]
+    l.dsa_mla_decode_layers_workspace_size.restype = sz
+    l.dsa_mla_decode_layers.argtypes = [vp, i32, vp, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, i32,
+                                        ctypes.c_float, vp, vp, sz, vp]
     l.dsa_status_string.restype = ctypes.c_char_p
     l.dsa_last_error.restype = ctypes.c_char_p
     return l
@@ -59,13 +64,13 @@ def _batch(nq=2, nseq=2, max_len=100):
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 10, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert lib.dsa_abi_version() == 2
+    assert lib.dsa_abi_version() == 3
     for st in (OK, NULL, SHAPE, DTYPE, ALIGN, WORKSPACE, UNSUPPORTED, -7):
         assert lib.dsa_status_string(st)
     assert b"unknown" in lib.dsa_status_string(42)
@@ -108,16 +113,18 @@ def test_mla_validation(lib):
     b = _batch()
     args = lambda **kw: dict(dict(dt=1, q=A, kv=A, idx=A, k=2048, out=A, odt=0, ws=A, wsb=1 << 40), **kw)
 
-    def call(**kw):
+    def call(rope=64, **kw):
         a = args(**kw)
-        return lib.mla_sparse_attend(ctypes.byref(b), a["dt"], a["q"], a["kv"], a["idx"], a["k"], 0.07,
+        return lib.mla_sparse_attend(ctypes.byref(b), a["dt"], rope, a["q"], a["kv"], a["idx"], a["k"], 0.07,
                                      a["out"], a["odt"], None, a["ws"], a["wsb"], None)
 
     assert call(dt=2) == DTYPE
+    assert call(rope=32) == SHAPE
+    assert call(rope=0, q=None) == NULL   # rotary width 0 is accepted
     assert call(odt=-1) == DTYPE
     long_b = _batch()
     long_b.max_len = 3728271   # rows past 2^32 bytes of a sequence are not addressable
-    assert lib.mla_sparse_attend(ctypes.byref(long_b), 1, A, A, A, 2048, 0.07, A, 0, None, A, 1 << 40,
+    assert lib.mla_sparse_attend(ctypes.byref(long_b), 1, 64, A, A, A, 2048, 0.07, A, 0, None, A, 1 << 40,
                                  None) == UNSUPPORTED
     assert call(k=0) == SHAPE
     assert call(k=4096) == UNSUPPORTED
@@ -139,10 +146,12 @@ def test_fused_validation(lib):
     need = lib.dsa_mla_decode_fused_workspace_size(2, 100, 2048, 2)
     assert need >= 2 * 100 * 4 + 2 * 2048 * 4
 
-    def call(n_layers=2, q=tab, kv=tab, out=tab, k=2048, ws=A, wsb=need, idt=1, dt=1, odt=0):
+    def call(n_layers=2, q=tab, kv=tab, out=tab, k=2048, ws=A, wsb=need, idt=1, dt=1, odt=0, rope=64):
         c = lambda t: ctypes.cast(t, ctypes.c_void_p) if t is not None else None
-        return lib.dsa_mla_decode_fused(ctypes.byref(b), idt, A, A, A, k, n_layers, dt, c(q), c(kv), c(out),
-                                        None, odt, 0.07, None, ws, wsb, None)
+        return lib.dsa_mla_decode_fused(ctypes.byref(b), idt, A, A, A, k, n_layers, dt, rope, c(q), c(kv),
+                                        c(out), None, odt, 0.07, None, ws, wsb, None)
+
+    assert call(rope=1) == SHAPE
 
     assert call(idt=5) == DTYPE
     assert call(dt=2) == DTYPE          # FP8 is for the indexer's inputs only
@@ -157,3 +166,66 @@ def test_fused_validation(lib):
     assert call(ws=None) == WORKSPACE
     assert call(wsb=need - 1) == WORKSPACE
     assert call(ws=MIS) == ALIGN
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("runs_indexer", ctypes.c_int32), ("rope_dim", ctypes.c_int32), ("kv_source", ctypes.c_int32)]
+
+
+def _plan(lib, n):
+    arr = (Plan * n)()
+    assert lib.dsa_ml4_layer_plan(n, ctypes.byref(arr)) == OK
+    return arr
+
+
+def test_layer_plan_matches_the_oracle_schedule(lib):
+    """The library's schedule (host code) equals the oracle's, layer by layer,
+    which the oracle's pins tie to the counts the concept page prints."""
+    import oracle
+    arr = _plan(lib, 72)
+    got = [(bool(p.runs_indexer), p.rope_dim == 64, p.kv_source) for p in arr]
+    assert got == oracle.layer_plan(72)
+    assert all(p.rope_dim in (0, 64) for p in arr)
+    # a prefix of the model takes the first layers' entries
+    assert [(p.runs_indexer, p.rope_dim, p.kv_source) for p in _plan(lib, 40)] == \
+        [(p.runs_indexer, p.rope_dim, p.kv_source) for p in arr[:40]]
+    assert lib.dsa_ml4_layer_plan(0, ctypes.byref(arr)) == SHAPE
+    assert lib.dsa_ml4_layer_plan(73, ctypes.byref(arr)) == SHAPE
+    assert lib.dsa_ml4_layer_plan(4, None) == NULL
+
+
+def test_decode_layers_validation(lib):
+    b = _batch()
+    n = 72
+    plan = _plan(lib, n)
+    need = lib.dsa_mla_decode_layers_workspace_size(2, 100, 2048, n, ctypes.byref(plan))
+    # runs of three layers share a selection: the MLA part is sized for three
+    assert need == lib.dsa_mla_decode_fused_workspace_size(2, 100, 2048, 3)
+    tab = (ctypes.c_void_p * n)(*([A] * n))
+
+    def call(pl=plan, nl=n, ws=A, wsb=need, t=tab, idt=1):
+        c = lambda x: ctypes.cast(x, ctypes.c_void_p) if x is not None else None
+        pp = ctypes.byref(pl) if pl is not None else None
+        return lib.dsa_mla_decode_layers(ctypes.byref(b), nl, pp, idt, c(t), c(t), c(t), 2048, 1, c(t), c(t),
+                                         c(t), None, 0, 0.07, None, ws, wsb, None)
+
+    assert call(pl=None) == NULL
+    assert call(nl=0) == SHAPE
+    assert call(idt=9) == DTYPE
+    assert call(t=None) == NULL
+    assert call(ws=None) == WORKSPACE
+    assert call(wsb=need - 1) == WORKSPACE
+    # invalid plans: each is rejected on the host, and the size query says 0
+    bad = [
+        lambda p: setattr(p[0], "runs_indexer", 0),        # nothing to reuse at layer 0
+        lambda p: setattr(p[5], "rope_dim", 32),           # neither 0 nor 64
+        lambda p: setattr(p[10], "kv_source", 11),         # a later layer
+        lambda p: setattr(p[39], "kv_source", 38),         # another rotary width
+        lambda p: setattr(p[43], "kv_source", 39),         # 39 reads 35, it owns no cache
+    ]
+    for mutate in bad:
+        pl = _plan(lib, n)
+        mutate(pl)
+        assert call(pl=pl) == SHAPE
+        assert lib.dsa_mla_decode_layers_workspace_size(2, 100, 2048, n, ctypes.byref(pl)) == 0
+

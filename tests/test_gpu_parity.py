@@ -309,8 +309,8 @@ def test_topk_nonint_scores_property(B):
 # ----------------------------------------------------------------------------
 
 
-def _mla_case(B, dtype, lens, k, nq_pad=0, out_dtype=torch.float32, seed=26):
-    w = wl.make_decode(lens, dtype, 1, seed=seed)
+def _mla_case(B, dtype, lens, k, nq_pad=0, out_dtype=torch.float32, seed=26, rope=64):
+    w = wl.make_decode(lens, dtype, 1, seed=seed, rope_dim=rope)
     t = w.to_torch(DEV)
     rng = np.random.default_rng(seed + 1)
     idx = np.full((w.nq, k), -1, np.int32)
@@ -342,16 +342,19 @@ def _mla_case(B, dtype, lens, k, nq_pad=0, out_dtype=torch.float32, seed=26):
         assert np.abs(l[qi] - r_l).max() <= LSE_TOL[dtype], f"query {qi} lse"
 
 
+@pytest.mark.parametrize("rope", [64, 0])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_mla_split_path(B, dtype):
-    # few queries -> the selection is split across workgroups and merged
-    _mla_case(B, dtype, [5, 40, 2048, 3000, 70000], 2048, nq_pad=1)
+def test_mla_split_path(B, dtype, rope):
+    # few queries -> the selection is split across workgroups and merged;
+    # rope 0: a layer without rotary encoding (512-wide rows)
+    _mla_case(B, dtype, [5, 40, 2048, 3000, 70000], 2048, nq_pad=1, rope=rope)
 
 
-def test_mla_unsplit_path_bf16(B):
+@pytest.mark.parametrize("rope", [64, 0])
+def test_mla_unsplit_path_bf16(B, rope):
     # enough queries that each runs in one workgroup
     lens = [2100 + 37 * i for i in range(520)]
-    _mla_case(B, "bf16", lens[:520], 2048, seed=27)
+    _mla_case(B, "bf16", lens[:520], 2048, seed=27, rope=rope)
 
 
 @pytest.mark.parametrize("k", [1, 100, 2047])
@@ -368,13 +371,14 @@ def test_mla_bf16_output(B):
 # ----------------------------------------------------------------------------
 
 
-@pytest.mark.parametrize("dtype,idt,lens,layers", [
-    ("bf16", "bf16", [1024, 2048, 2049, 3333, 40000], 4),
-    ("f32", "f32", [700, 4096], 2),
-    ("bf16", "fp8", [1500, 2049, 9000], 2),
+@pytest.mark.parametrize("dtype,idt,lens,layers,rope", [
+    ("bf16", "bf16", [1024, 2048, 2049, 3333, 40000], 4, 64),
+    ("f32", "f32", [700, 4096], 2, 64),
+    ("bf16", "fp8", [1500, 2049, 9000], 2, 64),
+    ("bf16", "bf16", [1500, 2049, 9000], 3, 0),
 ])
-def test_fused_decode(B, dtype, idt, lens, layers):
-    w = wl.make_decode(lens, dtype, layers, seed=30, index_dtype=idt)
+def test_fused_decode(B, dtype, idt, lens, layers, rope):
+    w = wl.make_decode(lens, dtype, layers, seed=30, index_dtype=idt, rope_dim=rope)
     t = w.to_torch(DEV)
     outs = [torch.empty((w.nq, 64, 512), device=DEV) for _ in range(layers)]
     lses = [torch.empty((w.nq, 64), device=DEV) for _ in range(layers)]
@@ -401,6 +405,62 @@ def test_fused_decode(B, dtype, idt, lens, layers):
         for l in range(layers):
             _assert_rel(outs[l][qi].cpu().numpy(), r_o[l], TOL[dtype], f"query {qi} layer {l}")
             assert np.abs(lses[l][qi].cpu().numpy() - r_l[l]).max() <= LSE_TOL[dtype]
+
+
+def test_fused_decode_shared_cache(B):
+    """Two layers of one fused call reading the same cache (pointer
+    aliasing, as layers 39, 43, ... read layer 35's latent)."""
+    w = wl.make_decode([1800, 5000], "bf16", 3, seed=31, rope_dim=0)
+    t = w.to_torch(DEV)
+    kvs = [t["kv"][0], t["kv"][0], t["kv"][2]]
+    outs = [torch.empty((w.nq, 64, 512), device=DEV) for _ in range(3)]
+    lses = [torch.empty((w.nq, 64), device=DEV) for _ in range(3)]
+    B.dsa_mla_decode_fused(_batch(B, w, t), t["qI"], t["w"], t["kI"], w.k, t["q"], kvs, outs, w.tau, lses)
+    torch.cuda.synchronize()
+    for qi, n in enumerate([1800, 5000]):
+        caches = [w.kv[0], w.kv[0], w.kv[2]]
+        r_idx, m, r_o, r_l = oracle.decode_query(
+            w.widen(w.qI)[qi], w.w[qi], w.widen(w.seq_rows(w.kI, qi)), [w.widen(x)[qi] for x in w.q],
+            [w.widen(w.seq_rows(x, qi)) for x in caches], n, w.k, w.tau)
+        for l in range(3):
+            _assert_rel(outs[l][qi].cpu().numpy(), r_o[l], TOL["bf16"], f"query {qi} layer {l}")
+            assert np.abs(lses[l][qi].cpu().numpy() - r_l[l]).max() <= LSE_TOL["bf16"]
+
+
+@pytest.mark.parametrize("idt,n_layers", [("bf16", 72), ("fp8", 44)])
+def test_decode_layers_schedule(B, idt, n_layers):
+    """A decode step over Mistral Large 4's schedule (the library's plan):
+    indexer layers select, reusing layers carry the selection, rotary-free
+    layers read 512-wide rows, and from layer 39 those read layer 35's
+    cache.  Every layer's output against the oracle's step over the
+    oracle's own schedule."""
+    plan = B.dsa_ml4_layer_plan(n_layers)
+    oplan = oracle.layer_plan(n_layers)
+    assert [(r, rope == 64, src) for r, rope, src in plan] == oplan
+    lens = [1500, 2600]
+    st = wl.make_layer_stack(lens, oplan, "bf16", seed=40, index_dtype=idt)
+    w = st.base
+    t = w.to_torch(DEV)
+    d = st.to_torch(DEV)
+    outs = [torch.empty((w.nq, 64, 512), device=DEV) for _ in plan]
+    lses = [torch.empty((w.nq, 64), device=DEV) for _ in plan]
+    idxs = [torch.full((w.nq, w.k), -7, dtype=torch.int32, device=DEV) if p[0] else None for p in plan]
+    ws = torch.full((B.dsa_mla_decode_layers_workspace_size(w.nq, w.max_len, w.k, plan),), 0xA5,
+                    dtype=torch.uint8, device=DEV)
+    B.dsa_mla_decode_layers(_batch(B, w, t), plan, d["qI"], d["w"], d["kI"], w.k, d["q"], d["kv"], outs, w.tau,
+                            lses, idxs, ws)
+    torch.cuda.synchronize()
+    for qi, n in enumerate(lens):
+        rows = lambda a: None if a is None else w.widen(w.seq_rows(a, qi))
+        r_idx, r_o, r_l = oracle.decode_layers(
+            oplan, [None if a is None else w.widen(a)[qi] for a in st.qI],
+            [None if a is None else a[qi] for a in st.w], [rows(a) for a in st.kI],
+            [w.widen(a)[qi] for a in st.q], [rows(a) for a in st.kv], n, w.k, w.tau)
+        for l, (runs, _, _) in enumerate(oplan):
+            if runs:
+                assert np.array_equal(idxs[l][qi].cpu().numpy(), r_idx[l]), f"query {qi} layer {l}: selection"
+            _assert_rel(outs[l][qi].cpu().numpy(), r_o[l], TOL["bf16"], f"query {qi} layer {l}")
+            assert np.abs(lses[l][qi].cpu().numpy() - r_l[l]).max() <= LSE_TOL["bf16"], f"query {qi} layer {l}"
 
 
 def test_empty_batch_is_noop(B):
