@@ -11,6 +11,10 @@ follow the "Mistral Large 4" concept page, sections "What to keep", "Where to
 look" and "Sparse attention"; the readings taken where that page lost its
 display formula are stated in the C file's header.
 
+The step just upstream of the read (rotary encoding with YaRN/LeRoPE
+frequencies, per-head query scaling, cache append) is in ``oracle/rope.py``,
+plain numpy in float64, pinned in tests/test_oracle_rope.py.
+
 Pins (tests/test_oracle_pins.py) tie every function to something other than
 itself: a rank-count brute force for the selection, an ReLU sign identity
 for the indexer, a library dense-attention routine for contexts of at most

@@ -1,0 +1,93 @@
+"""Pins of the rotary / query-scaling / cache-append oracle (oracle/rope.py)
+to the concept page's "Positions" section and its example's assertions, and
+to properties of rotations that any correct implementation has."""
+import math
+
+import numpy as np
+
+from oracle import rope
+
+
+def wavelengths(freq):
+    return 2 * math.pi / np.asarray(freq)
+
+
+def test_page_wavelength_assertions():
+    """The page's example asserts pair 3 turns in under 16 positions and
+    pair 16 in over 2^20."""
+    w = wavelengths(rope.yarn_frequencies())
+    assert w[3] < 16 and w[16] > 2 ** 20
+
+
+def test_yarn_kept_divided_and_blended_pairs():
+    """Pairs completing at least 32 turns in 512 positions keep their
+    frequency; pairs completing less than one turn are divided by 2,048; in
+    between the ratio moves linearly in the pair index."""
+    base = rope.base_frequencies()
+    f = rope.yarn_frequencies()
+    turns = 512 * base / (2 * math.pi)
+    kept = turns >= 32
+    divided = turns < 1
+    assert list(np.nonzero(kept)[0]) == [0, 1, 2, 3]
+    assert list(np.nonzero(divided)[0]) == list(range(16, 32))
+    np.testing.assert_array_equal(f[kept], base[kept])
+    np.testing.assert_allclose(f[divided], base[divided] / 2048, rtol=1e-15)
+    keep = (f / base - 1 / 2048) / (1 - 1 / 2048)    # blend weight of the original frequency
+    mid = np.arange(3, 17)
+    np.testing.assert_allclose(np.diff(keep[mid]), -1 / 13, rtol=1e-12)
+    assert np.all(np.diff(f) < 0)                     # frequencies still fall with the pair index
+
+
+def test_lerope_multiplier():
+    """LeRoPE multiplies frequency i by e^{alpha_i}: the page's e^0.9336 at
+    frequency 16 divides its wavelength by that factor, and the summary
+    page's 1.8x rise makes a wavelength 44% shorter."""
+    alpha = np.zeros(32)
+    alpha[16] = 0.9336
+    w0, w1 = wavelengths(rope.rope_frequencies()), wavelengths(rope.rope_frequencies(alpha))
+    np.testing.assert_allclose(w1[16], w0[16] / math.exp(0.9336), rtol=1e-14)
+    np.testing.assert_array_equal(np.delete(w1, 16), np.delete(w0, 16))
+    alpha[16] = math.log(1.8)
+    assert round(1 - wavelengths(rope.rope_frequencies(alpha))[16] / w0[16], 2) == 0.44
+
+
+def test_rotation_properties():
+    rng = np.random.default_rng(3)
+    f = rope.rope_frequencies(rng.standard_normal(32) * 0.3)
+    x, y = rng.standard_normal(64), rng.standard_normal(64)
+    np.testing.assert_array_equal(rope.rotate(x, 0, f), x)                 # position 0: identity
+    r = rope.rotate(x, 1234, f)
+    np.testing.assert_allclose(np.hypot(r[0::2], r[1::2]), np.hypot(x[0::2], x[1::2]), rtol=1e-13)
+    np.testing.assert_allclose(rope.rotate(rope.rotate(x, 300, f), 77, f), rope.rotate(x, 377, f), atol=1e-12)
+    # relative position: <R(p)x, R(q)y> = <R(p-q)x, y>
+    for p, q in ((1000, 10), (70000, 69000), (5, 900)):
+        np.testing.assert_allclose(rope.rotate(x, p, f) @ rope.rotate(y, q, f),
+                                   rope.rotate(x, p - q, f) @ y if p >= q else x @ rope.rotate(y, q - p, f),
+                                   atol=1e-10)
+    # a single pair, against the textbook 2-D rotation
+    e = np.zeros(64)
+    e[10] = 1.0
+    a = 9 * f[5]
+    np.testing.assert_allclose(rope.rotate(e, 9, f)[10:12], [math.cos(a), math.sin(a)], atol=1e-15)
+
+
+def test_query_scaling_and_append_row():
+    rng = np.random.default_rng(4)
+    f = rope.rope_frequencies()
+    q = rng.standard_normal((64, 576))
+    s, b = rng.standard_normal(64), rng.standard_normal(64)
+    t = 4095
+    out = rope.prepare_query(q, t, f, s, b)
+    m = s * math.log(4096) + b
+    np.testing.assert_allclose(out[:, :512], q[:, :512] * m[:, None], rtol=1e-14)
+    for h in (0, 33):
+        np.testing.assert_allclose(out[h, 512:], rope.rotate(q[h, 512:] * m[h], t, f), rtol=1e-13, atol=1e-14)
+    # s = 0, b = 1: no scaling; rotary-free queries are only scaled
+    np.testing.assert_allclose(rope.prepare_query(q, t, f, np.zeros(64), np.ones(64)), rope.prepare_query(q, t, f))
+    q512 = q[:, :512]
+    np.testing.assert_allclose(rope.prepare_query(q512, t, f, s, b), q512 * m[:, None], rtol=1e-14)
+    lat, kr = rng.standard_normal(512), rng.standard_normal(64)
+    row = rope.append_row(lat, kr, t, f)
+    np.testing.assert_array_equal(row[:512], lat)
+    np.testing.assert_allclose(row[512:], rope.rotate(kr, t, f))
+    np.testing.assert_array_equal(rope.append_row(lat, None, t, f), lat)
