@@ -266,6 +266,44 @@ int32_t dsa_mla_decode_layers(const dsa_batch_t* batch, int32_t n_layers, const 
                               void* const* out_l, float* const* lse_l, int32_t out_dtype, float scale,
                               int32_t* const* idx_l, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * The step just upstream of the read (concept page, "Positions" and "Query
+ * scaling"; the YaRN wavelength function of its example).
+ *
+ * dsa_rope_frequencies: HOST.  freq[i] (radians per position, i < 32) for
+ * pair i of the 64-value rotary part: omega_i = 10000^(-2i/64); YaRN with
+ * original window 512 and factor 2,048 keeps the pairs that complete at
+ * least 32 turns within the window, divides by 2,048 those that complete
+ * less than one, and blends linearly in the pair index in between (from the
+ * rounded-down index of 32 turns to the rounded-up index of one turn);
+ * LeRoPE then multiplies frequency i by e^{alpha[i]} (alpha: HOST [32], or
+ * NULL for zeros).  Computed in double precision.
+ *
+ * dsa_rope_append: for each query q of the batch (one new token at 0-based
+ * position t = q_pos[q] of sequence q_seq[q]; t must be < seq_len, else the
+ * token is skipped), with W = 512 + rope_dim:
+ *   kv[seq_row0 + t][0:512]  = latent[q]                        (rounded to dtype)
+ *   kv[seq_row0 + t][512:W]  = rope_key[q] rotated by t          (rope_dim = 64)
+ *   q_attn[q][h][:]          = m_h(t) * q_attn[q][h][:], then its values
+ *                              [512, W) rotated by t             (in place; may be NULL)
+ * where pair i = values (2i, 2i+1) turns by the angle t * freq[i] (formed in
+ * double precision), and m_h(t) = ssmax_s[h] * ln(t + 1) + ssmax_b[h] when
+ * both per-head arrays are given, else 1 (the page's query-scaling formula
+ * was lost; this affine function of the log of the number of visible
+ * positions is the reading taken).
+ *   dtype      DSA_F32 or DSA_BF16 (kv and q_attn)
+ *   rope_dim   DSA_ROPE, or 0 (a layer without rotary encoding: only the
+ *              latent is written and the query only scaled; freq and
+ *              rope_key may be NULL)
+ *   freq       [32] double (device)      latent [nq][512] float32
+ *   rope_key   [nq][64] float32          kv [rows][W] dtype
+ *   q_attn     [nq][64][W] dtype or NULL ssmax_s, ssmax_b [64] float32, both or neither
+ */
+int32_t dsa_rope_frequencies(const float* alpha, double* freq);
+int32_t dsa_rope_append(const dsa_batch_t* batch, int32_t dtype, int32_t rope_dim, const double* freq,
+                        const float* latent, const float* rope_key, void* kv, void* q_attn,
+                        const float* ssmax_s, const float* ssmax_b, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

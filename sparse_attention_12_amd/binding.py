@@ -24,6 +24,7 @@ EXPORTS = [
     "dsa_topk_workspace_size", "dsa_topk", "mla_sparse_attend_workspace_size",
     "mla_sparse_attend", "dsa_mla_decode_fused_workspace_size", "dsa_mla_decode_fused",
     "dsa_ml4_layer_plan", "dsa_mla_decode_layers_workspace_size", "dsa_mla_decode_layers",
+    "dsa_rope_frequencies", "dsa_rope_append",
 ]
 ML4_LAYERS = 72
 
@@ -77,6 +78,10 @@ def _load() -> ctypes.CDLL:
     lib.dsa_mla_decode_layers.argtypes = [bp, i32, pp, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, i32,
                                           ctypes.c_float, vp, vp, sz, vp]
     lib.dsa_mla_decode_layers.restype = i32
+    lib.dsa_rope_frequencies.argtypes = [vp, vp]
+    lib.dsa_rope_frequencies.restype = i32
+    lib.dsa_rope_append.argtypes = [bp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.dsa_rope_append.restype = i32
     return lib
 
 
@@ -257,4 +262,26 @@ def dsa_mla_decode_layers(batch: Batch, plan, qI_l: Sequence, w_l: Sequence, kI_
                                      _dt(out_l[0]), scale, cv(ia), _p(ws), wsb, _stream(stream)),
            "dsa_mla_decode_layers")
     return out_l
+
+
+def dsa_rope_frequencies(alpha=None):
+    """Rotary frequencies (radians per position) of the 32 pairs, YaRN-blended
+    and multiplied by e^alpha (host; returns a float64 numpy array)."""
+    import numpy as np
+    out = np.zeros(ROPE // 2, np.float64)
+    a = None if alpha is None else np.ascontiguousarray(alpha, np.float32)
+    _check(lib.dsa_rope_frequencies(None if a is None else a.ctypes.data_as(ctypes.c_void_p),
+                                    out.ctypes.data_as(ctypes.c_void_p)), "dsa_rope_frequencies")
+    return out
+
+
+def dsa_rope_append(batch: Batch, freq, latent, rope_key, kv, q_attn=None, ssmax_s=None, ssmax_b=None,
+                    stream=None):
+    """Write each new token's cache row (latent, rotated rotary key) and
+    scale/rotate its attention query in place.  freq: device float64 [32]
+    (None for rotary-free layers); the rotary width comes from kv's rows."""
+    rope = int(kv.shape[-1]) - LATENT
+    _check(lib.dsa_rope_append(batch.ref, _dt(kv), rope, _p(freq), _p(latent), _p(rope_key), _p(kv), _p(q_attn),
+                               _p(ssmax_s), _p(ssmax_b), _stream(stream)), "dsa_rope_append")
+    return kv
 

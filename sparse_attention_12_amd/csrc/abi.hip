@@ -386,4 +386,35 @@ int32_t dsa_mla_decode_layers(const dsa_batch_t* batch, int32_t n_layers, const 
   return DSA_OK;
 }
 
+int32_t dsa_rope_frequencies(const float* alpha, double* freq) {
+  if (freq == nullptr) return fail(DSA_ERR_NULL, "freq is NULL");
+  dsa::rope_frequencies(alpha, freq);
+  return DSA_OK;
+}
+
+int32_t dsa_rope_append(const dsa_batch_t* batch, int32_t dtype, int32_t rope_dim, const double* freq,
+                        const float* latent, const float* rope_key, void* kv, void* q_attn, const float* ssmax_s,
+                        const float* ssmax_b, void* stream) {
+  dsa::BatchDev b;
+  int st = check_batch(batch, &b);
+  if (st) return st;
+  if ((st = check_dtype(dtype, "dtype"))) return st;
+  if ((st = check_rope(rope_dim))) return st;
+  if ((ssmax_s == nullptr) != (ssmax_b == nullptr))
+    return fail(DSA_ERR_NULL, "ssmax_s and ssmax_b must be given together");
+  if (b.nq == 0) return DSA_OK;
+  REQUIRE_PTR(latent);
+  REQUIRE_PTR(kv);
+  if (rope_dim) {
+    REQUIRE_PTR(freq);
+    REQUIRE_PTR(rope_key);
+  }
+  if (q_attn && !aligned16(q_attn)) return fail(DSA_ERR_ALIGN, "q_attn is not 16-byte aligned");
+  if (ssmax_s && (!aligned16(ssmax_s) || !aligned16(ssmax_b)))
+    return fail(DSA_ERR_ALIGN, "ssmax arrays are not 16-byte aligned");
+  return hip_status(dsa::launch_rope_append(b, dtype, rope_dim, freq, latent, rope_key, kv, q_attn, ssmax_s, ssmax_b,
+                                            as_stream(stream)),
+                    "dsa_rope_append launch");
+}
+
 }  // extern "C"

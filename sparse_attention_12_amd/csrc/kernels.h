@@ -52,4 +52,10 @@ hipError_t launch_mla(const BatchDev& b, int dtype, int rope, const MlaLayers& l
                       const int32_t* idx, int k, float scale, int out_dtype, void* ws,
                       size_t ws_bytes, hipStream_t st);
 
+// Rotary frequencies (host) and the rotary / cache-append step (rope.hip).
+void rope_frequencies(const float* alpha, double* out);
+hipError_t launch_rope_append(const BatchDev& b, int dtype, int rope, const double* freq, const float* latent,
+                              const float* rope_key, void* kv, void* q, const float* ss, const float* sb,
+                              hipStream_t st);
+
 }  // namespace dsa

@@ -42,6 +42,8 @@ def lib():
     l.dsa_mla_decode_layers_workspace_size.restype = sz
     l.dsa_mla_decode_layers.argtypes = [vp, i32, vp, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, i32,
                                         ctypes.c_float, vp, vp, sz, vp]
+    l.dsa_rope_frequencies.argtypes = [vp, vp]
+    l.dsa_rope_append.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     l.dsa_status_string.restype = ctypes.c_char_p
     l.dsa_last_error.restype = ctypes.c_char_p
     return l
@@ -64,7 +66,7 @@ def _batch(nq=2, nseq=2, max_len=100):
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -228,4 +230,37 @@ def test_decode_layers_validation(lib):
         mutate(pl)
         assert call(pl=pl) == SHAPE
         assert lib.dsa_mla_decode_layers_workspace_size(2, 100, 2048, n, ctypes.byref(pl)) == 0
+
+
+def test_rope_frequencies_match_the_oracle(lib):
+    """The library's frequencies (host, double precision) against the
+    oracle's, which its pins tie to the page's wavelength assertions."""
+    import numpy as np
+    from oracle import rope
+    out = np.zeros(32, np.float64)
+    assert lib.dsa_rope_frequencies(None, out.ctypes.data) == OK
+    np.testing.assert_allclose(out, rope.rope_frequencies(), rtol=4e-16)
+    alpha = np.linspace(-1, 1, 32).astype(np.float32)
+    assert lib.dsa_rope_frequencies(alpha.ctypes.data, out.ctypes.data) == OK
+    np.testing.assert_allclose(out, rope.rope_frequencies(alpha.astype(np.float64)), rtol=4e-16)
+    assert lib.dsa_rope_frequencies(None, None) == NULL
+
+
+def test_rope_append_validation(lib):
+    b = _batch()
+
+    def call(dt=1, rope=64, freq=A, lat=A, kr=A, kv=A, q=None, s=None, bb=None):
+        return lib.dsa_rope_append(ctypes.byref(b), dt, rope, freq, lat, kr, kv, q, s, bb, None)
+
+    assert call(dt=2) == DTYPE
+    assert call(rope=16) == SHAPE
+    assert call(freq=None) == NULL
+    assert call(kr=None) == NULL
+    assert call(lat=MIS) == ALIGN
+    assert call(kv=None) == NULL
+    assert call(s=A) == NULL              # the two scaling arrays go together
+    assert call(q=MIS) == ALIGN
+    assert call(rope=0, freq=None, kr=None, lat=None) == NULL   # rotary-free still needs the latent
+    assert lib.dsa_rope_append(ctypes.byref(_batch(nq=0)), 1, 64, None, None, None, None, None, None, None,
+                               None) == OK
 

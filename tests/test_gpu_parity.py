@@ -463,6 +463,68 @@ def test_decode_layers_schedule(B, idt, n_layers):
             assert np.abs(lses[l][qi].cpu().numpy() - r_l[l]).max() <= LSE_TOL["bf16"], f"query {qi} layer {l}"
 
 
+def _round_ref(x, dtype):
+    """Bar for a value the kernel computes in float32 and stores in dtype:
+    the oracle's float64 value within one rounding of dtype plus float32
+    arithmetic."""
+    x = np.asarray(x, np.float64)
+    return (2.0 ** -8 if dtype == "bf16" else 2.0 ** -21) * np.abs(x) + 1e-6 * (np.abs(x).max() + 1e-30)
+
+
+@pytest.mark.parametrize("dtype,rope,scaled,with_q", [
+    ("bf16", 64, True, True), ("f32", 64, True, True), ("bf16", 64, False, False), ("bf16", 0, True, True),
+])
+def test_rope_append(B, dtype, rope, scaled, with_q):
+    """Cache append and query preparation against oracle/rope.py: rows of
+    the new tokens written, every other row untouched, queries scaled and
+    rotated in place, positions from 0 to 2^20 - 1."""
+    from oracle import rope as orope
+    rng = np.random.default_rng(50)
+    lens = np.array([1, 37, 4096, 70001, 1 << 20], np.int32)
+    nq, W = len(lens), 512 + rope
+    row0 = np.concatenate([[0], np.cumsum(lens[:-1])]).astype(np.int64)
+    rows = int(lens.sum())
+    q_pos = lens - 1
+    q_pos[1] = 40          # past its sequence: this token is skipped
+    alpha = (rng.standard_normal(32) * 0.3).astype(np.float32)
+    freq = B.dsa_rope_frequencies(alpha)
+    latent = rng.standard_normal((nq, 512)).astype(np.float32)
+    rkey = rng.standard_normal((nq, 64)).astype(np.float32)
+    qa = rng.standard_normal((nq, 64, W)).astype(np.float32)
+    s_h = (rng.standard_normal(64) * 0.1).astype(np.float32) if scaled else None
+    b_h = (1 + rng.standard_normal(64) * 0.1).astype(np.float32) if scaled else None
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    sentinel = torch.full((rows, W), 7.0, dtype=tdt, device=DEV)
+    kv = sentinel.clone()
+    q_in = torch.from_numpy(qa).to(DEV).to(tdt)
+    q_dev = q_in.clone() if with_q else None
+    batch = B.Batch(torch.arange(nq, dtype=torch.int32, device=DEV), torch.from_numpy(q_pos).to(DEV),
+                    torch.from_numpy(lens).to(DEV), torch.from_numpy(row0).to(DEV), int(lens.max()))
+    dv = lambda a: None if a is None else torch.from_numpy(a).to(DEV)
+    B.dsa_rope_append(batch, dv(freq) if rope else None, dv(latent), dv(rkey) if rope else None, kv, q_dev,
+                      dv(s_h), dv(b_h))
+    torch.cuda.synchronize()
+    changed = torch.nonzero((kv != 7.0).any(dim=1)).flatten().cpu().numpy()
+    q_h = None if q_dev is None else q_dev.float().cpu().numpy()
+    qin_h = q_in.float().cpu().numpy()        # the query as stored before the call
+    written = set()
+    for qi in range(nq):
+        t = int(q_pos[qi])
+        if t >= lens[qi]:
+            if q_h is not None:
+                assert np.array_equal(q_h[qi], qin_h[qi]), "a skipped token's query was modified"
+            continue
+        r = int(row0[qi]) + t
+        written.add(r)
+        ref = orope.append_row(latent[qi], rkey[qi] if rope else None, t, freq)
+        got = kv[r].float().cpu().numpy()
+        assert np.all(np.abs(got - ref) <= _round_ref(ref, dtype)), f"token {qi}: cache row"
+        if q_h is not None:
+            ref_q = orope.prepare_query(qin_h[qi], t, freq, s_h, b_h)
+            assert np.all(np.abs(q_h[qi] - ref_q) <= _round_ref(ref_q, dtype)), f"token {qi}: query"
+    assert set(changed.tolist()) <= written, "a row other than the new tokens' was written"
+
+
 def test_empty_batch_is_noop(B):
     z = torch.zeros(0, dtype=torch.int32, device=DEV)
     batch = B.Batch(z, z, torch.ones(1, dtype=torch.int32, device=DEV), torch.zeros(1, dtype=torch.int64, device=DEV), 1)
