@@ -203,8 +203,11 @@ def _topk_gpu(B, rows, k, ld=None):
     return idx.cpu().numpy(), cnt.cpu().numpy()
 
 
+@pytest.mark.parametrize("long_row", [False, True])
 @pytest.mark.parametrize("k", [1, 5, 64, 2048])
-def test_topk_engineered_rows(B, k):
+def test_topk_engineered_rows(B, k, long_row):
+    """long_row adds a 60,000-score row, which sends the batch down the
+    split path (rows of at most 49,152 scores take one workgroup per row)."""
     rng = np.random.default_rng(23)
     rows = [
         rng.integers(0, 50, 3000).astype(np.float32),                 # heavy ties
@@ -216,6 +219,8 @@ def test_topk_engineered_rows(B, k):
         rng.standard_normal(max(1, k - 3)).astype(np.float32),          # fewer candidates than k
         np.full(k, 5.0, np.float32),                                    # exactly k candidates
     ]
+    if long_row:
+        rows.append(rng.integers(0, 9, 60000).astype(np.float32))
     idx, cnt = _topk_gpu(B, rows, k)
     for i, r in enumerate(rows):
         ref, m = oracle.topk(r.astype(np.float64), k)
@@ -251,11 +256,14 @@ def test_topk_many_rows(B):
 def test_topk_unaligned_rows(B, nrows):
     """Row strides that are not a multiple of four floats: every row but the
     first starts off a 16-byte boundary, so the vector passes take their
-    scalar head and tail paths (few rows: split path; many: one per row)."""
+    scalar head and tail paths (few rows: split path, since some exceed
+    49,152 scores; many: one per row)."""
     rng = np.random.default_rng(32 + nrows)
     rows = []
     for i in range(nrows):
         n = int(rng.integers(2049, 40001)) if i % 3 else int(rng.integers(1, 5000))
+        if nrows < 256 and i == 1:
+            n = 60001
         rows.append(rng.integers(0, 60, n).astype(np.float32) if i % 2 else rng.standard_normal(n).astype(np.float32))
     L = max(len(r) for r in rows)
     idx, cnt = _topk_gpu(B, rows, 2048, ld=L + 3)
