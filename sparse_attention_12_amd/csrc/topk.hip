@@ -32,6 +32,11 @@ constexpr int TK_FCAP = 12288;          // candidate entries held in LDS
 constexpr int TK_CHUNK = 8192;          // scores per workgroup in the split path
 constexpr int TK_ROWS_SPLIT_MAX = 255;  // batches with more rows use one workgroup per row
 constexpr int TK_LEVEL_BITS = 11;       // fallback levels over 64-bit keys
+// First-level histograms are kept in TK_HCOPIES interleaved copies (bin b,
+// copy c at word TK_HCOPIES*b + c; lane l adds to copy l % TK_HCOPIES), so
+// lanes whose scores share a bin -- the scores crowd into few bins -- mostly
+// add to different words.
+constexpr int TK_HCOPIES = 4;
 
 // ---------------------------------------------------------------------------
 // block-wide helpers (1024 threads; every thread must call them)
@@ -110,12 +115,14 @@ __device__ void find_bucket(const uint32_t* hist, int nbins, uint32_t need, Scan
 // (at most three values each) are read one by one.
 __device__ void hist_range(const float* row, int c0, int c1, uint32_t* hist) {
   const int tid = threadIdx.x;
+  const uint32_t copy = (uint32_t)tid & (TK_HCOPIES - 1);
   const int mis = (int)(((uintptr_t)(row + c0) >> 2) & 3);
   const int a0 = min(c1, c0 + ((4 - mis) & 3));
   const int nv = (c1 - a0) >> 2;
   const int t0 = a0 + 4 * nv;
-  if (tid < a0 - c0) atomicAdd(&hist[score_key(row[c0 + tid]) >> TK_SHIFT1], 1u);
-  if (tid < c1 - t0) atomicAdd(&hist[score_key(row[t0 + tid]) >> TK_SHIFT1], 1u);
+  auto add = [&](float x) { atomicAdd(&hist[(score_key(x) >> TK_SHIFT1) * TK_HCOPIES + copy], 1u); };
+  if (tid < a0 - c0) add(row[c0 + tid]);
+  if (tid < c1 - t0) add(row[t0 + tid]);
   const float4* v = (const float4*)(row + a0);
   for (int i0 = 0; i0 < nv; i0 += 4 * TK_THREADS) {
     float4 x[4];
@@ -127,12 +134,25 @@ __device__ void hist_range(const float* row, int c0, int c1, uint32_t* hist) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       if (i0 + u * TK_THREADS + tid < nv) {
-        atomicAdd(&hist[score_key(x[u].x) >> TK_SHIFT1], 1u);
-        atomicAdd(&hist[score_key(x[u].y) >> TK_SHIFT1], 1u);
-        atomicAdd(&hist[score_key(x[u].z) >> TK_SHIFT1], 1u);
-        atomicAdd(&hist[score_key(x[u].w) >> TK_SHIFT1], 1u);
+        add(x[u].x);
+        add(x[u].y);
+        add(x[u].z);
+        add(x[u].w);
       }
     }
+  }
+}
+
+__device__ inline void hist_copies_zero(uint32_t* hc) {
+  for (int i = threadIdx.x; i < TK_BINS1 * TK_HCOPIES; i += TK_THREADS) hc[i] = 0;
+}
+
+// hist[b] = sum of the copies of bin b
+static_assert(TK_HCOPIES == 4, "the folds below read the copies of a bin as one uint4");
+__device__ inline void hist_copies_fold(const uint32_t* hc, uint32_t* hist) {
+  for (int b = threadIdx.x; b < TK_BINS1; b += TK_THREADS) {
+    const uint4 v = *(const uint4*)(hc + b * TK_HCOPIES);
+    hist[b] = v.x + v.y + v.z + v.w;
   }
 }
 
@@ -140,11 +160,17 @@ __device__ void hist_range(const float* row, int c0, int c1, uint32_t* hist) {
 // finalize from an ordered candidate list held in LDS
 // ---------------------------------------------------------------------------
 struct ListShared {
-  uint32_t ukey[TK_FCAP];
-  int32_t pos[TK_FCAP];
+  union {
+    struct {
+      uint32_t ukey[TK_FCAP];
+      int32_t pos[TK_FCAP];
+    };
+    uint32_t hcopies[TK_BINS1 * TK_HCOPIES];  // first-level histogram copies, before the list exists
+  };
   uint32_t hist[1 << 10];
   ScanShared ss;
 };
+static_assert(2 * TK_FCAP >= TK_BINS1 * TK_HCOPIES, "the histogram copies fit in the list area");
 
 // The list holds, in ascending position order, every position whose top 12
 // key bits are >= d1 (`total` entries, `need` of bucket d1 still to take).
@@ -306,7 +332,7 @@ struct RowShared {
 __global__ __launch_bounds__(TK_THREADS) void topk_row_kernel(BatchDev b, const float* __restrict__ scores,
                                                               int64_t ld, int k, int32_t* __restrict__ idx,
                                                               int32_t* __restrict__ count) {
-  __shared__ RowShared sm;
+  __shared__ __attribute__((aligned(16))) RowShared sm;
   const int q = blockIdx.x;
   const int tid = threadIdx.x;
   const QueryRange r = query_range(b, q);
@@ -318,9 +344,14 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_kernel(BatchDev b, const 
     return;
   }
   const float* row = scores + (int64_t)q * ld;
-  for (int i = tid; i < TK_BINS1; i += TK_THREADS) sm.hist1[i] = 0;
+  // the histogram copies live in the candidate-list area, unused until the
+  // compaction
+  uint32_t* hc = sm.list.hcopies;
+  hist_copies_zero(hc);
   __syncthreads();
-  hist_range(row, 0, n, sm.hist1);
+  hist_range(row, 0, n, hc);
+  __syncthreads();
+  hist_copies_fold(hc, sm.hist1);
   __syncthreads();
   int d1;
   uint32_t above;
@@ -350,21 +381,24 @@ struct SplitWs {
 
 __global__ __launch_bounds__(TK_THREADS) void topk_hist_kernel(BatchDev b, const float* __restrict__ scores,
                                                                int64_t ld, int k, SplitWs ws) {
-  __shared__ uint32_t hist[TK_BINS1];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[TK_BINS1 * TK_HCOPIES];
   const int q = blockIdx.y;
   const QueryRange r = query_range(b, q);
   const int c0 = blockIdx.x * TK_CHUNK;
   if (r.n <= k || c0 >= r.n) return;
   const int c1 = min(c0 + TK_CHUNK, r.n);
   const int tid = threadIdx.x;
-  for (int i = tid; i < TK_BINS1; i += TK_THREADS) hist[i] = 0;
+  hist_copies_zero(hist);
   __syncthreads();
   const float* row = scores + (int64_t)q * ld;
   hist_range(row, c0, c1, hist);
   __syncthreads();
   uint32_t* gh = ws.hist + (int64_t)q * TK_BINS1;
-  for (int i = tid; i < TK_BINS1; i += TK_THREADS)
-    if (hist[i]) atomicAdd(&gh[i], hist[i]);
+  for (int i = tid; i < TK_BINS1; i += TK_THREADS) {
+    const uint4 v = *(const uint4*)(hist + i * TK_HCOPIES);
+    const uint32_t s = v.x + v.y + v.z + v.w;
+    if (s) atomicAdd(&gh[i], s);
+  }
 }
 
 __global__ __launch_bounds__(TK_THREADS) void topk_gather_kernel(BatchDev b, const float* __restrict__ scores,
