@@ -18,6 +18,7 @@ pytestmark = pytest.mark.gpu
 
 DEV = torch.device("cuda:0")
 TOL = {"f32": 1e-4, "bf16": 1e-2}
+TAU_ = 1.0 / math.sqrt(192.0)
 LSE_TOL = {"f32": 1e-4, "bf16": 2e-3}
 
 
@@ -413,6 +414,46 @@ def test_fused_decode(B, dtype, idt, lens, layers, rope):
         for l in range(layers):
             _assert_rel(outs[l][qi].cpu().numpy(), r_o[l], TOL[dtype], f"query {qi} layer {l}")
             assert np.abs(lses[l][qi].cpu().numpy() - r_l[l]).max() <= LSE_TOL[dtype]
+
+
+def test_fused_decode_padded_layout_and_shared_sequence(B):
+    """Sequences stored out of order with gaps between them (seq_row0 is all
+    the library uses to find rows), two queries on one sequence at
+    different positions, and a selection size below 2,048."""
+    rng = np.random.default_rng(35)
+    lens = np.array([3000, 2500, 5000], np.int32)
+    gap = 777
+    row0 = np.array([2 * gap + 5000 + 2500, gap + 5000, 0], np.int64)   # reversed, with gaps
+    rows = int(row0.max() + lens[0] + gap)
+    q_seq = np.array([0, 1, 2, 0], np.int32)
+    q_pos = np.array([2999, 2499, 4999, 2000], np.int32)
+    k = 700
+    qI = rng.integers(-3, 4, (4, 32, 128)).astype(np.float32)
+    w_ = rng.integers(1, 5, (4, 32)).astype(np.float32)
+    kI = rng.integers(-3, 4, (rows, 128)).astype(np.float32)
+    layers = 2
+    q = [wl.bf16_bits_to_f32(wl.f32_to_bf16_bits(rng.standard_normal((4, 64, 576)).astype(np.float32)))
+         for _ in range(layers)]
+    kv = [wl.bf16_bits_to_f32(wl.f32_to_bf16_bits(rng.standard_normal((rows, 576)).astype(np.float32)))
+          for _ in range(layers)]
+    bf = lambda a: torch.from_numpy(a).to(DEV).to(torch.bfloat16)
+    batch = B.Batch(torch.from_numpy(q_seq).to(DEV), torch.from_numpy(q_pos).to(DEV), torch.from_numpy(lens).to(DEV),
+                    torch.from_numpy(row0).to(DEV), int(lens.max()))
+    outs = [torch.empty((4, 64, 512), device=DEV) for _ in range(layers)]
+    lses = [torch.empty((4, 64), device=DEV) for _ in range(layers)]
+    idx = torch.full((4, k), -7, dtype=torch.int32, device=DEV)
+    B.dsa_mla_decode_fused(batch, bf(qI), torch.from_numpy(w_).to(DEV), bf(kI), k, [bf(x) for x in q],
+                           [bf(x) for x in kv], outs, TAU_, lses, idx)
+    torch.cuda.synchronize()
+    for qi in range(4):
+        s, n = int(q_seq[qi]), int(q_pos[qi]) + 1
+        r0 = int(row0[s])
+        r_idx, m, r_o, r_l = oracle.decode_query(qI[qi], w_[qi], kI[r0:r0 + lens[s]], [x[qi] for x in q],
+                                                 [x[r0:r0 + lens[s]] for x in kv], n, k, TAU_)
+        assert np.array_equal(idx[qi].cpu().numpy(), r_idx), f"query {qi}: selection"
+        for l in range(layers):
+            _assert_rel(outs[l][qi].cpu().numpy(), r_o[l], TOL["bf16"], f"query {qi} layer {l}")
+            assert np.abs(lses[l][qi].cpu().numpy() - r_l[l]).max() <= LSE_TOL["bf16"]
 
 
 def test_fused_decode_shared_cache(B):
