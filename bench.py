@@ -7,6 +7,11 @@ batches, the three calls in turn for a prefill chunk.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 0..4] [--no-cpu]
                   [--index-dtype fp8]
+  python bench.py --model-layers 72 [--model-batch 64] [--model-context 32768]
+      one decode step of every layer of the model's schedule (indexer layers,
+      selection reuse, rotary-free layers, shared cache), inputs drawn on the
+      GPU from a seeded generator (the caches of 63 layers do not fit a
+      host-side draw in reasonable time); prints its own JSON line.
 
 The default workload is the decode batch of 64 sequences at 32,768 positions
 (bf16).  `roofline` describes the dominant kernel (the indexer): algorithmic
@@ -43,6 +48,10 @@ def parse():
     ap.add_argument("--index-dtype", choices=["bf16", "fp8"], default=None,
                     help="store the indexer's query and keys in this type (default: the workload's)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget")
+    ap.add_argument("--model-layers", type=int, default=0,
+                    help="time a decode step over this many layers of the model's schedule instead")
+    ap.add_argument("--model-batch", type=int, default=64)
+    ap.add_argument("--model-context", type=int, default=32768)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the run, copy a device buffer of this size (for counter calibration)")
     return ap.parse_args()
@@ -97,6 +106,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.model_layers:
+        model_step(args, dev)
+        return
     t_gen = time.time()
     w = workloads.config(args.config, args.index_dtype)
     print(f"[bench] workload {w.name}: nq={w.nq} layers={w.n_layers} max_len={w.max_len} "
@@ -219,6 +231,76 @@ def main():
                                "dsa_index_score + dsa_topk + mla_sparse_attend",
                  "indexer_ms": round(idx_ms, 5), "topk_ms": round(tk_ms, 5),
                  "mla_one_layer_ms": round(mla_ms, 5)},
+    }
+    print(json.dumps(rec))
+
+
+def model_step(args, dev):
+    """Decode step over the first `--model-layers` layers of the model's
+    schedule: per layer its own query; indexer inputs for the layers that run
+    the indexer; a cache for the layers that own one (rotary layers 576-wide,
+    the others 512-wide; from layer 39 the rotary-free layers read layer
+    35's).  One call of dsa_mla_decode_layers per step."""
+    import torch
+
+    from sparse_attention_12_amd import binding as B
+
+    nl, nq, L, k = args.model_layers, args.model_batch, args.model_context, 2048
+    plan = B.dsa_ml4_layer_plan(nl)
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    t_gen = time.time()
+    bf = torch.bfloat16
+    ints = lambda shape: torch.randint(-3, 4, shape, generator=g, device=dev, dtype=torch.int8).to(bf)
+    rows = nq * L
+    qI, wI, kI, q, kv = [], [], [], [], []
+    for l, (runs, rope, src) in enumerate(plan):
+        W = 512 + rope
+        qI.append(ints((nq, 32, 128)) if runs else None)
+        wI.append(torch.randint(1, 5, (nq, 32), generator=g, device=dev).float() if runs else None)
+        kI.append(ints((rows, 128)) if runs else None)
+        q.append(torch.randn((nq, 64, W), generator=g, device=dev, dtype=bf))
+        kv.append(torch.randn((rows, W), generator=g, device=dev, dtype=bf) if src == l else None)
+    torch.cuda.synchronize()
+    print(f"[bench] model step: {nl} layers ({sum(p[0] for p in plan)} run the indexer), {nq} x {L}, "
+          f"inputs drawn on the GPU in {time.time() - t_gen:.1f}s", file=sys.stderr, flush=True)
+    seq_len = torch.full((nq,), L, dtype=torch.int32, device=dev)
+    batch = B.Batch(torch.arange(nq, dtype=torch.int32, device=dev), seq_len - 1, seq_len,
+                    torch.arange(nq, device=dev, dtype=torch.int64) * L, L)
+    outs = [torch.empty((nq, 64, 512), device=dev) for _ in plan]
+    ws = torch.empty(B.dsa_mla_decode_layers_workspace_size(nq, L, k, plan), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    tau = 1.0 / math.sqrt(192.0)
+    step = lambda: B.dsa_mla_decode_layers(batch, plan, qI, wI, kI, k, q, kv, outs, tau, ws=ws)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    # algorithmic bytes: indexer keys and queries of the indexer layers, the
+    # selected rows, queries and outputs of every layer
+    n_sel = min(k, L)
+    idx_bytes = sum(nq * (L * 256 + 32 * 128 * 2 + 32 * 4) for r, _, _ in plan if r)
+    mla_bytes = sum(nq * (n_sel * (512 + rope) * 2 + 64 * (512 + rope) * 2 + 64 * (512 * 4 + 4))
+                    for _, rope, _ in plan)
+    gbps = (idx_bytes + mla_bytes) / (ms / 1e3) / 1e9
+    rec = {
+        "metric": "query-tokens/s for the attention read of every layer of the model's schedule",
+        "value": round(nq / (ms / 1e3), 1), "unit": "query-tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic, drawn on the GPU (seeded torch generator): integer indexer inputs, N(0,1) queries and caches",
+        "config": {"workload": f"decode_b{nq}_L{L}_bf16_{nl}layer_schedule", "queries": nq, "max_context": L,
+                   "layers": nl, "indexer_layers": sum(p[0] for p in plan), "topk": k},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "whole step",
+                     "per_launch": idx_bytes + mla_bytes, "per_launch_unit": "B"},
+        "cpu_baseline": None,
     }
     print(json.dumps(rec))
 
