@@ -319,22 +319,12 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_bf16_kernel(MlaParams p) {
   const int d = wave_u >> 2;
   const int n16 = lane & 15;
   const int g = lane >> 4;
-  const QueryRange r = query_range(p.b, q);
   const int j_begin = split * p.split_len;
   const int nent = max(0, min(j_begin + p.split_len, p.k) - j_begin);
-  const int ntiles = r.n > 0 ? (nent + MLA_TILE - 1) / MLA_TILE : 0;
   const int head = hgrp * 16 + n16;
 
-  // this split's selected positions, padded with -1 to whole tiles (at
-  // least two: tiles 0 and 1 are always gathered); entries outside [0, n)
-  // become -1
-  {
-    const int32_t* sel = p.idx + (int64_t)q * p.k + j_begin;
-    for (int j = tid; j < max(ntiles, 2) * MLA_TILE; j += MLA_THREADS) {
-      const int pos = j < nent ? sel[j] : -1;
-      sel_l[j] = (pos >= 0 && pos < r.n) ? pos : -1;
-    }
-  }
+  // Q and this split's entries of idx are requested first: neither depends
+  // on the sequence, so their round trip overlaps the batch lookups.
   // Q^T (this wave's heads and half of the contraction) as the B operand:
   // head `head`, contraction slots (KSTEPS*d + tt)*32 + 8g + [0,8)
   bf16x8 qf[MLA_KSTEPS];
@@ -342,6 +332,26 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_bf16_kernel(MlaParams p) {
     const uint16_t* qp = (const uint16_t*)p.L.q[layer] + ((int64_t)q * H + head) * G::W + d * (G::W / 2) + g * 8;
 #pragma unroll
     for (int tt = 0; tt < MLA_KSTEPS; ++tt) qf[tt] = as_bf16x8(load16(qp + tt * 32));
+  }
+  constexpr int SEL_PER = MLA_SPLIT_MAX / MLA_THREADS;
+  int selv[SEL_PER];
+  {
+    const int32_t* sel = p.idx + (int64_t)q * p.k + j_begin;
+#pragma unroll
+    for (int i = 0; i < SEL_PER; ++i) {
+      const int j = tid + i * MLA_THREADS;
+      selv[i] = j < nent ? sel[j] : -1;
+    }
+  }
+  const QueryRange r = query_range(p.b, q);
+  const int ntiles = r.n > 0 ? (nent + MLA_TILE - 1) / MLA_TILE : 0;
+  // this split's selected positions, padded with -1 to whole tiles (at
+  // least two: tiles 0 and 1 are always gathered); entries outside [0, n)
+  // become -1
+#pragma unroll
+  for (int i = 0; i < SEL_PER; ++i) {
+    const int j = tid + i * MLA_THREADS;
+    if (j < max(ntiles, 2) * MLA_TILE) sel_l[j] = (selv[i] >= 0 && selv[i] < r.n) ? selv[i] : -1;
   }
   // buffer resource over exactly this sequence's rows (raw addressing): a
   // gather outside them reads zeros and touches no memory
