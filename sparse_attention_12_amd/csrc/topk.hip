@@ -495,26 +495,36 @@ __global__ __launch_bounds__(TK_THREADS) void topk_final_kernel(BatchDev b, cons
     if (tid < nch) sm.off[tid] = o;
     __syncthreads();
     const int64_t lq = (int64_t)q * ws.nchunk * TK_CHUNK;
+    // thread t copies the run of entries [t*R, t*R + R): one search for the
+    // chunk of its first entry, then a forward walk over the offsets
     constexpr int PER = (TK_FCAP + TK_THREADS - 1) / TK_THREADS;
+    const uint32_t R = (total + TK_THREADS - 1) / TK_THREADS;
+    const uint32_t e0 = (uint32_t)tid * R;
+    int c = 0;
+    {
+      int hi = nch - 1;  // last chunk whose offset is <= e0
+      while (c < hi) {
+        const int mid = (c + hi + 1) >> 1;
+        if (sm.off[mid] <= e0) c = mid;
+        else hi = mid - 1;
+      }
+    }
     uint32_t kv[PER];
     int32_t pv[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const uint32_t e = tid + i * TK_THREADS;
-      int lo = 0, hi = nch - 1;  // last chunk whose offset is <= e
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (sm.off[mid] <= e) lo = mid;
-        else hi = mid - 1;
+      const uint32_t e = e0 + i;
+      if ((uint32_t)i < R && e < total) {
+        while (c + 1 < nch && sm.off[c + 1] <= e) ++c;
+        const int64_t src = lq + (int64_t)c * TK_CHUNK + (e - sm.off[c]);
+        kv[i] = ws.lkey[src];
+        pv[i] = ws.lpos[src];
       }
-      const int64_t src = lq + (int64_t)lo * TK_CHUNK + (e < total ? e - sm.off[lo] : 0);
-      kv[i] = ws.lkey[src];
-      pv[i] = ws.lpos[src];
     }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const uint32_t e = tid + i * TK_THREADS;
-      if (e < total) {
+      const uint32_t e = e0 + i;
+      if ((uint32_t)i < R && e < total) {
         sm.list.ukey[e] = kv[i];
         sm.list.pos[e] = pv[i];
       }
