@@ -366,9 +366,9 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_bf16_kernel(MlaParams p) {
   __syncthreads();
 
   // tile t goes to buffer t % 3; two tiles are gathered ahead.  Tiles 0
-  // and 1 are issued whatever the tile count (a missing tile gathers rows
-  // of position -1, which the buffer range check turns into zeros without
-  // a memory access), so the wait below is the same on every path.
+  // and 1 are issued whatever the tile count (a missing tile's entries are
+  // -1 and gather row 0, which the kept-position mask then ignores), so the
+  // wait below is the same on every path.
   int rows[MLA_WAVE_DMAS];
   mla_rows<ROPE>(rows, sel_l, 0, lane, wave_u);
   mla_issue<ROPE>(tile0, scratch_blk, kv, rows, lane, wave_u);
