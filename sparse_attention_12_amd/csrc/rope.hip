@@ -25,6 +25,7 @@
 namespace dsa {
 
 constexpr int ROPE_THREADS = 256;
+constexpr int ROPE_HGROUPS = 8;   // workgroups per token in small batches, each over 8 query heads
 
 template <typename T>
 struct Elem;
@@ -42,8 +43,11 @@ struct Elem<uint16_t> {
   static __device__ inline void put2(uint16_t* p, int i, float a, float b) { *(uint32_t*)(p + i) = pack_bf16x2(a, b); }
 };
 
-// One workgroup per new token.  Pair work is spread over the threads; each
-// pair is two adjacent values, so every access is a 4- or 8-byte vector.
+// gridDim.y workgroups per new token (blockIdx.y: a group of 64/gridDim.y
+// query heads; the first group also writes the cache row): small batches
+// spread a token over ROPE_HGROUPS workgroups, large ones take one each.
+// Pair work is spread over the threads; each pair is two adjacent values, so
+// every access is a 4- or 8-byte vector.
 template <typename T>
 __global__ __launch_bounds__(ROPE_THREADS) void rope_append_kernel(BatchDev b, int rope, const double* __restrict__ freq,
                                                                   const float* __restrict__ latent,
@@ -68,7 +72,7 @@ __global__ __launch_bounds__(ROPE_THREADS) void rope_append_kernel(BatchDev b, i
   const int W = DC + rope;
   // cache row
   T* row = kv + (r.row0 + t) * (int64_t)W;
-  for (int e = tid; e < W / 2; e += ROPE_THREADS) {
+  for (int e = tid; e < (blockIdx.y == 0 ? W / 2 : 0); e += ROPE_THREADS) {
     if (2 * e < DC) {
       const f32x2 v = *(const f32x2*)(latent + (int64_t)qi * DC + 2 * e);
       Elem<T>::put2(row, 2 * e, v[0], v[1]);
@@ -80,10 +84,12 @@ __global__ __launch_bounds__(ROPE_THREADS) void rope_append_kernel(BatchDev b, i
   }
   if (q == nullptr) return;
   // query, in place: scaled per head, rotary pairs rotated
+  const int HG = H / (int)gridDim.y;
   T* qq = q + (int64_t)qi * H * W;
-  for (int e = tid; e < H * W / 2; e += ROPE_THREADS) {
-    const int h = e / (W / 2);
-    const int c = 2 * (e - h * (W / 2));
+  for (int e = tid; e < HG * W / 2; e += ROPE_THREADS) {
+    const int hl = e / (W / 2);
+    const int h = blockIdx.y * HG + hl;
+    const int c = 2 * (e - hl * (W / 2));
     const f32x2 v = Elem<T>::get2(qq, h * W + c);
     const float x = v[0] * msc[h], y = v[1] * msc[h];
     if (c < DC) {
@@ -115,11 +121,12 @@ hipError_t launch_rope_append(const BatchDev& b, int dtype, int rope, const doub
                               const float* rope_key, void* kv, void* q, const float* ss, const float* sb,
                               hipStream_t st) {
   if (b.nq == 0) return hipSuccess;
+  const dim3 grid(b.nq, b.nq < 256 ? ROPE_HGROUPS : 1);
   if (dtype == 0)
-    hipLaunchKernelGGL(rope_append_kernel<float>, dim3(b.nq), dim3(ROPE_THREADS), 0, st, b, rope, freq, latent,
+    hipLaunchKernelGGL(rope_append_kernel<float>, grid, dim3(ROPE_THREADS), 0, st, b, rope, freq, latent,
                        rope_key, (float*)kv, (float*)q, ss, sb);
   else
-    hipLaunchKernelGGL(rope_append_kernel<uint16_t>, dim3(b.nq), dim3(ROPE_THREADS), 0, st, b, rope, freq, latent,
+    hipLaunchKernelGGL(rope_append_kernel<uint16_t>, grid, dim3(ROPE_THREADS), 0, st, b, rope, freq, latent,
                        rope_key, (uint16_t*)kv, (uint16_t*)q, ss, sb);
   return hipGetLastError();
 }

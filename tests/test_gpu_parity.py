@@ -574,6 +574,39 @@ def test_rope_append(B, dtype, rope, scaled, with_q):
     assert set(changed.tolist()) <= written, "a row other than the new tokens' was written"
 
 
+def test_rope_append_prefill_chunk(B):
+    """A chunk of 300 new tokens of one sequence (consecutive positions;
+    batches of 256 or more tokens take one workgroup per token)."""
+    from oracle import rope as orope
+    rng = np.random.default_rng(51)
+    L, nq, first = 5000, 300, 4700
+    freq = B.dsa_rope_frequencies()
+    latent = rng.standard_normal((nq, 512)).astype(np.float32)
+    rkey = rng.standard_normal((nq, 64)).astype(np.float32)
+    qa = rng.standard_normal((nq, 64, 576)).astype(np.float32)
+    s_h = (rng.standard_normal(64) * 0.1).astype(np.float32)
+    b_h = (1 + rng.standard_normal(64) * 0.1).astype(np.float32)
+    kv = torch.full((L, 576), 7.0, dtype=torch.bfloat16, device=DEV)
+    q_in = torch.from_numpy(qa).to(DEV).to(torch.bfloat16)
+    q_dev = q_in.clone()
+    batch = B.Batch(torch.zeros(nq, dtype=torch.int32, device=DEV),
+                    torch.arange(first, first + nq, dtype=torch.int32, device=DEV),
+                    torch.tensor([L], dtype=torch.int32, device=DEV), torch.zeros(1, dtype=torch.int64, device=DEV), L)
+    dv = lambda a: torch.from_numpy(a).to(DEV)
+    B.dsa_rope_append(batch, dv(freq), dv(latent), dv(rkey), kv, q_dev, dv(s_h), dv(b_h))
+    torch.cuda.synchronize()
+    kv_h = kv.float().cpu().numpy()
+    q_h = q_dev.float().cpu().numpy()
+    qin_h = q_in.float().cpu().numpy()
+    for qi in range(0, nq, 37):
+        t = first + qi
+        ref = orope.append_row(latent[qi], rkey[qi], t, freq)
+        assert np.all(np.abs(kv_h[t] - ref) <= _round_ref(ref, "bf16")), f"token {qi}: cache row"
+        ref_q = orope.prepare_query(qin_h[qi], t, freq, s_h, b_h)
+        assert np.all(np.abs(q_h[qi] - ref_q) <= _round_ref(ref_q, "bf16")), f"token {qi}: query"
+    assert np.all(kv_h[:first] == 7.0)
+
+
 def test_empty_batch_is_noop(B):
     z = torch.zeros(0, dtype=torch.int32, device=DEV)
     batch = B.Batch(z, z, torch.ones(1, dtype=torch.int32, device=DEV), torch.zeros(1, dtype=torch.int64, device=DEV), 1)
