@@ -105,7 +105,7 @@ def test_config4_decode_1m(B):
         _check_query(w, qi, idx, outs, lses)
 
 
-@pytest.mark.parametrize("cfg,queries", [(1, (0, 63)), (3, (0, 1024, 2047)), (4, (1,))])
+@pytest.mark.parametrize("cfg,queries", [(1, (0, 63)), (2, (0, 2, 9)), (3, (0, 1024, 2047)), (4, (1,))])
 def test_config_fp8_indexer(B, cfg, queries):
     """The same workloads with the indexer's query and keys stored in FP8
     E4M3 (bench.py --index-dtype fp8): the integer draws are exact in E4M3,
