@@ -390,6 +390,24 @@ constexpr int PF_QB = PF_WAVES * PF_QPW;     // queries per workgroup
 constexpr int PF_TK = 32;                    // keys per LDS tile
 constexpr int PF_KC = 8192;                  // keys per workgroup
 
+// (key chunk, query block) of a prefill workgroup.  Workgroups go to the 8
+// XCDs round-robin in launch order (linear id L -> XCD L % 8), each XCD with
+// its own L2; the pairs are numbered chunk-major and XCD x takes the x-th
+// contiguous eighth of them, so the workgroups that share a key chunk run
+// on one XCD and read it into one L2.  (A remainder of fewer than 8
+// workgroups keeps the launch order.)
+struct PfTile {
+  int chunk, qblock;
+};
+__device__ inline PfTile prefill_tile() {
+  const int nchunk = gridDim.x, nqb = gridDim.y;
+  const int n = nchunk * nqb;
+  const int L = blockIdx.y * nchunk + blockIdx.x;
+  const int per = n / 8;
+  const int p = L < 8 * per ? (L % 8) * per + L / 8 : L;
+  return PfTile{p / nqb, p % nqb};
+}
+
 __global__ __launch_bounds__(PF_THREADS) void idx_prefill_bf16(
     BatchDev b, const uint16_t* __restrict__ qI, const float* __restrict__ w,
     const uint16_t* __restrict__ kI, float* __restrict__ scores, int64_t ld) {
@@ -403,8 +421,9 @@ __global__ __launch_bounds__(PF_THREADS) void idx_prefill_bf16(
   const int wave = tid >> 6;
   const int col = lane & 31;
   const int half = lane >> 5;
-  const int qg0 = blockIdx.y * PF_QB;
-  const int kbase = blockIdx.x * PF_KC;
+  const PfTile tile = prefill_tile();
+  const int qg0 = tile.qblock * PF_QB;
+  const int kbase = tile.chunk * PF_KC;
 
   if (tid < PF_QB) {
     const int qi = qg0 + tid;
@@ -492,8 +511,9 @@ __global__ __launch_bounds__(PF_THREADS) void idx_prefill_fp8(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31;
   const int half = lane >> 5;
-  const int qg0 = blockIdx.y * PF_QB;
-  const int kbase = blockIdx.x * PF_KC;
+  const PfTile tile = prefill_tile();
+  const int qg0 = tile.qblock * PF_QB;
+  const int kbase = tile.chunk * PF_KC;
 
   if (tid < PF_QB) {
     const int qi = qg0 + tid;

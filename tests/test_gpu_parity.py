@@ -88,7 +88,8 @@ def test_index_score_decode_many_queries(B, idt):
 
 
 @pytest.mark.parametrize("idt", ["bf16", "fp8"])
-@pytest.mark.parametrize("cache,first,nq", [(3000, 2900, 70), (5000, 10, 64), (9000, 8960, 40)])
+@pytest.mark.parametrize("cache,first,nq", [(3000, 2900, 70), (5000, 10, 64), (9000, 8960, 40),
+                                            (30000, 29840, 160)])
 def test_index_score_prefill_exact(B, cache, first, nq, idt):
     w = wl.make_prefill(cache, first, nq, "bf16", seed=22, index_dtype=idt)
     t = w.to_torch(DEV)
