@@ -15,7 +15,8 @@
 //      earlier positions with u == T were kept (lower position wins ties).
 // Long rows with few queries (decode) split steps 1-2 over many workgroups
 // (per-chunk lists, concatenated in chunk order); many rows (prefill) run
-// one workgroup per row.  If the candidate list would not fit in LDS (for
+// one workgroup per row, which keeps up to 49,152 of a row's scores in
+// registers between steps 1 and 2.  If the candidate list would not fit in LDS (for
 // instance every score equal), a row-streaming fallback selects with
 // 64-bit (u, position) keys and compacts the row itself.
 #include "dsa_common.h"
@@ -329,43 +330,107 @@ struct RowShared {
   ListShared list;
 };
 
-__global__ __launch_bounds__(TK_THREADS) void topk_row_kernel(BatchDev b, const float* __restrict__ scores,
-                                                              int64_t ld, int k, int32_t* __restrict__ idx,
-                                                              int32_t* __restrict__ count) {
+// Rows of n <= k keep every position.
+__device__ inline void keep_all(int n, int k, int32_t* out) {
+  for (int j = threadIdx.x; j < k; j += TK_THREADS) out[j] = j < n ? j : -1;
+}
+
+// One workgroup per row, its first NST * 16,384 scores held in registers:
+// thread t loads the runs [16t, 16t + 16) of each such 16,384-score stretch
+// once, as keys, and the histogram and the ordered compaction both read
+// them there, so that part of the row crosses HBM once.  The rest of a
+// longer row (beyond what 128 registers per thread hold) is read twice,
+// as in the two-pass path.
+template <int NST>
+__global__ __launch_bounds__(TK_THREADS) void topk_row_reg_kernel(BatchDev b, const float* __restrict__ scores,
+                                                                 int64_t ld, int k, int32_t* __restrict__ idx,
+                                                                 int32_t* __restrict__ count) {
   __shared__ __attribute__((aligned(16))) RowShared sm;
   const int q = blockIdx.x;
   const int tid = threadIdx.x;
   const QueryRange r = query_range(b, q);
   const int n = r.n;
   int32_t* out = idx + (int64_t)q * k;
-  if (n <= k) {
-    for (int j = tid; j < k; j += TK_THREADS) out[j] = j < n ? j : -1;
-    if (tid == 0 && count) count[q] = n;
-    return;
-  }
   const float* row = scores + (int64_t)q * ld;
-  // the histogram copies live in the candidate-list area, unused until the
-  // compaction
-  uint32_t* hc = sm.list.hcopies;
-  hist_copies_zero(hc);
-  __syncthreads();
-  hist_range(row, 0, n, hc);
-  __syncthreads();
-  hist_copies_fold(hc, sm.hist1);
-  __syncthreads();
-  int d1;
-  uint32_t above;
-  find_bucket(sm.hist1, TK_BINS1, (uint32_t)k, sm.list.ss, &d1, &above);
-  const uint32_t need = (uint32_t)k - above;
-  const uint32_t total = above + sm.hist1[d1];
-  if (total <= (uint32_t)TK_FCAP) {
-    compact_chunk(row, 0, n, (uint32_t)d1, sm.list.ukey, sm.list.pos, TK_FCAP, sm.list.ss);
-    __syncthreads();
-    finalize_list(sm.list, (int)total, (uint32_t)d1, need, out);
+  if (n <= k) {
+    keep_all(n, k, out);
   } else {
-    select_row_streaming(row, n, k, (uint32_t)d1, need, sm.hist1, sm.list.ss, out);
+    constexpr int REG = NST * TK_STRETCH;
+    uint32_t* hc = sm.list.hcopies;
+    hist_copies_zero(hc);
+    // keys of this thread's runs (positions at or past n are never counted)
+    uint32_t u[NST][TK_RUN];
+    const bool vec = (((uintptr_t)row) & 15) == 0;
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      const int s0 = st * TK_STRETCH + tid * TK_RUN;
+      if (vec && s0 + TK_RUN <= n) {
+#pragma unroll
+        for (int i = 0; i < TK_RUN / 4; ++i) {
+          const float4 x = *(const float4*)(row + s0 + 4 * i);
+          u[st][4 * i + 0] = score_key(x.x);
+          u[st][4 * i + 1] = score_key(x.y);
+          u[st][4 * i + 2] = score_key(x.z);
+          u[st][4 * i + 3] = score_key(x.w);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < TK_RUN; ++j) u[st][j] = s0 + j < n ? score_key(row[s0 + j]) : 0u;
+      }
+    }
+    __syncthreads();  // copies cleared
+    const uint32_t copy = (uint32_t)tid & (TK_HCOPIES - 1);
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      const int s0 = st * TK_STRETCH + tid * TK_RUN;
+#pragma unroll
+      for (int j = 0; j < TK_RUN; ++j)
+        if (s0 + j < n) atomicAdd(&hc[(u[st][j] >> TK_SHIFT1) * TK_HCOPIES + copy], 1u);
+    }
+    if (n > REG) hist_range(row, REG, n, hc);
+    __syncthreads();
+    hist_copies_fold(hc, sm.hist1);
+    __syncthreads();
+    int d1;
+    uint32_t above;
+    find_bucket(sm.hist1, TK_BINS1, (uint32_t)k, sm.list.ss, &d1, &above);
+    const uint32_t need = (uint32_t)k - above;
+    const uint32_t total = above + sm.hist1[d1];
+    if (total <= (uint32_t)TK_FCAP) {
+      // ordered compaction of the keys with top 12 bits >= d1, one block
+      // scan per stretch
+      uint32_t base = 0;
+#pragma unroll
+      for (int st = 0; st < NST; ++st) {
+        const int s0 = st * TK_STRETCH + tid * TK_RUN;
+        uint32_t f = 0;
+#pragma unroll
+        for (int j = 0; j < TK_RUN; ++j)
+          if (s0 + j < n && (u[st][j] >> TK_SHIFT1) >= (uint32_t)d1) f |= 1u << j;
+        uint32_t pslot = block_exclusive_scan(__builtin_popcount(f), sm.list.ss.wsum, &sm.list.ss.total);
+#pragma unroll
+        for (int j = 0; j < TK_RUN; ++j) {
+          if (f & (1u << j)) {
+            const uint32_t slot = base + pslot++;
+            if (slot < (uint32_t)TK_FCAP) {
+              sm.list.ukey[slot] = u[st][j];
+              sm.list.pos[slot] = s0 + j;
+            }
+          }
+        }
+        base += sm.list.ss.total;
+        __syncthreads();
+      }
+      if (n > REG) {
+        compact_chunk(row, REG, n, (uint32_t)d1, sm.list.ukey + base, sm.list.pos + base, TK_FCAP - base, sm.list.ss);
+        __syncthreads();
+      }
+      finalize_list(sm.list, (int)total, (uint32_t)d1, need, out);
+    } else {
+      select_row_streaming(row, n, k, (uint32_t)d1, need, sm.hist1, sm.list.ss, out);
+    }
   }
-  if (tid == 0 && count) count[q] = k;
+  if (tid == 0 && count) count[q] = min(n, k);
 }
 
 // ---------------------------------------------------------------------------
@@ -589,7 +654,14 @@ hipError_t launch_topk(const BatchDev& b, const float* scores, int64_t ld, int k
                        int32_t* count, void* wsp, size_t ws_bytes, hipStream_t st, bool ws_zeroed) {
   if (b.nq == 0) return hipSuccess;
   if (!use_split(b.nq, b.max_len)) {
-    hipLaunchKernelGGL(topk_row_kernel, dim3(b.nq), dim3(TK_THREADS), 0, st, b, scores, ld, k, idx, count);
+    // as many 16,384-score stretches in registers as the row needs, at most 3
+    const int nst = (b.max_len + TK_STRETCH - 1) / TK_STRETCH;
+    if (nst <= 1)
+      hipLaunchKernelGGL(topk_row_reg_kernel<1>, dim3(b.nq), dim3(TK_THREADS), 0, st, b, scores, ld, k, idx, count);
+    else if (nst == 2)
+      hipLaunchKernelGGL(topk_row_reg_kernel<2>, dim3(b.nq), dim3(TK_THREADS), 0, st, b, scores, ld, k, idx, count);
+    else
+      hipLaunchKernelGGL(topk_row_reg_kernel<3>, dim3(b.nq), dim3(TK_THREADS), 0, st, b, scores, ld, k, idx, count);
     return hipGetLastError();
   }
   SplitWs ws;

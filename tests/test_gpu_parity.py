@@ -275,6 +275,28 @@ def test_topk_unaligned_rows(B, nrows):
         assert np.array_equal(idx[i], ref), f"row {i}: selection differs"
 
 
+def test_topk_many_long_rows(B):
+    """Many rows, some longer than the 49,152 scores the per-row kernel keeps
+    in registers: the rest of such a row is read from memory in both passes
+    (row stride odd, so off 16-byte boundaries), including a long all-equal
+    row that overflows the LDS candidate list."""
+    rng = np.random.default_rng(41)
+    rows = []
+    for i in range(260):
+        n = int(rng.integers(1, 4000))
+        rows.append(rng.integers(0, 30, n).astype(np.float32) if i % 2 else rng.standard_normal(n).astype(np.float32))
+    rows[3] = rng.integers(0, 9, 60001).astype(np.float32)          # remainder of 10,849 scores, heavy ties
+    rows[4] = np.zeros(65536, np.float32)                            # all equal: streaming fallback
+    rows[7] = rng.standard_normal(70001).astype(np.float32)          # distinct, longest
+    rows[10] = rng.integers(0, 4, 49153).astype(np.float32) * 1e3    # one score past the registers
+    L = max(len(r) for r in rows)
+    idx, cnt = _topk_gpu(B, rows, 2048, ld=L + 1)
+    for i, r in enumerate(rows):
+        ref, m = oracle.topk(r.astype(np.float64), 2048)
+        assert cnt[i] == m, f"row {i}"
+        assert np.array_equal(idx[i], ref), f"row {i}: selection differs"
+
+
 def test_topk_on_indexer_scores(B):
     w = wl.make_decode([2048, 2049, 5000, 33000], "bf16", 1, seed=24)
     t = w.to_torch(DEV)
