@@ -97,7 +97,7 @@ def indexer_kernel(w) -> str:
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(every workload runs on a single MI355X); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
