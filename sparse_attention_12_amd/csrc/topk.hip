@@ -438,6 +438,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_reg_kernel(BatchDev b, co
 // ---------------------------------------------------------------------------
 struct SplitWs {
   uint32_t* hist;     // [nq][4096]
+  uint32_t* bucket;   // [nq][4]: threshold bucket d1, entries above it, entries in it
   uint32_t* cnt;      // [nq][nchunk]
   uint32_t* lkey;     // [nq][nchunk * TK_CHUNK]
   int32_t* lpos;      // [nq][nchunk * TK_CHUNK]
@@ -509,6 +510,12 @@ __global__ __launch_bounds__(TK_THREADS) void topk_gather_kernel(BatchDev b, con
   for (int j = 0; j < GR; ++j)
     if (s0 + j < c1 && (u[j] >> TK_SHIFT1) >= (uint32_t)d1) f |= 1u << j;
   uint32_t slot = block_exclusive_scan(__builtin_popcount(f), ss.wsum, &ss.total);
+  // every chunk finds the same bucket; the first publishes it for the final pass
+  if (c == 0 && tid == 0) {
+    ws.bucket[q * 4 + 0] = (uint32_t)d1;
+    ws.bucket[q * 4 + 1] = above;
+    ws.bucket[q * 4 + 2] = hist[d1];
+  }
   const int64_t lbase = ((int64_t)q * ws.nchunk + c) * TK_CHUNK;
 #pragma unroll
   for (int j = 0; j < GR; ++j) {
@@ -541,17 +548,14 @@ __global__ __launch_bounds__(TK_THREADS) void topk_final_kernel(BatchDev b, cons
     if (tid == 0 && count) count[q] = n;
     return;
   }
-  // the histogram and the per-chunk list lengths are read together
-  const uint32_t* gh = ws.hist + (int64_t)q * TK_BINS1;
+  // the threshold bucket (found by the gather pass) and the per-chunk list
+  // lengths are read together
   const int nch = (n + TK_CHUNK - 1) / TK_CHUNK;
   const uint32_t mine = tid < nch ? ws.cnt[(int64_t)q * ws.nchunk + tid] : 0u;
-  for (int i = tid; i < TK_BINS1; i += TK_THREADS) sm.hist1[i] = gh[i];
-  __syncthreads();
-  int d1;
-  uint32_t above;
-  find_bucket(sm.hist1, TK_BINS1, (uint32_t)k, sm.list.ss, &d1, &above);
+  const int d1 = (int)ws.bucket[q * 4 + 0];
+  const uint32_t above = ws.bucket[q * 4 + 1];
   const uint32_t need = (uint32_t)k - above;
-  const uint32_t total = above + sm.hist1[d1];
+  const uint32_t total = above + ws.bucket[q * 4 + 2];
   if (total <= (uint32_t)TK_FCAP) {
     // concatenate the per-chunk lists in chunk (= position) order: offsets
     // by a block scan, then every entry copied in one parallel pass with all
@@ -624,11 +628,13 @@ static size_t split_bytes(int nq, int max_len, SplitWs* ws, char* base) {
     return at;
   };
   const size_t h = take((size_t)nq * TK_BINS1 * 4);
+  const size_t bk = take((size_t)nq * 4 * 4);
   const size_t c = take((size_t)nq * nchunk * 4);
   const size_t kk = take((size_t)nq * nchunk * TK_CHUNK * 4);
   const size_t p = take((size_t)nq * nchunk * TK_CHUNK * 4);
   if (ws) {
     ws->hist = (uint32_t*)(base + h);
+    ws->bucket = (uint32_t*)(base + bk);
     ws->cnt = (uint32_t*)(base + c);
     ws->lkey = (uint32_t*)(base + kk);
     ws->lpos = (int32_t*)(base + p);
