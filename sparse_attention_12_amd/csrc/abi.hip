@@ -196,9 +196,14 @@ static size_t fused_parts(int32_t nq, int32_t max_len, int32_t k, int32_t n_laye
   *off_topk = off;
   off = align_up(off + dsa::topk_workspace_bytes(nq, max_len, k));
   *off_mla = off;
-  size_t a = dsa::mla_workspace_bytes(0, nq, k, n_layers);
-  size_t c = dsa::mla_workspace_bytes(1, nq, k, n_layers);
-  off = align_up(off + (a > c ? a : c));
+  // a launch over fewer layers can take more splits: size for the largest
+  size_t m = 0;
+  for (int n = 1; n <= n_layers; ++n)
+    for (int dt = 0; dt < 2; ++dt) {
+      const size_t x = dsa::mla_workspace_bytes(dt, nq, k, n);
+      m = x > m ? x : m;
+    }
+  off = align_up(off + m);
   return off;
 }
 

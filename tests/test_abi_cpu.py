@@ -232,6 +232,21 @@ def test_decode_layers_validation(lib):
         assert lib.dsa_mla_decode_layers_workspace_size(2, 100, 2048, n, ctypes.byref(pl)) == 0
 
 
+def test_decode_layers_workspace_covers_every_run(lib):
+    """A run of fewer layers sharing a selection can take more splits than
+    the longest run (at 32 queries, three layers take three splits and four
+    layers two), so the layers workspace covers every run length."""
+    n = 7
+    arr = (Plan * n)()
+    for l in range(n):
+        arr[l].runs_indexer = int(l in (0, 4))
+        arr[l].rope_dim = 64
+        arr[l].kv_source = 0
+    need = lib.dsa_mla_decode_layers_workspace_size(32, 3000, 2048, n, ctypes.byref(arr))
+    for run in (3, 4):
+        assert need >= lib.dsa_mla_decode_fused_workspace_size(32, 3000, 2048, run)
+
+
 def test_rope_frequencies_match_the_oracle(lib):
     """The library's frequencies (host, double precision) against the
     oracle's, which its pins tie to the page's wavelength assertions."""

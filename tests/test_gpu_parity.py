@@ -535,6 +535,41 @@ def test_decode_layers_schedule(B, idt, n_layers):
             assert np.abs(lses[l][qi].cpu().numpy() - r_l[l]).max() <= LSE_TOL["bf16"], f"query {qi} layer {l}"
 
 
+def test_decode_layers_runs_of_four_and_three(B):
+    """Runs of four and three layers over one shared cache at 32 queries:
+    the three-layer run's launch takes more splits than the four-layer
+    one's, and both fit the workspace the size query returns."""
+    n = 7
+    oplan = [(l in (0, 4), True, 0) for l in range(n)]
+    plan = [(int(r), 64, src) for r, _, src in oplan]
+    rng = np.random.default_rng(44)
+    lens = [int(x) for x in rng.integers(2049, 2400, 32)]
+    st = wl.make_layer_stack(lens, oplan, "bf16", seed=45)
+    w = st.base
+    t = w.to_torch(DEV)
+    d = st.to_torch(DEV)
+    outs = [torch.empty((w.nq, 64, 512), device=DEV) for _ in plan]
+    lses = [torch.empty((w.nq, 64), device=DEV) for _ in plan]
+    idxs = [torch.full((w.nq, w.k), -7, dtype=torch.int32, device=DEV) if r else None for r, _, _ in plan]
+    ws = torch.full((B.dsa_mla_decode_layers_workspace_size(w.nq, w.max_len, w.k, plan),), 0xA5,
+                    dtype=torch.uint8, device=DEV)
+    B.dsa_mla_decode_layers(_batch(B, w, t), plan, d["qI"], d["w"], d["kI"], w.k, d["q"], d["kv"], outs, w.tau,
+                            lses, idxs, ws)
+    torch.cuda.synchronize()
+    for qi in (0, 31):
+        n_c = lens[qi]
+        rows = lambda a: None if a is None else w.widen(w.seq_rows(a, qi))
+        r_idx, r_o, r_l = oracle.decode_layers(
+            oplan, [None if a is None else w.widen(a)[qi] for a in st.qI],
+            [None if a is None else a[qi] for a in st.w], [rows(a) for a in st.kI],
+            [w.widen(a)[qi] for a in st.q], [rows(a) for a in st.kv], n_c, w.k, w.tau)
+        for l, (runs, _, _) in enumerate(oplan):
+            if runs:
+                assert np.array_equal(idxs[l][qi].cpu().numpy(), r_idx[l]), f"query {qi} layer {l}: selection"
+            _assert_rel(outs[l][qi].cpu().numpy(), r_o[l], TOL["bf16"], f"query {qi} layer {l}")
+            assert np.abs(lses[l][qi].cpu().numpy() - r_l[l]).max() <= LSE_TOL["bf16"], f"query {qi} layer {l}"
+
+
 def _round_ref(x, dtype):
     """Bar for a value the kernel computes in float32 and stores in dtype:
     the oracle's float64 value within one rounding of dtype plus float32
