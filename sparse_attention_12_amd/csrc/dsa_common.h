@@ -63,6 +63,12 @@ __device__ inline float bf16_to_f32(uint16_t x) { return __uint_as_float((uint32
 // pure VALU, no LDS round trip.  Each swap of x with itself leaves, in every
 // lane, the values of the two rows being paired, so the pair's max or sum
 // needs no lane select.
+// max(x, 0) in one integer instruction: a float with the sign bit set is a
+// negative integer, and non-negative floats order as their bit patterns, so
+// the signed-integer max with 0 is max(x, +0) for every non-NaN x (fmaxf
+// costs a second instruction that quiets NaNs first).
+__device__ inline float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 __device__ inline float rows4_max(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));

@@ -106,8 +106,8 @@ __device__ __forceinline__ void idx_decode_range(const BatchDev& b, const uint16
       float part = 0.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        part = fmaf(wr[0][i], fmaxf(acc0[i], 0.0f), part);
-        part = fmaf(wr[1][i], fmaxf(acc1[i], 0.0f), part);
+        part = fmaf(wr[0][i], relu(acc0[i]), part);
+        part = fmaf(wr[1][i], relu(acc1[i]), part);
       }
       part = rows4_sum(part);
       const int key = k + kb2 * 16 + c16;
@@ -199,8 +199,8 @@ __device__ __forceinline__ void idx_decode_range_f8(const BatchDev& b, const uin
       float part = 0.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        part = fmaf(wr[0][i], fmaxf(acc0[i], 0.0f), part);
-        part = fmaf(wr[1][i], fmaxf(acc1[i], 0.0f), part);
+        part = fmaf(wr[0][i], relu(acc0[i]), part);
+        part = fmaf(wr[1][i], relu(acc1[i]), part);
       }
       part = rows4_sum(part);
       const int key = k + kb4 * 16 + c16;
@@ -375,7 +375,7 @@ __global__ __launch_bounds__(IDX_F32_THREADS) void idx_decode_f32(
       dot = fmaf(qh[4 * i + 2], kr[i].z, dot);
       dot = fmaf(qh[4 * i + 3], kr[i].w, dot);
     }
-    total = fmaf(wsh[h], fmaxf(dot, 0.0f), total);
+    total = fmaf(wsh[h], relu(dot), total);
   }
   scores[(int64_t)q * ld + key] = total;
 }
@@ -477,7 +477,7 @@ __global__ __launch_bounds__(PF_THREADS) void idx_prefill_bf16(
       const float* wq = wl + (wave * PF_QPW + j) * HI + 4 * half;
       float part = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) part = fmaf(wq[8 * (i >> 2) + (i & 3)], fmaxf(acc[i], 0.0f), part);
+      for (int i = 0; i < 16; ++i) part = fmaf(wq[8 * (i >> 2) + (i & 3)], relu(acc[i]), part);
       part = halves_sum(part);
       const int key = k0 + col;
       if (half == 0 && key < nj[j])
@@ -595,7 +595,7 @@ __global__ __launch_bounds__(PF_THREADS) void idx_prefill_fp8(
       for (int j = 0; j < PF_QPW; ++j) {
         float part = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) part = fmaf(wr[j][i], fmaxf(acc[j][i], 0.0f), part);
+        for (int i = 0; i < 16; ++i) part = fmaf(wr[j][i], relu(acc[j][i]), part);
         part = halves_sum(part);
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, part), srs[j], soff, 0, 0);
       }
