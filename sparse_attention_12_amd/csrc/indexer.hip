@@ -457,6 +457,16 @@ __global__ __launch_bounds__(PF_THREADS) void idx_prefill_bf16(
   const int lc = tid & 15;   // its 16-byte chunk
   const int lslot = lk * 16 + (lc ^ (lk & 15));
   const uint16_t* kb = kI + row0 * DI + lc * 8;
+  // per query, a buffer resource over exactly its candidate columns: a
+  // store at a column >= n_cand (or from the upper half-wave, which holds no
+  // result) lies outside it and is dropped without a branch
+  __amdgpu_buffer_rsrc_t srs[PF_QPW];
+#pragma unroll
+  for (int j = 0; j < PF_QPW; ++j) {
+    const int n = __builtin_amdgcn_readfirstlane(nj[j]);
+    srs[j] = __builtin_amdgcn_make_buffer_rsrc(scores + (int64_t)(qg0 + wave * PF_QPW + j) * ld, (short)0,
+                                               (int)((uint32_t)n * 4u), 0x00020000);
+  }
   u32x4 pre = load16_nt(kb + (int64_t)min(kbase + lk, kend - 1) * DI);
   int buf = 0;
   for (int k0 = kbase; k0 < kend; k0 += PF_TK) {
@@ -467,21 +477,29 @@ __global__ __launch_bounds__(PF_THREADS) void idx_prefill_bf16(
 #pragma unroll
     for (int t = 0; t < 8; ++t)
       bfr[t] = as_bf16x8(ktile[buf][col * 16 + ((2 * t + half) ^ (col & 15))]);
+    const int soff = half ? (int)0x80000000u : (k0 + col) * 4;
+    // the wave's queries two at a time, branch-free: two independent
+    // product chains, then their ReLU-weighted head sums
 #pragma unroll
-    for (int j = 0; j < PF_QPW; ++j) {
-      if (k0 >= nj[j]) continue;
-      f32x16 acc = {};
+    for (int jp = 0; jp < PF_QPW; jp += 2) {
+      f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j][t], bfr[t], acc, 0, 0, 0);
-      const float* wq = wl + (wave * PF_QPW + j) * HI + 4 * half;
-      float part = 0.0f;
+      for (int t = 0; t < 8; ++t) {
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[jp][t], bfr[t], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[jp + 1][t], bfr[t], acc1, 0, 0, 0);
+      }
+      const float* wq0 = wl + (wave * PF_QPW + jp) * HI + 4 * half;
+      const float* wq1 = wq0 + HI;
+      float p0 = 0.0f, p1 = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) part = fmaf(wq[8 * (i >> 2) + (i & 3)], relu(acc[i]), part);
-      part = halves_sum(part);
-      const int key = k0 + col;
-      if (half == 0 && key < nj[j])
-        scores[(int64_t)(qg0 + wave * PF_QPW + j) * ld + key] = part;
+      for (int i = 0; i < 16; ++i) {
+        p0 = fmaf(wq0[8 * (i >> 2) + (i & 3)], relu(acc0[i]), p0);
+        p1 = fmaf(wq1[8 * (i >> 2) + (i & 3)], relu(acc1[i]), p1);
+      }
+      p0 = halves_sum(p0);
+      p1 = halves_sum(p1);
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, p0), srs[jp], soff, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, p1), srs[jp + 1], soff, 0, 0);
     }
     buf ^= 1;
   }
