@@ -570,6 +570,43 @@ def test_decode_layers_runs_of_four_and_three(B):
             assert np.abs(lses[l][qi].cpu().numpy() - r_l[l]).max() <= LSE_TOL["bf16"], f"query {qi} layer {l}"
 
 
+def test_fused_read_under_graph_capture(B):
+    """The fused decode read captured in a graph (workspace passed in, so the
+    capture allocates nothing): every replay, with eager work and
+    synchronisations between replays, equals an eager call bit for bit --
+    the library clears its scratch with its own kernels, never with a
+    memset node."""
+    w = wl.make_decode([1500, 2600, 70000], "bf16", 2, seed=46)
+    t = w.to_torch(DEV)
+    batch = _batch(B, w, t)
+    ws = torch.empty(B.dsa_mla_decode_fused_workspace_size(w.nq, w.max_len, w.k, 2), dtype=torch.uint8, device=DEV)
+    outs = [torch.empty((w.nq, 64, 512), device=DEV) for _ in range(2)]
+    lses = [torch.empty((w.nq, 64), device=DEV) for _ in range(2)]
+    idx = torch.empty((w.nq, w.k), dtype=torch.int32, device=DEV)
+    call = lambda: B.dsa_mla_decode_fused(batch, t["qI"], t["w"], t["kI"], w.k, t["q"], t["kv"], outs, w.tau,
+                                          lses, idx, ws)
+    call()
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in outs + lses + [idx]]
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            call()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for x in outs + lses:
+            x.fill_(float("nan"))
+        idx.fill_(-7)
+        ws.fill_(0xA5)                    # stale scratch before every replay
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs + lses + [idx], ref):
+            assert torch.equal(a, b), f"replay {rep} differs from the eager call"
+
+
 def _round_ref(x, dtype):
     """Bar for a value the kernel computes in float32 and stores in dtype:
     the oracle's float64 value within one rounding of dtype plus float32
