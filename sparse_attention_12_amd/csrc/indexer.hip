@@ -10,9 +10,10 @@
 // with 8 of the 32 head dot products of one key; the ReLU and the weighted
 // head sum stay in registers and finish with two cross-lane adds.
 //
-// Prefill (many queries of one sequence) is a blocked product: a workgroup
+// Prefill (many queries per sequence) is a blocked product: a workgroup
 // keeps 32 queries' indexer rows in registers (4 per wave) and streams key
-// tiles through LDS, so each key tile read from L2 feeds 32 queries.
+// tiles through LDS, so each key tile read from L2 feeds the block's queries
+// of that sequence.
 #include "dsa_common.h"
 #include "kernels.h"
 
@@ -381,7 +382,7 @@ __global__ __launch_bounds__(IDX_F32_THREADS) void idx_decode_f32(
 }
 
 // ---------------------------------------------------------------------------
-// prefill, bf16: 32 queries of one sequence per workgroup
+// prefill, bf16: 32 queries per workgroup
 // ---------------------------------------------------------------------------
 constexpr int PF_THREADS = 512;
 constexpr int PF_WAVES = PF_THREADS / 64;
@@ -408,14 +409,50 @@ __device__ inline PfTile prefill_tile() {
   return PfTile{p / nqb, p % nqb};
 }
 
-__global__ __launch_bounds__(PF_THREADS) void idx_prefill_bf16(
-    BatchDev b, const uint16_t* __restrict__ qI, const float* __restrict__ w,
-    const uint16_t* __restrict__ kI, float* __restrict__ scores, int64_t ld) {
+// The block's queries may belong to several sequences (a prefill batch of
+// several chunks): the key chunk is swept once per sequence, the first
+// sweep for the sequence of the block's first query, each for every block
+// query of that sequence.  Fills sq for the next sequence not yet swept
+// (same values in every thread) and returns false when none is left.
+struct PfSeq {
+  int s;          // sequence
+  int nmax;       // most candidates among its queries
+  uint32_t mine;  // its queries (bit j: block query j)
+  uint32_t done;  // queries swept so far
+};
+__device__ inline bool next_block_sequence(const int* qseq, const int* ncand, PfSeq& sq) {
+  int s = -1;
+  for (int j = 0; j < PF_QB; ++j)
+    if (s < 0 && !((sq.done >> j) & 1u) && qseq[j] >= 0) s = qseq[j];
+  if (s < 0) return false;
+  uint32_t mine = 0u;
+  int nmax = 0;
+  for (int j = 0; j < PF_QB; ++j)
+    if (qseq[j] == s) {
+      mine |= 1u << j;
+      nmax = max(nmax, ncand[j]);
+    }
+  sq.s = s;
+  sq.nmax = nmax;
+  sq.mine = mine;
+  sq.done |= mine;
+  return true;
+}
+
+// MULTI: the block's queries may belong to several sequences (one sweep of
+// the key chunk per sequence, queries one at a time: a pair in flight spills
+// registers on top of the sequence loop); otherwise one sequence, queries in
+// branch-free pairs.
+template <bool MULTI>
+__device__ __forceinline__ void prefill_bf16_body(const BatchDev& b, const uint16_t* __restrict__ qI,
+                                                  const float* __restrict__ w, const uint16_t* __restrict__ kI,
+                                                  float* __restrict__ scores, int64_t ld) {
   // Key tile: 32 keys x 16 chunks of 16 B; chunk c of key k sits at slot
   // k*16 + (c ^ (k & 15)) so that the B-operand reads hit distinct banks.
   __shared__ u32x4 ktile[2][PF_TK * 16];
   __shared__ float wl[PF_QB * HI];
   __shared__ int ncand[PF_QB];
+  __shared__ int qseq[PF_QB];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -428,21 +465,15 @@ __global__ __launch_bounds__(PF_THREADS) void idx_prefill_bf16(
   if (tid < PF_QB) {
     const int qi = qg0 + tid;
     ncand[tid] = qi < b.nq ? query_range(b, qi).n : 0;
+    qseq[tid] = qi < b.nq ? b.q_seq[qi] : -1;
   }
   for (int i = tid; i < PF_QB * HI; i += PF_THREADS) {
     const int qi = qg0 + i / HI;
     wl[i] = qi < b.nq ? w[(int64_t)qg0 * HI + i] : 0.0f;
   }
   __syncthreads();
-  int nmax = 0;
-#pragma unroll
-  for (int j = 0; j < PF_QB; ++j) nmax = max(nmax, ncand[j]);
-  const int kend = min(kbase + PF_KC, nmax);
-  if (kbase >= kend) return;
-  const int64_t row0 = b.seq_row0[0];
 
   bf16x8 a[PF_QPW][8];
-  int nj[PF_QPW];
 #pragma unroll
   for (int j = 0; j < PF_QPW; ++j) {
     const int ql = wave * PF_QPW + j;
@@ -450,63 +481,132 @@ __global__ __launch_bounds__(PF_THREADS) void idx_prefill_bf16(
     const uint16_t* qrow = qI + ((int64_t)qc * HI + col) * DI + half * 8;
 #pragma unroll
     for (int t = 0; t < 8; ++t) a[j][t] = as_bf16x8(load16(qrow + t * 16));
-    nj[j] = ncand[ql];
   }
 
-  const int lk = tid >> 4;   // key of the tile this thread stages
-  const int lc = tid & 15;   // its 16-byte chunk
-  const int lslot = lk * 16 + (lc ^ (lk & 15));
-  const uint16_t* kb = kI + row0 * DI + lc * 8;
-  // per query, a buffer resource over exactly its candidate columns: a
-  // store at a column >= n_cand (or from the upper half-wave, which holds no
-  // result) lies outside it and is dropped without a branch
-  __amdgpu_buffer_rsrc_t srs[PF_QPW];
+  if constexpr (!MULTI) {
+    int nmax = 0;
 #pragma unroll
-  for (int j = 0; j < PF_QPW; ++j) {
-    const int n = __builtin_amdgcn_readfirstlane(nj[j]);
-    srs[j] = __builtin_amdgcn_make_buffer_rsrc(scores + (int64_t)(qg0 + wave * PF_QPW + j) * ld, (short)0,
-                                               (int)((uint32_t)n * 4u), 0x00020000);
-  }
-  u32x4 pre = load16_nt(kb + (int64_t)min(kbase + lk, kend - 1) * DI);
-  int buf = 0;
-  for (int k0 = kbase; k0 < kend; k0 += PF_TK) {
-    ktile[buf][lslot] = pre;
-    __syncthreads();
-    if (k0 + PF_TK < kend) pre = load16_nt(kb + (int64_t)min(k0 + PF_TK + lk, kend - 1) * DI);
-    bf16x8 bfr[8];
+    for (int j = 0; j < PF_QB; ++j) nmax = max(nmax, ncand[j]);
+    const int kend = min(kbase + PF_KC, nmax);
+    if (kbase >= kend) return;
+    const int64_t row0 = b.seq_row0[0];
+    int nj[PF_QPW];
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
-      bfr[t] = as_bf16x8(ktile[buf][col * 16 + ((2 * t + half) ^ (col & 15))]);
-    const int soff = half ? (int)0x80000000u : (k0 + col) * 4;
-    // the wave's queries two at a time, branch-free: two independent
-    // product chains, then their ReLU-weighted head sums
+    for (int j = 0; j < PF_QPW; ++j) nj[j] = ncand[wave * PF_QPW + j];
+    const int lk = tid >> 4;   // key of the tile this thread stages
+    const int lc = tid & 15;   // its 16-byte chunk
+    const int lslot = lk * 16 + (lc ^ (lk & 15));
+    const uint16_t* kb = kI + row0 * DI + lc * 8;
+    // per query, a buffer resource over exactly its candidate columns: a
+    // store at a column >= n_cand (or from the upper half-wave, which holds no
+    // result) lies outside it and is dropped without a branch
+    __amdgpu_buffer_rsrc_t srs[PF_QPW];
 #pragma unroll
-    for (int jp = 0; jp < PF_QPW; jp += 2) {
-      f32x16 acc0 = {}, acc1 = {};
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[jp][t], bfr[t], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[jp + 1][t], bfr[t], acc1, 0, 0, 0);
-      }
-      const float* wq0 = wl + (wave * PF_QPW + jp) * HI + 4 * half;
-      const float* wq1 = wq0 + HI;
-      float p0 = 0.0f, p1 = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        p0 = fmaf(wq0[8 * (i >> 2) + (i & 3)], relu(acc0[i]), p0);
-        p1 = fmaf(wq1[8 * (i >> 2) + (i & 3)], relu(acc1[i]), p1);
-      }
-      p0 = halves_sum(p0);
-      p1 = halves_sum(p1);
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, p0), srs[jp], soff, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, p1), srs[jp + 1], soff, 0, 0);
+    for (int j = 0; j < PF_QPW; ++j) {
+      const int n = __builtin_amdgcn_readfirstlane(nj[j]);
+      srs[j] = __builtin_amdgcn_make_buffer_rsrc(scores + (int64_t)(qg0 + wave * PF_QPW + j) * ld, (short)0,
+                                                 (int)((uint32_t)n * 4u), 0x00020000);
     }
-    buf ^= 1;
+    u32x4 pre = load16_nt(kb + (int64_t)min(kbase + lk, kend - 1) * DI);
+    int buf = 0;
+    for (int k0 = kbase; k0 < kend; k0 += PF_TK) {
+      ktile[buf][lslot] = pre;
+      __syncthreads();
+      if (k0 + PF_TK < kend) pre = load16_nt(kb + (int64_t)min(k0 + PF_TK + lk, kend - 1) * DI);
+      bf16x8 bfr[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        bfr[t] = as_bf16x8(ktile[buf][col * 16 + ((2 * t + half) ^ (col & 15))]);
+      const int soff = half ? (int)0x80000000u : (k0 + col) * 4;
+      // the wave's queries two at a time, branch-free: two independent
+      // product chains, then their ReLU-weighted head sums
+#pragma unroll
+      for (int jp = 0; jp < PF_QPW; jp += 2) {
+        f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[jp][t], bfr[t], acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[jp + 1][t], bfr[t], acc1, 0, 0, 0);
+        }
+        const float* wq0 = wl + (wave * PF_QPW + jp) * HI + 4 * half;
+        const float* wq1 = wq0 + HI;
+        float p0 = 0.0f, p1 = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          p0 = fmaf(wq0[8 * (i >> 2) + (i & 3)], relu(acc0[i]), p0);
+          p1 = fmaf(wq1[8 * (i >> 2) + (i & 3)], relu(acc1[i]), p1);
+        }
+        p0 = halves_sum(p0);
+        p1 = halves_sum(p1);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, p0), srs[jp], soff, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, p1), srs[jp + 1], soff, 0, 0);
+      }
+      buf ^= 1;
+    }
+  } else {
+    const int lk = tid >> 4;   // key of the tile this thread stages
+    const int lc = tid & 15;   // its 16-byte chunk
+    const int lslot = lk * 16 + (lc ^ (lk & 15));
+    int buf = 0;
+    // one pass over the key chunk per sequence among the block's queries
+    PfSeq sq{-1, 0, 0u, 0u};
+    while (next_block_sequence(qseq, ncand, sq)) {
+      const int kend = min(kbase + PF_KC, sq.nmax);
+      if (kbase >= kend) continue;
+      const uint16_t* kb = kI + b.seq_row0[sq.s] * DI + lc * 8;
+      // candidates of the wave's queries in this pass (none for a query of
+      // another sequence)
+      int nj[PF_QPW];
+#pragma unroll
+      for (int j = 0; j < PF_QPW; ++j) {
+        const int ql = wave * PF_QPW + j;
+        nj[j] = ((sq.mine >> ql) & 1u) ? ncand[ql] : 0;
+      }
+      u32x4 pre = load16_nt(kb + (int64_t)min(kbase + lk, kend - 1) * DI);
+      for (int k0 = kbase; k0 < kend; k0 += PF_TK) {
+        ktile[buf][lslot] = pre;
+        __syncthreads();
+        if (k0 + PF_TK < kend) pre = load16_nt(kb + (int64_t)min(k0 + PF_TK + lk, kend - 1) * DI);
+        bf16x8 bfr[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          bfr[t] = as_bf16x8(ktile[buf][col * 16 + ((2 * t + half) ^ (col & 15))]);
+#pragma unroll
+        for (int j = 0; j < PF_QPW; ++j) {
+          if (k0 >= nj[j]) continue;
+          f32x16 acc = {};
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j][t], bfr[t], acc, 0, 0, 0);
+          const float* wq = wl + (wave * PF_QPW + j) * HI + 4 * half;
+          float part = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) part = fmaf(wq[8 * (i >> 2) + (i & 3)], relu(acc[i]), part);
+          part = halves_sum(part);
+          const int key = k0 + col;
+          if (half == 0 && key < nj[j]) scores[(int64_t)(qg0 + wave * PF_QPW + j) * ld + key] = part;
+        }
+        buf ^= 1;
+      }
+    }
   }
 }
 
+__global__ __launch_bounds__(PF_THREADS) void idx_prefill_bf16(BatchDev b, const uint16_t* __restrict__ qI,
+                                                               const float* __restrict__ w,
+                                                               const uint16_t* __restrict__ kI,
+                                                               float* __restrict__ scores, int64_t ld) {
+  prefill_bf16_body<false>(b, qI, w, kI, scores, ld);
+}
+__global__ __launch_bounds__(PF_THREADS) void idx_prefill_bf16_multi(BatchDev b, const uint16_t* __restrict__ qI,
+                                                                     const float* __restrict__ w,
+                                                                     const uint16_t* __restrict__ kI,
+                                                                     float* __restrict__ scores, int64_t ld) {
+  prefill_bf16_body<true>(b, qI, w, kI, scores, ld);
+}
+
 // ---------------------------------------------------------------------------
-// prefill, fp8: 32 queries of one sequence per workgroup
+// prefill, fp8: 32 queries per workgroup
 // ---------------------------------------------------------------------------
 // v_mfma_f32_32x32x64_f8f6f4: 32 heads on M, 32 keys on N, two products for
 // the 128-wide contraction.  Lane (col, half) holds 32 operand bytes per
@@ -524,6 +624,7 @@ __global__ __launch_bounds__(PF_THREADS) void idx_prefill_fp8(
   __shared__ u32x4 ktile[2][PF8_TK * 8];
   __shared__ float wl[PF_QB * HI];
   __shared__ int ncand[PF_QB];
+  __shared__ int qseq[PF_QB];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -536,22 +637,16 @@ __global__ __launch_bounds__(PF_THREADS) void idx_prefill_fp8(
   if (tid < PF_QB) {
     const int qi = qg0 + tid;
     ncand[tid] = qi < b.nq ? query_range(b, qi).n : 0;
+    qseq[tid] = qi < b.nq ? b.q_seq[qi] : -1;
   }
   for (int i = tid; i < PF_QB * HI; i += PF_THREADS) {
     const int qi = qg0 + i / HI;
     wl[i] = qi < b.nq ? w[(int64_t)qg0 * HI + i] : 0.0f;
   }
   __syncthreads();
-  int nmax = 0;
-#pragma unroll
-  for (int j = 0; j < PF_QB; ++j) nmax = max(nmax, ncand[j]);
-  const int kend = min(kbase + PF_KC, nmax);
-  if (kbase >= kend) return;
-  const int64_t row0 = b.seq_row0[0];
 
   i32x8 a[PF_QPW][2];
   float wr[PF_QPW][16];
-  int nj[PF_QPW];
 #pragma unroll
   for (int j = 0; j < PF_QPW; ++j) {
     const int ql = wave * PF_QPW + j;
@@ -559,7 +654,6 @@ __global__ __launch_bounds__(PF_THREADS) void idx_prefill_fp8(
     const uint8_t* qrow = qI + ((int64_t)qc * HI + col) * DI + half * 64;
     a[j][0] = cat32(load16(qrow), load16(qrow + 16));
     a[j][1] = cat32(load16(qrow + 32), load16(qrow + 48));
-    nj[j] = ncand[ql];
 #pragma unroll
     for (int i = 0; i < 16; ++i) wr[j][i] = wl[ql * HI + 4 * half + 8 * (i >> 2) + (i & 3)];
   }
@@ -569,56 +663,64 @@ __global__ __launch_bounds__(PF_THREADS) void idx_prefill_fp8(
   const int lk = tid >> 3;   // key of the tile this thread stages (plus r*PF_THREADS/8)
   const int lc = tid & 7;    // its 16-byte chunk
   const int lslot = lk * 8 + (lc ^ ((lk >> 1) & 7));
-  const uint8_t* kb = kI + row0 * DI + lc * 16;
-  u32x4 pre[NR];
-#pragma unroll
-  for (int r = 0; r < NR; ++r) pre[r] = load16_nt(kb + (int64_t)min(kbase + lk + (PF_THREADS / 8) * r, kend - 1) * DI);
-  // one buffer resource per query over exactly its candidate columns: a
-  // store at a column >= n_cand (or from the upper half-wave, which holds no
-  // result) lies outside it and is dropped without a branch
-  __amdgpu_buffer_rsrc_t srs[PF_QPW];
-#pragma unroll
-  for (int j = 0; j < PF_QPW; ++j) {
-    const int n = __builtin_amdgcn_readfirstlane(nj[j]);
-    srs[j] = __builtin_amdgcn_make_buffer_rsrc(scores + (int64_t)(qg0 + wave * PF_QPW + j) * ld, (short)0,
-                                               (int)((uint32_t)n * 4u), 0x00020000);
-  }
   int buf = 0;
-  for (int k0 = kbase; k0 < kend; k0 += TK) {
+  // one pass over the key chunk per sequence among the block's queries
+  PfSeq sq{-1, 0, 0u, 0u};
+  while (next_block_sequence(qseq, ncand, sq)) {
+    const int kend = min(kbase + PF_KC, sq.nmax);
+    if (kbase >= kend) continue;
+    const uint8_t* kb = kI + b.seq_row0[sq.s] * DI + lc * 16;
+    u32x4 pre[NR];
 #pragma unroll
-    for (int r = 0; r < NR; ++r) ktile[buf][lslot + r * PF_THREADS] = pre[r];
-    __syncthreads();
-    // next tile (clamped, so the last iteration re-reads an in-range key)
+    for (int r = 0; r < NR; ++r) pre[r] = load16_nt(kb + (int64_t)min(kbase + lk + (PF_THREADS / 8) * r, kend - 1) * DI);
+    // one buffer resource per query over exactly its candidate columns (none
+    // for a query of another sequence): a store at a column >= n_cand (or
+    // from the upper half-wave, which holds no result) lies outside it and is
+    // dropped without a branch
+    __amdgpu_buffer_rsrc_t srs[PF_QPW];
 #pragma unroll
-    for (int r = 0; r < NR; ++r) pre[r] = load16_nt(kb + (int64_t)min(k0 + TK + lk + (PF_THREADS / 8) * r, kend - 1) * DI);
-    const int nsub = min(TK / 32, (kend - k0 + 31) / 32);
-    for (int sub = 0; sub < nsub; ++sub) {
-      const int kk = sub * 32 + col;
-      const int sw = (kk >> 1) & 7;
-      const u32x4* krow = &ktile[buf][kk * 8];
-      const i32x8 b0 = cat32(krow[(4 * half + 0) ^ sw], krow[(4 * half + 1) ^ sw]);
-      const i32x8 b1 = cat32(krow[(4 * half + 2) ^ sw], krow[(4 * half + 3) ^ sw]);
-      // all queries of the wave, branch-free, so the products of one query
-      // overlap the epilogue of another
-      f32x16 acc[PF_QPW];
-#pragma unroll
-      for (int j = 0; j < PF_QPW; ++j) {
-        const f32x16 z = {};
-        // format 0 = FP8 E4M3 for both operands, no block scaling
-        acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[j][0], b0, z, 0, 0, 0, 0, 0, 0);
-        acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[j][1], b1, acc[j], 0, 0, 0, 0, 0, 0);
-      }
-      const int soff = half ? (int)0x80000000u : (k0 + sub * 32 + col) * 4;
-#pragma unroll
-      for (int j = 0; j < PF_QPW; ++j) {
-        float part = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) part = fmaf(wr[j][i], relu(acc[j][i]), part);
-        part = halves_sum(part);
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, part), srs[j], soff, 0, 0);
-      }
+    for (int j = 0; j < PF_QPW; ++j) {
+      const int ql = wave * PF_QPW + j;
+      const int n = __builtin_amdgcn_readfirstlane(((sq.mine >> ql) & 1u) ? ncand[ql] : 0);
+      srs[j] = __builtin_amdgcn_make_buffer_rsrc(scores + (int64_t)(qg0 + ql) * ld, (short)0,
+                                                 (int)((uint32_t)n * 4u), 0x00020000);
     }
-    buf ^= 1;
+    for (int k0 = kbase; k0 < kend; k0 += TK) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) ktile[buf][lslot + r * PF_THREADS] = pre[r];
+      __syncthreads();
+      // next tile (clamped, so the last iteration re-reads an in-range key)
+#pragma unroll
+      for (int r = 0; r < NR; ++r) pre[r] = load16_nt(kb + (int64_t)min(k0 + TK + lk + (PF_THREADS / 8) * r, kend - 1) * DI);
+      const int nsub = min(TK / 32, (kend - k0 + 31) / 32);
+      for (int sub = 0; sub < nsub; ++sub) {
+        const int kk = sub * 32 + col;
+        const int sw = (kk >> 1) & 7;
+        const u32x4* krow = &ktile[buf][kk * 8];
+        const i32x8 b0 = cat32(krow[(4 * half + 0) ^ sw], krow[(4 * half + 1) ^ sw]);
+        const i32x8 b1 = cat32(krow[(4 * half + 2) ^ sw], krow[(4 * half + 3) ^ sw]);
+        // all queries of the wave, branch-free, so the products of one query
+        // overlap the epilogue of another
+        f32x16 acc[PF_QPW];
+#pragma unroll
+        for (int j = 0; j < PF_QPW; ++j) {
+          const f32x16 z = {};
+          // format 0 = FP8 E4M3 for both operands, no block scaling
+          acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[j][0], b0, z, 0, 0, 0, 0, 0, 0);
+          acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[j][1], b1, acc[j], 0, 0, 0, 0, 0, 0);
+        }
+        const int soff = half ? (int)0x80000000u : (k0 + sub * 32 + col) * 4;
+#pragma unroll
+        for (int j = 0; j < PF_QPW; ++j) {
+          float part = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) part = fmaf(wr[j][i], relu(acc[j][i]), part);
+          part = halves_sum(part);
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, part), srs[j], soff, 0, 0);
+        }
+      }
+      buf ^= 1;
+    }
   }
 }
 
@@ -652,15 +754,21 @@ hipError_t launch_index_score(const BatchDev& b, int dtype, const void* qI, cons
     dim3 grid((b.max_len + IDX_F32_THREADS - 1) / IDX_F32_THREADS, b.nq);
     hipLaunchKernelGGL(idx_decode_f32, grid, dim3(IDX_F32_THREADS), 0, st, b, (const float*)qI, w,
                        (const float*)kI, scores, ld, z);
-  } else if (b.nseq == 1 && b.nq >= PF_QB) {
+  } else if (b.nq >= PF_QB && (int64_t)b.nq >= (int64_t)PF_QB * b.nseq) {
+    // at least a block's worth of queries per sequence on average: a
+    // sequence's queries are best contiguous in the batch, so that blocks
+    // rarely straddle sequences
     hipError_t e = launch_zero(z, b.nq, st);
     if (e != hipSuccess) return e;
     dim3 grid((b.max_len + PF_KC - 1) / PF_KC, (b.nq + PF_QB - 1) / PF_QB);
     if (dtype == 2)
       hipLaunchKernelGGL(idx_prefill_fp8, grid, dim3(PF_THREADS), 0, st, b, (const uint8_t*)qI, w,
                          (const uint8_t*)kI, scores, ld);
-    else
+    else if (b.nseq == 1)
       hipLaunchKernelGGL(idx_prefill_bf16, grid, dim3(PF_THREADS), 0, st, b, (const uint16_t*)qI, w,
+                         (const uint16_t*)kI, scores, ld);
+    else
+      hipLaunchKernelGGL(idx_prefill_bf16_multi, grid, dim3(PF_THREADS), 0, st, b, (const uint16_t*)qI, w,
                          (const uint16_t*)kI, scores, ld);
   } else if (b.nq <= IDX_BAL_MAXQ) {
     if (dtype == 2)

@@ -105,6 +105,47 @@ def test_index_score_prefill_exact(B, cache, first, nq, idt):
         assert np.all(np.isnan(sc[qi, n:]))
 
 
+@pytest.mark.parametrize("idt", ["bf16", "fp8"])
+@pytest.mark.parametrize("order", ["grouped", "interleaved"])
+def test_index_score_prefill_several_sequences(B, idt, order):
+    """A prefill batch over three sequences (50, 100 and 40 queries at the
+    ends of 5,000-, 9,000- and 3,000-position caches) takes the blocked
+    prefill kernels: grouped, the 32-query blocks straddle sequence
+    boundaries; interleaved, every block holds queries of all three, and the
+    key chunk is swept once per sequence.  Every score exact, columns past a
+    query's candidates untouched."""
+    rng = np.random.default_rng(47)
+    lens = np.array([5000, 9000, 3000], np.int32)
+    counts = [50, 100, 40]
+    row0 = np.concatenate([[0], np.cumsum(lens[:-1])]).astype(np.int64)
+    q_seq = np.concatenate([np.full(c, s, np.int32) for s, c in enumerate(counts)])
+    q_pos = np.concatenate([np.arange(lens[s] - c, lens[s], dtype=np.int32) for s, c in enumerate(counts)])
+    if order == "interleaved":
+        starts = np.concatenate([[0], np.cumsum(counts)[:-1]])
+        perm = [starts[s] + k for k in range(max(counts)) for s in range(3) if k < counts[s]]
+        q_seq, q_pos = q_seq[perm], q_pos[perm]
+    nq = len(q_seq)
+    qI_i = rng.integers(-3, 4, size=(nq, 32, 128), dtype=np.int8)
+    kI_i = rng.integers(-3, 4, size=(int(lens.sum()), 128), dtype=np.int8)
+    w_ = rng.integers(1, 5, size=(nq, 32)).astype(np.float32)
+    qI = wl._small_int_bits(qI_i, idt)
+    kI = wl._small_int_bits(kI_i, idt)
+    batch = B.Batch(torch.from_numpy(q_seq).to(DEV), torch.from_numpy(q_pos).to(DEV),
+                    torch.from_numpy(lens).to(DEV), torch.from_numpy(row0).to(DEV), int(lens.max()))
+    scores = torch.full((nq, int(lens.max())), float("nan"), device=DEV)
+    dev = lambda a: torch.from_numpy(a).to(DEV).view(torch.bfloat16) if a.dtype == np.uint16 else \
+        torch.from_numpy(a).to(DEV)
+    B.dsa_index_score(batch, dev(qI), torch.from_numpy(w_).to(DEV), dev(kI), scores)
+    torch.cuda.synchronize()
+    sc = scores.cpu().numpy()
+    for qi in range(nq):
+        s, n = int(q_seq[qi]), int(q_pos[qi]) + 1
+        keys = kI_i[row0[s]: row0[s] + n].astype(np.float32)
+        ref = oracle.index_score(qI_i[qi].astype(np.float32), w_[qi], keys)
+        assert np.array_equal(sc[qi, :n].astype(np.float64), ref), f"query {qi} (sequence {s})"
+        assert np.all(np.isnan(sc[qi, n:]))
+
+
 FINITE_E4M3 = np.array([b for b in range(256) if (b & 0x7F) != 0x7F], np.uint8)
 
 
