@@ -108,8 +108,9 @@ typedef enum { DSA_F32 = 0, DSA_BF16 = 1, DSA_FP8_E4M3 = 2 } dsa_dtype_t;
  * The candidates of query q are positions s in [0, n_cand(q)) with
  *   n_cand(q) = min(q_pos[q] + 1, seq_len[q_seq[q]], max_len)
  * (its own position and every earlier one; "Sparse attention" section).
- * Decode is nq = nseq with q_pos = seq_len - 1; a prefill chunk is nq
- * queries of one sequence at increasing positions (causal).
+ * Decode is nq = nseq with q_pos = seq_len - 1; a prefill chunk is many
+ * queries of a sequence at increasing positions (causal), and a prefill
+ * batch may hold chunks of several sequences.
  * Out-of-range device values are clamped so that no access leaves
  * [seq_row0, seq_row0 + n_cand); the results are then undefined.
  */
@@ -138,9 +139,10 @@ const char* dsa_last_error(void);
  *   scores [nq][ld]      float32    column s < n_cand(q) receives I[q][s];
  *                                   columns >= n_cand(q) are left untouched.
  *   ld >= max_len.
- * Decode batches stream the keys once per query; batches of one sequence
- * with many queries (prefill) run as a blocked matrix product that shares
- * each key tile across 32 queries.
+ * Decode batches stream the keys once per query; batches with many queries
+ * per sequence (prefill; on average at least 32) run as a blocked matrix
+ * product that shares each key tile across the queries of a 32-query block
+ * that belong to its sequence, so a sequence's queries are best contiguous.
  */
 int32_t dsa_index_score(const dsa_batch_t* batch, int32_t dtype, const void* q_idx,
                         const float* w_idx, const void* k_idx, float* scores, int64_t ld,

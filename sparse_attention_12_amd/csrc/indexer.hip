@@ -465,7 +465,8 @@ __device__ __forceinline__ void prefill_bf16_body(const BatchDev& b, const uint1
   if (tid < PF_QB) {
     const int qi = qg0 + tid;
     ncand[tid] = qi < b.nq ? query_range(b, qi).n : 0;
-    qseq[tid] = qi < b.nq ? b.q_seq[qi] : -1;
+    const int sq_i = qi < b.nq ? b.q_seq[qi] : -1;
+    qseq[tid] = (sq_i >= 0 && sq_i < b.nseq) ? sq_i : -1;  // out of range: no candidates, like padding
   }
   for (int i = tid; i < PF_QB * HI; i += PF_THREADS) {
     const int qi = qg0 + i / HI;
@@ -637,7 +638,8 @@ __global__ __launch_bounds__(PF_THREADS) void idx_prefill_fp8(
   if (tid < PF_QB) {
     const int qi = qg0 + tid;
     ncand[tid] = qi < b.nq ? query_range(b, qi).n : 0;
-    qseq[tid] = qi < b.nq ? b.q_seq[qi] : -1;
+    const int sq_i = qi < b.nq ? b.q_seq[qi] : -1;
+    qseq[tid] = (sq_i >= 0 && sq_i < b.nseq) ? sq_i : -1;  // out of range: no candidates, like padding
   }
   for (int i = tid; i < PF_QB * HI; i += PF_THREADS) {
     const int qi = qg0 + i / HI;

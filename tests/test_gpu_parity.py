@@ -124,6 +124,8 @@ def test_index_score_prefill_several_sequences(B, idt, order):
         starts = np.concatenate([[0], np.cumsum(counts)[:-1]])
         perm = [starts[s] + k for k in range(max(counts)) for s in range(3) if k < counts[s]]
         q_seq, q_pos = q_seq[perm], q_pos[perm]
+    else:
+        q_seq[-1] = 3          # no such sequence: no candidates, its row untouched
     nq = len(q_seq)
     qI_i = rng.integers(-3, 4, size=(nq, 32, 128), dtype=np.int8)
     kI_i = rng.integers(-3, 4, size=(int(lens.sum()), 128), dtype=np.int8)
@@ -140,6 +142,9 @@ def test_index_score_prefill_several_sequences(B, idt, order):
     sc = scores.cpu().numpy()
     for qi in range(nq):
         s, n = int(q_seq[qi]), int(q_pos[qi]) + 1
+        if s >= len(lens):
+            assert np.all(np.isnan(sc[qi])), f"query {qi} of no sequence"
+            continue
         keys = kI_i[row0[s]: row0[s] + n].astype(np.float32)
         ref = oracle.index_score(qI_i[qi].astype(np.float32), w_[qi], keys)
         assert np.array_equal(sc[qi, :n].astype(np.float64), ref), f"query {qi} (sequence {s})"
