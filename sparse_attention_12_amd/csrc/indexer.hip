@@ -389,7 +389,9 @@ constexpr int PF_WAVES = PF_THREADS / 64;
 constexpr int PF_QPW = 4;                    // queries per wave
 constexpr int PF_QB = PF_WAVES * PF_QPW;     // queries per workgroup
 constexpr int PF_TK = 32;                    // keys per LDS tile
-constexpr int PF_KC = 8192;                  // keys per workgroup
+constexpr int PF_KC = 8192;                  // keys per workgroup (at most)
+constexpr int PF_KC_MIN = 1024;              // shortest key chunk (a power of two below PF_KC)
+constexpr int PF_MIN_GRID = 512;             // workgroups the chunk length aims for
 
 // (key chunk, query block) of a prefill workgroup.  Workgroups go to the 8
 // XCDs round-robin in launch order (linear id L -> XCD L % 8), each XCD with
@@ -446,7 +448,7 @@ __device__ inline bool next_block_sequence(const int* qseq, const int* ncand, Pf
 template <bool MULTI>
 __device__ __forceinline__ void prefill_bf16_body(const BatchDev& b, const uint16_t* __restrict__ qI,
                                                   const float* __restrict__ w, const uint16_t* __restrict__ kI,
-                                                  float* __restrict__ scores, int64_t ld) {
+                                                  float* __restrict__ scores, int64_t ld, int kc) {
   // Key tile: 32 keys x 16 chunks of 16 B; chunk c of key k sits at slot
   // k*16 + (c ^ (k & 15)) so that the B-operand reads hit distinct banks.
   __shared__ u32x4 ktile[2][PF_TK * 16];
@@ -460,7 +462,7 @@ __device__ __forceinline__ void prefill_bf16_body(const BatchDev& b, const uint1
   const int half = lane >> 5;
   const PfTile tile = prefill_tile();
   const int qg0 = tile.qblock * PF_QB;
-  const int kbase = tile.chunk * PF_KC;
+  const int kbase = tile.chunk * kc;
 
   if (tid < PF_QB) {
     const int qi = qg0 + tid;
@@ -488,7 +490,7 @@ __device__ __forceinline__ void prefill_bf16_body(const BatchDev& b, const uint1
     int nmax = 0;
 #pragma unroll
     for (int j = 0; j < PF_QB; ++j) nmax = max(nmax, ncand[j]);
-    const int kend = min(kbase + PF_KC, nmax);
+    const int kend = min(kbase + kc, nmax);
     if (kbase >= kend) return;
     const int64_t row0 = b.seq_row0[0];
     int nj[PF_QPW];
@@ -552,7 +554,7 @@ __device__ __forceinline__ void prefill_bf16_body(const BatchDev& b, const uint1
     // one pass over the key chunk per sequence among the block's queries
     PfSeq sq{-1, 0, 0u, 0u};
     while (next_block_sequence(qseq, ncand, sq)) {
-      const int kend = min(kbase + PF_KC, sq.nmax);
+      const int kend = min(kbase + kc, sq.nmax);
       if (kbase >= kend) continue;
       const uint16_t* kb = kI + b.seq_row0[sq.s] * DI + lc * 8;
       // candidates of the wave's queries in this pass (none for a query of
@@ -596,14 +598,14 @@ __device__ __forceinline__ void prefill_bf16_body(const BatchDev& b, const uint1
 __global__ __launch_bounds__(PF_THREADS) void idx_prefill_bf16(BatchDev b, const uint16_t* __restrict__ qI,
                                                                const float* __restrict__ w,
                                                                const uint16_t* __restrict__ kI,
-                                                               float* __restrict__ scores, int64_t ld) {
-  prefill_bf16_body<false>(b, qI, w, kI, scores, ld);
+                                                               float* __restrict__ scores, int64_t ld, int kc) {
+  prefill_bf16_body<false>(b, qI, w, kI, scores, ld, kc);
 }
 __global__ __launch_bounds__(PF_THREADS) void idx_prefill_bf16_multi(BatchDev b, const uint16_t* __restrict__ qI,
                                                                      const float* __restrict__ w,
                                                                      const uint16_t* __restrict__ kI,
-                                                                     float* __restrict__ scores, int64_t ld) {
-  prefill_bf16_body<true>(b, qI, w, kI, scores, ld);
+                                                                     float* __restrict__ scores, int64_t ld, int kc) {
+  prefill_bf16_body<true>(b, qI, w, kI, scores, ld, kc);
 }
 
 // ---------------------------------------------------------------------------
@@ -616,9 +618,13 @@ __global__ __launch_bounds__(PF_THREADS) void idx_prefill_bf16_multi(BatchDev b,
 // query and key, so each lane reads 64 contiguous bytes of one key.
 constexpr int PF8_TK = 256;  // keys per LDS tile (eight 32-key products)
 
+// KC: keys per workgroup, a compile-time constant (this kernel uses every
+// register, and a run-time chunk length costs it spills)
+template <int KC>
 __global__ __launch_bounds__(PF_THREADS) void idx_prefill_fp8(
     BatchDev b, const uint8_t* __restrict__ qI, const float* __restrict__ w,
     const uint8_t* __restrict__ kI, float* __restrict__ scores, int64_t ld) {
+  constexpr int kc = KC;
   // Key tile: 256 keys x 8 chunks of 16 B; chunk c of key k sits at slot
   // k*8 + (c ^ ((k >> 1) & 7)), so the 16 keys a quarter-wave reads fall on
   // 16 distinct 16-byte bank groups.
@@ -633,7 +639,7 @@ __global__ __launch_bounds__(PF_THREADS) void idx_prefill_fp8(
   const int half = lane >> 5;
   const PfTile tile = prefill_tile();
   const int qg0 = tile.qblock * PF_QB;
-  const int kbase = tile.chunk * PF_KC;
+  const int kbase = tile.chunk * kc;
 
   if (tid < PF_QB) {
     const int qi = qg0 + tid;
@@ -669,7 +675,7 @@ __global__ __launch_bounds__(PF_THREADS) void idx_prefill_fp8(
   // one pass over the key chunk per sequence among the block's queries
   PfSeq sq{-1, 0, 0u, 0u};
   while (next_block_sequence(qseq, ncand, sq)) {
-    const int kend = min(kbase + PF_KC, sq.nmax);
+    const int kend = min(kbase + kc, sq.nmax);
     if (kbase >= kend) continue;
     const uint8_t* kb = kI + b.seq_row0[sq.s] * DI + lc * 16;
     u32x4 pre[NR];
@@ -762,16 +768,29 @@ hipError_t launch_index_score(const BatchDev& b, int dtype, const void* qI, cons
     // rarely straddle sequences
     hipError_t e = launch_zero(z, b.nq, st);
     if (e != hipSuccess) return e;
-    dim3 grid((b.max_len + PF_KC - 1) / PF_KC, (b.nq + PF_QB - 1) / PF_QB);
-    if (dtype == 2)
-      hipLaunchKernelGGL(idx_prefill_fp8, grid, dim3(PF_THREADS), 0, st, b, (const uint8_t*)qI, w,
-                         (const uint8_t*)kI, scores, ld);
-    else if (b.nseq == 1)
+    // key chunks of PF_KC, halved (to PF_KC_MIN at the shortest) while the
+    // grid has fewer than PF_MIN_GRID workgroups (few, short sequences)
+    const int nqb = (b.nq + PF_QB - 1) / PF_QB;
+    int kc = PF_KC;
+    while (kc > PF_KC_MIN && (int64_t)((b.max_len + kc - 1) / kc) * nqb < PF_MIN_GRID) kc >>= 1;
+    dim3 grid((b.max_len + kc - 1) / kc, nqb);
+    if (dtype == 2) {
+      const uint8_t* q8 = (const uint8_t*)qI;
+      const uint8_t* k8 = (const uint8_t*)kI;
+      if (kc == 8192)
+        hipLaunchKernelGGL(idx_prefill_fp8<8192>, grid, dim3(PF_THREADS), 0, st, b, q8, w, k8, scores, ld);
+      else if (kc == 4096)
+        hipLaunchKernelGGL(idx_prefill_fp8<4096>, grid, dim3(PF_THREADS), 0, st, b, q8, w, k8, scores, ld);
+      else if (kc == 2048)
+        hipLaunchKernelGGL(idx_prefill_fp8<2048>, grid, dim3(PF_THREADS), 0, st, b, q8, w, k8, scores, ld);
+      else
+        hipLaunchKernelGGL(idx_prefill_fp8<1024>, grid, dim3(PF_THREADS), 0, st, b, q8, w, k8, scores, ld);
+    } else if (b.nseq == 1)
       hipLaunchKernelGGL(idx_prefill_bf16, grid, dim3(PF_THREADS), 0, st, b, (const uint16_t*)qI, w,
-                         (const uint16_t*)kI, scores, ld);
+                         (const uint16_t*)kI, scores, ld, kc);
     else
       hipLaunchKernelGGL(idx_prefill_bf16_multi, grid, dim3(PF_THREADS), 0, st, b, (const uint16_t*)qI, w,
-                         (const uint16_t*)kI, scores, ld);
+                         (const uint16_t*)kI, scores, ld, kc);
   } else if (b.nq <= IDX_BAL_MAXQ) {
     if (dtype == 2)
       hipLaunchKernelGGL(idx_decode_fp8_bal, dim3(IDX_BAL_GRID), dim3(IDX_DEC_THREADS), 0, st, b, qI, w, kI,
