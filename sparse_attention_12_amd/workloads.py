@@ -5,7 +5,9 @@ them in the requested precision and lays sequences out in the caches.  Both
 the HIP path (tests, bench) and the CPU oracle (tests, bench CPU leg) take
 their inputs from here.
 
-Recipe (one ``numpy.random.default_rng(seed)`` stream, drawn in this order):
+Recipe.  A workload's draws come from one ``Draws`` stream seeded with the
+workload's seed: every array takes the next child of a
+``numpy.random.SeedSequence``, in this order:
   1. context lengths (ragged decode only),
   2. indexer queries qI [nq,32,128]: integers uniform in {-3..3},
   3. indexer head weights w [nq,32]: integers uniform in {1..4} (float32),
@@ -14,16 +16,20 @@ Recipe (one ``numpy.random.default_rng(seed)`` stream, drawn in this order):
   6. per layer: cache rows kv [rows,576] ~ N(0,1) (512 latent then 64 rotary;
      with ``split_kv`` the latent block [rows,512] is drawn before the rotary
      block [rows,64] and the two are concatenated).
-Normal draws are float32 and are rounded once to bf16 (round to nearest even)
-when the workload is bf16; integer draws are exact in either precision and
-also in FP8 E4M3, in which the indexer's qI and kI may be stored
-(``index_dtype="fp8"``, as uint8 bit patterns).  Decode queries sit at the
-last position of their sequence.
+An array is drawn in blocks of 2^22 elements, block b from the b-th child of
+the array's seed, on a pool of threads; the values do not depend on the
+number of threads.  Normal draws are float32 and are rounded once to bf16
+(round to nearest even) when the workload is bf16; integer draws are exact in
+either precision and also in FP8 E4M3, in which the indexer's qI and kI may
+be stored (``index_dtype="fp8"``, as uint8 bit patterns).  Decode queries sit
+at the last position of their sequence.
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import dataclasses
 import math
+import os
 from typing import List, Optional
 
 import numpy as np
@@ -120,16 +126,58 @@ def _small_int_bits(values: np.ndarray, dtype: str) -> np.ndarray:
     return lut[values.astype(np.int16) + 128]
 
 
-def _normal(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
-    n = int(np.prod(shape))
-    if dtype == "f32":
-        return rng.standard_normal(n, dtype=np.float32).reshape(shape)
-    out = np.empty(n, np.uint16)
-    step = 1 << 24
-    for s in range(0, n, step):
-        m = min(step, n - s)
-        out[s:s + m] = f32_to_bf16_bits(rng.standard_normal(m, dtype=np.float32))
-    return out.reshape(shape)
+# --------------------------------------------------------------------------
+# seeded draws
+# --------------------------------------------------------------------------
+
+BLOCK = 1 << 22
+_POOL = None
+
+
+def _pool() -> cf.ThreadPoolExecutor:
+    global _POOL
+    if _POOL is None:
+        _POOL = cf.ThreadPoolExecutor(max_workers=max(1, min(16, os.cpu_count() or 1)))
+    return _POOL
+
+
+class Draws:
+    """A seeded stream of arrays.  Each call takes the next child of the
+    stream's SeedSequence; the array is filled in blocks of BLOCK elements,
+    block b from the b-th child of that seed, in parallel."""
+
+    def __init__(self, seed: int):
+        self._ss = np.random.SeedSequence(int(seed))
+
+    def _fill(self, n: int, out: np.ndarray, draw) -> None:
+        seeds = self._ss.spawn(1)[0].spawn(max(1, -(-n // BLOCK)))
+
+        def one(b):
+            lo = b * BLOCK
+            hi = min(n, lo + BLOCK)
+            if hi > lo:
+                draw(np.random.default_rng(seeds[b]), out[lo:hi])
+
+        list(_pool().map(one, range(len(seeds))))
+
+    def integers(self, lo: int, hi: int, shape, dtype=np.int8) -> np.ndarray:
+        """Integers uniform in [lo, hi) (int8 unless dtype says otherwise)."""
+        n = int(np.prod(shape))
+        out = np.empty(n, dtype)
+        self._fill(n, out, lambda g, o: o.__setitem__(slice(None), g.integers(lo, hi, size=o.size, dtype=dtype)))
+        return out.reshape(shape)
+
+    def normal(self, shape, dtype: str) -> np.ndarray:
+        """N(0,1) float32 draws; for dtype "bf16" rounded once to bf16 bits."""
+        n = int(np.prod(shape))
+        if dtype == "f32":
+            out = np.empty(n, np.float32)
+            self._fill(n, out, lambda g, o: g.standard_normal(size=o.size, dtype=np.float32, out=o))
+        else:
+            out = np.empty(n, np.uint16)
+            self._fill(n, out, lambda g, o: o.__setitem__(
+                slice(None), f32_to_bf16_bits(g.standard_normal(size=o.size, dtype=np.float32))))
+        return out.reshape(shape)
 
 
 # --------------------------------------------------------------------------
@@ -217,29 +265,29 @@ def _layout(lens: np.ndarray):
 
 def make_decode(lens, dtype: str = "bf16", n_layers: int = 1, seed: int = 0,
                 name: Optional[str] = None, split_kv: bool = False,
-                rng: Optional[np.random.Generator] = None,
+                draws: Optional[Draws] = None,
                 index_dtype: Optional[str] = None, rope_dim: int = DR) -> Workload:
     """Decode batch: one query per sequence, at its last position.  With
     rope_dim=0 the layers have no rotary part: q [nq,64,512], kv [rows,512]."""
-    rng = rng if rng is not None else np.random.default_rng(seed)
+    dr = draws if draws is not None else Draws(seed)
     idt = index_dtype or dtype
     lens = np.asarray(lens, np.int32)
     nq = len(lens)
     row0, rows = _layout(lens)
-    qI = _small_int_bits(rng.integers(-3, 4, size=(nq, HI, DI), dtype=np.int8), idt)
-    w = rng.integers(1, 5, size=(nq, HI), dtype=np.int8).astype(np.float32)
-    kI = _small_int_bits(rng.integers(-3, 4, size=(rows, DI), dtype=np.int8), idt)
+    qI = _small_int_bits(dr.integers(-3, 4, (nq, HI, DI)), idt)
+    w = dr.integers(1, 5, (nq, HI)).astype(np.float32)
+    kI = _small_int_bits(dr.integers(-3, 4, (rows, DI)), idt)
     width = DC + rope_dim
     qs, kvs = [], []
     for _ in range(n_layers):
-        qs.append(_normal(rng, (nq, H, width), dtype))
+        qs.append(dr.normal((nq, H, width), dtype))
     for _ in range(n_layers):
         if split_kv and rope_dim:
-            lat = _normal(rng, (rows, DC), dtype)
-            rot = _normal(rng, (rows, rope_dim), dtype)
+            lat = dr.normal((rows, DC), dtype)
+            rot = dr.normal((rows, rope_dim), dtype)
             kvs.append(np.ascontiguousarray(np.concatenate([lat, rot], axis=1)))
         else:
-            kvs.append(_normal(rng, (rows, width), dtype))
+            kvs.append(dr.normal((rows, width), dtype))
     return Workload(
         name=name or f"decode_b{nq}_{dtype}", kind="decode", dtype=dtype, n_layers=n_layers,
         seq_len=lens, seq_row0=row0, q_seq=np.arange(nq, dtype=np.int32),
@@ -251,15 +299,15 @@ def make_prefill(cache_len: int, first_pos: int, nq: int, dtype: str = "bf16",
                  seed: int = 0, name: Optional[str] = None,
                  index_dtype: Optional[str] = None) -> Workload:
     """Causal prefill chunk: nq consecutive queries of one sequence."""
-    rng = np.random.default_rng(seed)
+    dr = Draws(seed)
     idt = index_dtype or dtype
     lens = np.asarray([cache_len], np.int32)
     row0, rows = _layout(lens)
-    qI = _small_int_bits(rng.integers(-3, 4, size=(nq, HI, DI), dtype=np.int8), idt)
-    w = rng.integers(1, 5, size=(nq, HI), dtype=np.int8).astype(np.float32)
-    kI = _small_int_bits(rng.integers(-3, 4, size=(rows, DI), dtype=np.int8), idt)
-    q = _normal(rng, (nq, H, D), dtype)
-    kv = _normal(rng, (rows, D), dtype)
+    qI = _small_int_bits(dr.integers(-3, 4, (nq, HI, DI)), idt)
+    w = dr.integers(1, 5, (nq, HI)).astype(np.float32)
+    kI = _small_int_bits(dr.integers(-3, 4, (rows, DI)), idt)
+    q = dr.normal((nq, H, D), dtype)
+    kv = dr.normal((rows, D), dtype)
     return Workload(
         name=name or f"prefill_{nq}q_{dtype}", kind="prefill", dtype=dtype, n_layers=1,
         seq_len=lens, seq_row0=row0, q_seq=np.zeros(nq, np.int32),
@@ -301,27 +349,27 @@ def make_layer_stack(lens, plan, dtype: str = "bf16", seed: int = 0,
     """Decode batch over the layers of `plan`: per layer, in layer order,
     the indexer inputs (qI, w, kI) if it runs its indexer, its query (512 +
     64 wide, or 512 without rotary part), its cache if it owns one."""
-    rng = np.random.default_rng(seed)
+    dr = Draws(seed)
     idt = index_dtype or dtype
-    base = make_decode(lens, dtype, 0, seed, "layer_stack", rng=np.random.default_rng(seed + 1), index_dtype=idt)
+    base = make_decode(lens, dtype, 0, seed, "layer_stack", draws=Draws(seed + 1), index_dtype=idt)
     nq, rows = base.nq, base.rows
     qI, w, kI, q, kv = [], [], [], [], []
     for l, (runs, rope, src) in enumerate(plan):
         width = DC + (DR if rope else 0)
         if runs:
-            qI.append(_small_int_bits(rng.integers(-3, 4, size=(nq, HI, DI), dtype=np.int8), idt))
-            w.append(rng.integers(1, 5, size=(nq, HI), dtype=np.int8).astype(np.float32))
-            kI.append(_small_int_bits(rng.integers(-3, 4, size=(rows, DI), dtype=np.int8), idt))
+            qI.append(_small_int_bits(dr.integers(-3, 4, (nq, HI, DI)), idt))
+            w.append(dr.integers(1, 5, (nq, HI)).astype(np.float32))
+            kI.append(_small_int_bits(dr.integers(-3, 4, (rows, DI)), idt))
         else:
             qI.append(None)
             w.append(None)
             kI.append(None)
-        q.append(_normal(rng, (nq, H, width), dtype))
-        kv.append(_normal(rng, (rows, width), dtype) if src == l else None)
+        q.append(dr.normal((nq, H, width), dtype))
+        kv.append(dr.normal((rows, width), dtype) if src == l else None)
     return LayerStack(base=base, plan=list(plan), qI=qI, w=w, kI=kI, q=q, kv=kv)
 
 
-def ragged_lengths(rng: np.random.Generator, b: int, lo: int, hi: int, forced=(1024, 2048, 2049)):
+def ragged_lengths(draws: Draws, b: int, lo: int, hi: int, forced=(1024, 2048, 2049)):
     """Context lengths for the ragged decode batch.
 
     The first entries are forced to sit at, just below and just above the
@@ -329,7 +377,7 @@ def ragged_lengths(rng: np.random.Generator, b: int, lo: int, hi: int, forced=(1
     present); the rest are uniform integers in [lo, hi].
     """
     forced = [int(x) for x in forced][:b]
-    rest = rng.integers(lo, hi + 1, size=b - len(forced)).astype(np.int32)
+    rest = draws.integers(lo, hi + 1, (b - len(forced),), np.int32)
     return np.concatenate([np.asarray(forced, np.int32), rest])
 
 
@@ -358,9 +406,9 @@ def config(i: int, index_dtype: Optional[str] = None) -> Workload:
     if i == 1:
         return make_decode([32768] * 64, "bf16", 1, seed, name, index_dtype=index_dtype)
     if i == 2:
-        rng = np.random.default_rng(seed)
-        lens = ragged_lengths(rng, 16, 1024, 131072)
-        return make_decode(lens, "bf16", 4, seed, name, rng=rng, index_dtype=index_dtype)
+        dr = Draws(seed)
+        lens = ragged_lengths(dr, 16, 1024, 131072)
+        return make_decode(lens, "bf16", 4, seed, name, draws=dr, index_dtype=index_dtype)
     if i == 3:
         return make_prefill(65536, 63488, 2048, "bf16", seed, name, index_dtype=index_dtype)
     if i == 4:
