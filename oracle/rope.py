@@ -6,21 +6,24 @@ TEST INFRASTRUCTURE ONLY (same rule as the rest of this package): only the
 tests, the smoke check and the benchmark's CPU leg may call it.
 
 Sources ("Mistral Large 4" concept page, sections "Positions" and "Query
-scaling", and its executable example's YaRN wavelength function):
+scaling"):
   * pair i < 32 of the 64-value rotary part rotates at omega_i = 10000^(-2i/64);
-  * YaRN, original window 512, factor 2,048: pairs that complete at least 32
-    turns within the window keep omega_i, pairs that complete less than one
-    get omega_i / 2,048, and the pairs in between blend linearly in the pair
-    index, between the rounded-down index where a pair completes 32 turns
-    and the rounded-up index where it completes one (as the page's example
-    computes it);
+  * YaRN, original window 512, factor 2,048: a pair that turns at least 32
+    times within the window keeps omega_i, a pair that turns less than once
+    there gets omega_i / 2,048, and the pairs in between move linearly from
+    one to the other.  Reading of "linearly": linear in the pair index,
+    from the last pair that is kept (weight 0 on the divided frequency) to
+    the first pair that is divided (weight 1); the page's own worked numbers
+    (pair 3 turns in under 16 positions, pair 16 in over 2^20) pin both ends;
   * LeRoPE multiplies frequency i by a learned e^{alpha_i};
   * query scaling: each head multiplies its query by a learned function of
-    position.  The formula was lost in extraction.  Reading taken here (parity
-    unpinned): m_h(t) = s_h * ln(t + 1) + b_h at 0-based position t, i.e. a
-    learned affine function of the log of the number of visible positions,
-    after the Scalable-Softmax idea the section describes (logits times
-    c ln n).
+    position.  The formula was lost in extraction; the section's argument
+    fixes its form: with the logits multiplied by c ln n over n visible
+    positions, a key leading n - 1 competitors by Delta keeps the weight
+    1/(1 + (n - 1) n^(-c Delta)).  Reading taken: m_h(t) = s_h ln(t + 1) + b_h
+    at 0-based position t (n = t + 1 visible positions); the ln(t + 1) term is
+    pinned by that identity (tests/test_oracle_rope.py), the learned offset
+    b_h is the part that remains a reading.
 Readings for what the pages leave open: dimension pair i is (2i, 2i+1) of
 the rotary part; a position rotates by the angle t * omega''_i; the scaling
 multiplies the whole attention query (latent-space and rotary parts).  All
@@ -36,8 +39,8 @@ ROPE_DIMS = 64
 THETA = 10000.0
 WINDOW = 512
 FACTOR = 2048.0
-BETA_FAST = 32.0
-BETA_SLOW = 1.0
+TURNS_KEPT = 32.0      # pairs turning at least this often within the window keep their frequency
+TURNS_DIVIDED = 1.0    # pairs turning less often than this are divided by FACTOR
 
 
 def base_frequencies() -> np.ndarray:
@@ -46,21 +49,30 @@ def base_frequencies() -> np.ndarray:
     return THETA ** (-2.0 * i / ROPE_DIMS)
 
 
-def _pair_completing(turns: float) -> float:
-    """Fractional pair index whose rotation completes `turns` turns within
-    the original window: solve WINDOW * omega_i = turns * 2 pi for i."""
-    return ROPE_DIMS * math.log(WINDOW / (turns * 2.0 * math.pi)) / (2.0 * math.log(THETA))
+def turns_in_window() -> np.ndarray:
+    """Turns each pair completes within the original window: 512 omega_i / 2 pi."""
+    return WINDOW * base_frequencies() / (2.0 * math.pi)
 
 
 def yarn_frequencies() -> np.ndarray:
-    """YaRN-blended frequencies (concept page, "Positions")."""
+    """YaRN-blended frequencies (concept page, "Positions"): pairs turning
+    at least 32 times within the window keep their frequency, pairs turning
+    less than once are divided by 2,048, and between the last kept pair and
+    the first divided one the weight of the divided frequency rises
+    linearly with the pair index."""
     w = base_frequencies()
-    lo = math.floor(_pair_completing(BETA_FAST))
-    hi = math.ceil(_pair_completing(BETA_SLOW))
+    turns = turns_in_window()
+    last_kept = int(np.nonzero(turns >= TURNS_KEPT)[0].max())
+    first_divided = int(np.nonzero(turns < TURNS_DIVIDED)[0].min())
     out = np.empty_like(w)
     for i in range(w.shape[0]):
-        keep = 1.0 - min(max((i - lo) / (hi - lo), 0.0), 1.0)
-        out[i] = w[i] * keep + (w[i] / FACTOR) * (1.0 - keep)
+        if i <= last_kept:
+            out[i] = w[i]
+        elif i >= first_divided:
+            out[i] = w[i] / FACTOR
+        else:
+            g = (i - last_kept) / (first_divided - last_kept)
+            out[i] = (1.0 - g) * w[i] + g * (w[i] / FACTOR)
     return out
 
 

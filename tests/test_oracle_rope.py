@@ -4,7 +4,9 @@ to properties of rotations that any correct implementation has."""
 import math
 
 import numpy as np
+import pytest
 
+import oracle
 from oracle import rope
 
 
@@ -91,3 +93,63 @@ def test_query_scaling_and_append_row():
     np.testing.assert_array_equal(row[:512], lat)
     np.testing.assert_allclose(row[512:], rope.rotate(kr, t, f))
     np.testing.assert_array_equal(rope.append_row(lat, None, t, f), lat)
+
+
+@pytest.mark.parametrize("n", [2, 7, 4096, 70001])
+def test_query_scaling_bounds_the_competitors(n):
+    """The concept page's "Query scaling" section: a key that beats n - 1
+    competitors by a logit gap Delta gets weight 1/(1 + (n - 1) e^-Delta);
+    with the logits multiplied by c ln n the competitors' total becomes
+    (n - 1) n^(-c Delta).  Composing the oracle's query preparation at the
+    last position t = n - 1 (s_h = c_h, b_h = 0) with its attention over all
+    n visible positions must give the leader exactly that weight, for every
+    head's own c_h: this ties query_scale to the log of the number of
+    visible positions, t + 1, and to the factor multiplying the whole logit.
+
+    Construction: 512-wide rows without rotary part (a rotary-free layer) and
+    one with a zero rotary part; the leader's latent is e_0, the others' have
+    a zero first value (their other values are free), and every head's query
+    is e_0 * Delta / tau, so the unscaled logits are Delta and 0.  The
+    leader's weight is then the first value of each head's output."""
+    rng = np.random.default_rng(60 + n)
+    tau = 1.0 / math.sqrt(192.0)
+    t = n - 1
+    c = np.linspace(0.25, 2.0, 64)                 # per-head learned slope s_h
+    delta = 1.3
+    lead = int(rng.integers(0, n))
+    for width in (512, 576):
+        kv = rng.standard_normal((n, width)).astype(np.float32)
+        kv[:, 0] = 0.0
+        kv[lead] = 0.0
+        kv[lead, 0] = 1.0
+        if width == 576:
+            kv[:, 512:] = 0.0                      # the rotary key plays no part
+        q = np.zeros((64, width))
+        q[:, 0] = delta / tau
+        qs = rope.prepare_query(q, t, rope.rope_frequencies(), c, np.zeros(64))
+        q32 = qs.astype(np.float32)
+        o, lse = oracle.mla_attend(q32, kv, np.arange(n, dtype=np.int32), tau)
+        # given the float32 query the attention passes on, the leader's logit
+        # is tau * q32[h][0] exactly and its weight follows
+        gap = tau * q32[:, 0].astype(np.float64)
+        # (to the rounding of the oracle's n-term sum in double)
+        np.testing.assert_allclose(o[:, 0], 1.0 / (1.0 + (n - 1) * np.exp(-gap)), rtol=1e-12 + 2e-16 * n, atol=0)
+        # the page's identity, up to the one float32 rounding of the scaled
+        # query (a relative 6e-8 of a logit below 40)
+        expect = 1.0 / (1.0 + (n - 1) * float(n) ** (-c * delta))
+        np.testing.assert_allclose(o[:, 0], expect, rtol=5e-6, atol=0)
+
+
+def test_query_scaling_leader_weight_exact_in_double():
+    """The same identity with the composition carried out in float64 end to
+    end (the oracle's attention widens float32 inputs, so the query is
+    applied to the logits here by hand with the oracle's query_scale): the
+    leader's weight equals 1/(1 + (n - 1) n^(-c Delta)) to 1e-12."""
+    for n in (3, 100, 1 << 20):
+        for c, delta in ((0.5, 2.0), (1.0, 1.0), (1.7, 0.4)):
+            m = float(rope.query_scale(n - 1, np.array([c]), np.array([0.0]))[0])
+            logits = np.zeros(n)
+            logits[0] = m * delta                  # the leader; n - 1 competitors at 0
+            p = np.exp(logits - logits.max())
+            p /= p.sum()
+            assert abs(p[0] - 1.0 / (1.0 + (n - 1) * float(n) ** (-c * delta))) <= 1e-12
