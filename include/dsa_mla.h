@@ -42,9 +42,14 @@
  *   - Dtypes: DSA_BF16 (bf16 storage, fp32 accumulation) or DSA_F32; the
  *     indexer's query and keys may also be DSA_FP8_E4M3.  Indexer weights,
  *     scores and log-sum-exp are always float32.
- *   - Alignment: every pointer 16-byte aligned.  Row strides are fixed:
- *     indexer keys 128 elements, cache rows 512 + rope_dim (512 latent, then
- *     the rotary key if any).
+ *   - Alignment: the arrays read or written as 16-byte vectors -- q_idx,
+ *     w_idx, k_idx, q, kv, out, the workspace ws, and every array of
+ *     dsa_rope_append -- must be 16-byte aligned; every other array needs
+ *     only its element's alignment: 4 bytes for scores, idx, count, lse and
+ *     the int32 batch arrays, 8 bytes for seq_row0.  A misaligned pointer is
+ *     DSA_ERR_ALIGN.  Row strides are fixed: indexer keys 128 elements, cache
+ *     rows 512 + rope_dim (512 latent, then the rotary key if any); the
+ *     score row stride ld is free (rows need not start on 16 bytes).
  *   - Entries are re-entrant; calls that share a workspace race unless they
  *     are ordered on one stream.
  */
@@ -77,7 +82,7 @@ typedef enum {
   DSA_ERR_NULL = -1,        /* a required pointer is NULL                         */
   DSA_ERR_SHAPE = -2,       /* a size is out of range                             */
   DSA_ERR_DTYPE = -3,       /* unknown dtype                                      */
-  DSA_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned                   */
+  DSA_ERR_ALIGN = -4,       /* a pointer lacks the alignment its array needs      */
   DSA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than the size query says */
   DSA_ERR_UNSUPPORTED = -6, /* valid but not supported (k > 2,048, too many layers) */
   DSA_ERR_HIP = -7          /* the HIP runtime reported an error                  */

@@ -26,12 +26,28 @@ int hip_status(hipError_t e, const char* what) {
   return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+bool aligned16(const void* p) { return aligned(p, 16); }
 
+// A required array read or written as 16-byte vectors.
 #define REQUIRE_PTR(p)                                        \
   do {                                                        \
     if ((p) == nullptr) return fail(DSA_ERR_NULL, "%s is NULL", #p); \
     if (!aligned16(p)) return fail(DSA_ERR_ALIGN, "%s is not 16-byte aligned", #p); \
+  } while (0)
+
+// A required array of 4-byte elements (int32 or float32), accessed one
+// element at a time.
+#define REQUIRE_PTR4(p)                                       \
+  do {                                                        \
+    if ((p) == nullptr) return fail(DSA_ERR_NULL, "%s is NULL", #p); \
+    if (!aligned((p), 4)) return fail(DSA_ERR_ALIGN, "%s is not 4-byte aligned", #p); \
+  } while (0)
+
+// An optional array (NULL allowed) of 4-byte elements.
+#define OPTIONAL_PTR4(p)                                      \
+  do {                                                        \
+    if ((p) != nullptr && !aligned((p), 4)) return fail(DSA_ERR_ALIGN, "%s is not 4-byte aligned", #p); \
   } while (0)
 
 int check_batch(const dsa_batch_t* b, dsa::BatchDev* out) {
@@ -44,6 +60,9 @@ int check_batch(const dsa_batch_t* b, dsa::BatchDev* out) {
   if (b->nq > 0) {
     if (!b->q_seq || !b->q_pos || !b->seq_len || !b->seq_row0)
       return fail(DSA_ERR_NULL, "a batch index array is NULL");
+    if (!aligned(b->q_seq, 4) || !aligned(b->q_pos, 4) || !aligned(b->seq_len, 4))
+      return fail(DSA_ERR_ALIGN, "a batch int32 array is not 4-byte aligned");
+    if (!aligned(b->seq_row0, 8)) return fail(DSA_ERR_ALIGN, "batch seq_row0 is not 8-byte aligned");
   }
   out->nq = b->nq;
   out->nseq = b->nseq;
@@ -95,7 +114,7 @@ const char* dsa_status_string(int32_t st) {
     case DSA_ERR_NULL: return "DSA_ERR_NULL: a required pointer is NULL";
     case DSA_ERR_SHAPE: return "DSA_ERR_SHAPE: a size is out of range";
     case DSA_ERR_DTYPE: return "DSA_ERR_DTYPE: unknown dtype";
-    case DSA_ERR_ALIGN: return "DSA_ERR_ALIGN: a pointer is not 16-byte aligned";
+    case DSA_ERR_ALIGN: return "DSA_ERR_ALIGN: a pointer lacks the alignment its array needs";
     case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE: workspace missing or too small";
     case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED: valid but unsupported arguments";
     case DSA_ERR_HIP: return "DSA_ERR_HIP: the HIP runtime reported an error";
@@ -115,7 +134,7 @@ int32_t dsa_index_score(const dsa_batch_t* batch, int32_t dtype, const void* q_i
   REQUIRE_PTR(q_idx);
   REQUIRE_PTR(w_idx);
   REQUIRE_PTR(k_idx);
-  if (scores == nullptr) return fail(DSA_ERR_NULL, "scores is NULL");
+  REQUIRE_PTR4(scores);
   if (ld < b.max_len) return fail(DSA_ERR_SHAPE, "ld = %lld < max_len = %d", (long long)ld, b.max_len);
   return hip_status(dsa::launch_index_score(b, dtype, q_idx, w_idx, k_idx, scores, ld, as_stream(stream)),
                     "dsa_index_score launch");
@@ -133,12 +152,14 @@ int32_t dsa_topk(const dsa_batch_t* batch, const float* scores, int64_t ld, int3
   if (st) return st;
   if ((st = check_k(k))) return st;
   if (b.nq == 0) return DSA_OK;
-  if (scores == nullptr) return fail(DSA_ERR_NULL, "scores is NULL");
-  if (idx == nullptr) return fail(DSA_ERR_NULL, "idx is NULL");
+  REQUIRE_PTR4(scores);
+  REQUIRE_PTR4(idx);
+  OPTIONAL_PTR4(count);
   if (ld < b.max_len) return fail(DSA_ERR_SHAPE, "ld = %lld < max_len = %d", (long long)ld, b.max_len);
   const size_t need = dsa::topk_workspace_bytes(b.nq, b.max_len, k);
   if (need > 0 && (ws == nullptr || ws_bytes < need))
     return fail(DSA_ERR_WORKSPACE, "top-k workspace: %zu bytes given, %zu needed", ws_bytes, need);
+  if (need > 0 && !aligned16(ws)) return fail(DSA_ERR_ALIGN, "ws is not 16-byte aligned");
   return hip_status(dsa::launch_topk(b, scores, ld, k, idx, count, ws, ws_bytes, as_stream(stream)),
                     "dsa_topk launch");
 }
@@ -170,7 +191,8 @@ int32_t mla_sparse_attend(const dsa_batch_t* batch, int32_t dtype, int32_t rope_
   if ((st = check_k(k))) return st;
   if (b.nq == 0) return DSA_OK;
   if ((st = check_mla_layer(q, kv, out))) return st;
-  if (idx == nullptr) return fail(DSA_ERR_NULL, "idx is NULL");
+  REQUIRE_PTR4(idx);
+  OPTIONAL_PTR4(lse);
   const size_t need = dsa::mla_workspace_bytes(dtype, b.nq, k, 1);
   if (need > 0 && (ws == nullptr || ws_bytes < need))
     return fail(DSA_ERR_WORKSPACE, "MLA workspace: %zu bytes given, %zu needed", ws_bytes, need);
@@ -256,11 +278,13 @@ int32_t dsa_mla_decode_fused(const dsa_batch_t* batch, int32_t index_dtype, cons
   memset(&L, 0, sizeof(L));
   for (int l = 0; l < n_layers; ++l) {
     if ((st = check_mla_layer(q_l[l], kv_l[l], out_l[l]))) return st;
+    if (lse_l && lse_l[l] && !aligned(lse_l[l], 4)) return fail(DSA_ERR_ALIGN, "lse_l[%d] is not 4-byte aligned", l);
     L.q[l] = q_l[l];
     L.kv[l] = kv_l[l];
     L.out[l] = out_l[l];
     L.lse[l] = lse_l ? lse_l[l] : nullptr;
   }
+  OPTIONAL_PTR4(idx_out);
   size_t off_idx, off_topk, off_mla;
   const size_t need = fused_parts(b.nq, b.max_len, k, n_layers, &off_idx, &off_topk, &off_mla);
   if (ws == nullptr || ws_bytes < need)
@@ -280,10 +304,10 @@ int32_t dsa_ml4_layer_plan(int32_t n_layers, dsa_layer_plan_t* plan) {
   if (n_layers < 1 || n_layers > DSA_ML4_LAYERS)
     return fail(DSA_ERR_SHAPE, "n_layers = %d outside [1, %d]", n_layers, DSA_ML4_LAYERS);
   for (int l = 0; l < n_layers; ++l) {
-    const bool rotary = (l + 1) % 4 != 0;   // every fourth layer has no rotary encoding
-    plan[l].rope_dim = rotary ? DSA_ROPE : 0;
-    plan[l].kv_source = (!rotary && l >= 39) ? 35 : l;   // layer 35's latent, from layer 39 on
-    plan[l].runs_indexer = (l >= 16 && (l % 4 == 1 || l % 4 == 2)) ? 0 : 1;
+    const bool nope = (l & 3) == 3;                     // layers 3, 7, 11, ...: no rotary encoding
+    plan[l].rope_dim = nope ? 0 : DSA_ROPE;
+    plan[l].kv_source = (nope && l > 35) ? 35 : l;      // later rotary-free layers read layer 35's latent
+    plan[l].runs_indexer = (l < 16 || (l & 3) == 0 || nope) ? 1 : 0;  // from 16, the middle two of a group reuse
   }
   return DSA_OK;
 }
@@ -349,9 +373,10 @@ int32_t dsa_mla_decode_layers(const dsa_batch_t* batch, int32_t n_layers, const 
       REQUIRE_PTR(q_idx);
       REQUIRE_PTR(w_idx);
       REQUIRE_PTR(k_idx);
-      if (idx_l && idx_l[l] && !aligned16(idx_l[l])) return fail(DSA_ERR_ALIGN, "idx_l[%d] is not 16-byte aligned", l);
+      if (idx_l && idx_l[l] && !aligned(idx_l[l], 4)) return fail(DSA_ERR_ALIGN, "idx_l[%d] is not 4-byte aligned", l);
     }
     if ((st = check_mla_layer(q_l[l], kv_l[plan[l].kv_source], out_l[l]))) return st;
+    if (lse_l && lse_l[l] && !aligned(lse_l[l], 4)) return fail(DSA_ERR_ALIGN, "lse_l[%d] is not 4-byte aligned", l);
   }
   size_t off_idx, off_topk, off_mla;
   const size_t need = fused_parts(b.nq, b.max_len, k, max_group, &off_idx, &off_topk, &off_mla);

@@ -248,16 +248,18 @@ def test_decode_layers_workspace_covers_every_run(lib):
 
 
 def test_rope_frequencies_match_the_oracle(lib):
-    """The library's frequencies (host, double precision) against the
-    oracle's, which its pins tie to the page's wavelength assertions."""
+    """The library's frequencies (host, double precision; found from the
+    wavelengths) against the oracle's (found from the turn counts), which its
+    pins tie to the page's wavelength figures.  The two take different
+    arithmetic routes, so they agree to a few units in the last place."""
     import numpy as np
     from oracle import rope
     out = np.zeros(32, np.float64)
     assert lib.dsa_rope_frequencies(None, out.ctypes.data) == OK
-    np.testing.assert_allclose(out, rope.rope_frequencies(), rtol=4e-16)
+    np.testing.assert_allclose(out, rope.rope_frequencies(), rtol=2e-15)
     alpha = np.linspace(-1, 1, 32).astype(np.float32)
     assert lib.dsa_rope_frequencies(alpha.ctypes.data, out.ctypes.data) == OK
-    np.testing.assert_allclose(out, rope.rope_frequencies(alpha.astype(np.float64)), rtol=4e-16)
+    np.testing.assert_allclose(out, rope.rope_frequencies(alpha.astype(np.float64)), rtol=2e-15)
     assert lib.dsa_rope_frequencies(None, None) == NULL
 
 
@@ -279,3 +281,107 @@ def test_rope_append_validation(lib):
     assert lib.dsa_rope_append(ctypes.byref(_batch(nq=0)), 1, 64, None, None, None, None, None, None, None,
                                None) == OK
 
+
+
+# addresses with a given alignment: A4 is 4- but not 8- or 16-byte aligned,
+# A8 is 8- but not 16-byte aligned, ODD is not even 4-byte aligned
+A4, A8, ODD = 0x10004, 0x10008, 0x10002
+
+
+def test_alignment_contract_index_score(lib):
+    """Each pointer of dsa_index_score against the header's alignment rule:
+    q_idx, w_idx and k_idx 16 bytes; scores 4 bytes (a 4-byte aligned scores
+    pointer passes alignment and fails on the later ld check instead)."""
+    b = ctypes.byref(_batch())
+    call = lambda q=A, w=A, k=A, s=A, ld=100: lib.dsa_index_score(b, 1, q, w, k, s, ld, None)
+    for name, kw in (("q_idx", "q"), ("w_idx", "w"), ("k_idx", "k")):
+        assert call(**{kw: A4}) == ALIGN, name
+        assert name.encode() in lib.dsa_last_error()
+    assert call(s=ODD) == ALIGN
+    assert b"scores" in lib.dsa_last_error()
+    assert call(s=A4, ld=99) == SHAPE
+
+
+def test_alignment_contract_batch_arrays(lib):
+    """The batch's int32 arrays need 4 bytes, seq_row0 (int64) 8 bytes."""
+    for field, bad, good in (("q_seq", ODD, A4), ("q_pos", ODD, A4), ("seq_len", ODD, A4),
+                             ("seq_row0", A4, A8)):
+        b = _batch()
+        setattr(b, field, bad)
+        assert lib.dsa_index_score(ctypes.byref(b), 1, A, A, A, A, 100, None) == ALIGN, field
+        setattr(b, field, good)
+        assert lib.dsa_index_score(ctypes.byref(b), 1, A, A, A, A, 99, None) == SHAPE, field
+
+
+def test_alignment_contract_topk(lib):
+    """scores, idx and count 4 bytes; the workspace 16 bytes when one is
+    needed (few rows longer than 49,152 scores)."""
+    b = ctypes.byref(_batch())
+    call = lambda s=A, i=A, c=None, ld=100: lib.dsa_topk(b, s, ld, 8, i, c, None, 0, None)
+    assert call(s=ODD) == ALIGN
+    assert call(i=ODD) == ALIGN
+    assert call(c=ODD) == ALIGN
+    assert call(s=A4, i=A4, c=A4, ld=99) == SHAPE
+    long_b = _batch(max_len=60000)
+    need = lib.dsa_topk_workspace_size(2, 60000, 2048)
+    assert need > 0
+    assert lib.dsa_topk(ctypes.byref(long_b), A, 60000, 2048, A, None, A4, need, None) == ALIGN
+
+
+def test_alignment_contract_mla(lib):
+    """q, kv, out and ws 16 bytes; idx and lse 4 bytes."""
+    b = ctypes.byref(_batch())
+
+    def call(q=A, kv=A, idx=A, out=A, lse=None, ws=A, k=2048):
+        return lib.mla_sparse_attend(b, 1, 64, q, kv, idx, k, 0.07, out, 0, lse, ws, 1 << 40, None)
+
+    for kw in ("q", "kv", "out", "ws"):
+        assert call(**{kw: A4}) == ALIGN, kw
+    assert call(idx=ODD) == ALIGN
+    assert call(lse=ODD) == ALIGN
+    assert call(idx=A4, lse=A4, k=0) == SHAPE      # k is checked first: shape error, not alignment
+    assert call(idx=A4, lse=A4, ws=None) == WORKSPACE
+
+
+def test_alignment_contract_fused_and_layers(lib):
+    """The fused entry: per-layer q, kv, out 16 bytes, lse entries and
+    idx_out 4 bytes; the layers entry: idx_l and lse_l entries 4 bytes."""
+    b = ctypes.byref(_batch())
+    need = lib.dsa_mla_decode_fused_workspace_size(2, 100, 2048, 2)
+    tab = lambda *p: ctypes.cast((ctypes.c_void_p * 2)(*p), ctypes.c_void_p)
+
+    def call(q=(A, A), kv=(A, A), out=(A, A), lse=None, idx=None, ws=A, wsb=need):
+        return lib.dsa_mla_decode_fused(b, 1, A, A, A, 2048, 2, 1, 64, tab(*q), tab(*kv), tab(*out),
+                                        None if lse is None else tab(*lse), 0, 0.07, idx, ws, wsb, None)
+
+    assert call(q=(A, A4)) == ALIGN
+    assert call(out=(A4, A)) == ALIGN
+    assert call(lse=(A, ODD)) == ALIGN
+    assert call(idx=ODD) == ALIGN
+    assert call(lse=(A4, None), idx=A4, wsb=need - 1) == WORKSPACE
+    n = 72
+    plan = _plan(lib, n)
+    lneed = lib.dsa_mla_decode_layers_workspace_size(2, 100, 2048, n, ctypes.byref(plan))
+    full = lambda v: ctypes.cast((ctypes.c_void_p * n)(*([v] * n)), ctypes.c_void_p)
+
+    def lcall(idx_l=None, lse_l=None, wsb=lneed):
+        t = full(A)
+        return lib.dsa_mla_decode_layers(b, n, ctypes.byref(plan), 1, t, t, t, 2048, 1, t, t, t, lse_l, 0, 0.07,
+                                         idx_l, A, wsb, None)
+
+    assert lcall(idx_l=full(ODD)) == ALIGN
+    assert lcall(lse_l=full(ODD)) == ALIGN
+    assert lcall(idx_l=full(A4), lse_l=full(A4), wsb=lneed - 1) == WORKSPACE
+
+
+def test_alignment_contract_rope_append(lib):
+    """Every array of dsa_rope_append is 16-byte aligned."""
+    b = ctypes.byref(_batch())
+
+    def call(freq=A, lat=A, kr=A, kv=A, q=None, s=None, bb=None):
+        return lib.dsa_rope_append(b, 1, 64, freq, lat, kr, kv, q, s, bb, None)
+
+    for kw in ("freq", "lat", "kr", "kv", "q"):
+        assert call(**{kw: A8}) == ALIGN, kw
+    assert call(s=A8, bb=A) == ALIGN
+    assert call(s=A, bb=A8) == ALIGN
