@@ -175,23 +175,31 @@ LAYERS = 72
 def layer_plan(n_layers: int = LAYERS):
     """Per layer l < n_layers: (runs_indexer, rope, kv_source).
 
-    Rules of the concept page's list of changes to the DeepSeek recipe:
-      * every fourth layer (l = 3, 7, 11, ...) has no rotary encoding;
+    Rules of the concept page's list of changes to the DeepSeek recipe,
+    applied to the model's 18 groups of four consecutive layers:
+      * every fourth layer has no rotary encoding: the last layer of each
+        group (layers 3, 7, 11, ...);
       * from layer 39 on, those layers read layer 35's latent instead of
-        keeping their own (every layer that shares a cache is rotary-free,
-        and so is layer 35);
+        keeping their own: the rotary-free layers of the groups after the
+        one that ends at layer 35 (every layer that shares a cache is
+        rotary-free, and so is layer 35);
       * 28 layers reuse the selection of the most recent layer that ran its
         indexer.  Which ones (reading of the summary page's DSA paragraph):
-        from layer 16 on, in every group of four layers (16-19, 20-23, ...)
-        the middle two reuse the selection of the group's first layer, and
-        the first and last run their own indexer.
+        in the groups from layer 16 on, the two middle layers reuse the
+        selection of the group's first layer, and the first and last run
+        their own indexer.
     """
     plan = []
-    for l in range(n_layers):
-        rope = (l + 1) % 4 != 0
-        kv_source = 35 if (l >= 39 and not rope) else l
-        reuses = l >= 16 and l % 4 in (1, 2)
-        plan.append((not reuses, rope, kv_source))
+    source_group = 35 // 4
+    for g in range((n_layers + 3) // 4):
+        for j in range(4):
+            l = 4 * g + j
+            if l >= n_layers:
+                break
+            rotary = j != 3
+            reuses = g >= 4 and j in (1, 2)
+            kv_source = 35 if (not rotary and g > source_group) else l
+            plan.append((not reuses, rotary, kv_source))
     return plan
 
 

@@ -7,8 +7,8 @@ Two parts:
    (sections "Cache", "Sparse attention", "When does sparse attention pay?"
    and the 1M-token serving scenario), rebuilt from the layer rules the page
    states in its list of changes to the DeepSeek recipe:
-     * every fourth layer (layer index l with (l+1) divisible by 4) has no
-       rotary encoding (NoPE);
+     * every fourth layer (0-based layers 3, 7, 11, ...) has no rotary
+       encoding (NoPE);
      * from layer 39 on, those NoPE layers read layer 35's latent instead of
        writing their own;
      * 28 of the 72 layers reuse the selection of the most recent layer that
@@ -17,9 +17,11 @@ Two parts:
        original four-layer group share one indexer, so in every group
        (16-19, 20-23, ...) the first layer runs it, the next two reuse it and
        the NoPE layer runs its own.
-   The tests pin every printed figure (35,712 values; 74.9 GB; 33x;
-   4.94e6 and 1.80e5 multiply-adds; ~56,000 tokens; 3.5x/19x/26x; ~4%;
-   39%; 5.9 GB; 95%; ~1e17).
+   The figures are counted from a census of layer kinds (rotary or not,
+   owning its cache or not, running its indexer or not).  The tests pin
+   every printed figure (35,712 values; 74.9 GB; 33x; 4.94e6 and 1.80e5
+   multiply-adds; ~56,000 tokens; 3.5x/19x/26x; ~4%; 39%; 5.9 GB; 95%;
+   ~1e17).
 
 2. Per-workload algorithmic traffic of this library's hot path: bytes that
    must cross HBM at least once (inputs read once, final outputs written
@@ -28,6 +30,9 @@ Two parts:
    position and 64 x (512 + 64 + 512) per attended position.
 """
 from __future__ import annotations
+
+import collections
+import functools
 
 import numpy as np
 
@@ -40,17 +45,20 @@ INDEXER_DIM = 128
 TOPK = 2048
 FIRST_SHARED_INDEXER_LAYER = 16
 YOCO_SOURCE = 35
-YOCO_FIRST_READER = 39
+
+
+# Three facts describe a layer: whether it has rotary encoding, whose latent
+# it reads, and whether it runs its own indexer.
 
 
 def is_rope_layer(l: int) -> bool:
-    return (l + 1) % 4 != 0
+    """Layers 3, 7, 11, ... (every fourth, counting from one) are NoPE."""
+    return l % 4 != 3
 
 
 def kv_source(l: int) -> int:
-    if l >= YOCO_FIRST_READER and not is_rope_layer(l):
-        return YOCO_SOURCE
-    return l
+    """The NoPE layers that come after layer 35 read its latent."""
+    return YOCO_SOURCE if (not is_rope_layer(l) and l > YOCO_SOURCE) else l
 
 
 def runs_indexer(l: int) -> bool:
@@ -59,19 +67,37 @@ def runs_indexer(l: int) -> bool:
     return (l - FIRST_SHARED_INDEXER_LAYER) % 4 in (0, 3)
 
 
+@functools.lru_cache(maxsize=None)
+def _census():
+    """Number of layers of each kind (rotary, owns its cache, runs its indexer)."""
+    return collections.Counter((is_rope_layer(l), kv_source(l) == l, runs_indexer(l)) for l in range(LAYERS))
+
+
+def _layers(rope=None, owns=None, indexer=None) -> int:
+    """Layers of the kinds that match every given fact."""
+    return sum(n for (r, o, i), n in _census().items()
+               if (rope is None or r == rope) and (owns is None or o == owns) and (indexer is None or i == indexer))
+
+
+def row_values(rope: bool) -> int:
+    """Values one position adds to a cache: the latent, plus the rotary key
+    in a rotary layer."""
+    return LATENT + (ROPE if rope else 0)
+
+
 def indexer_layers() -> int:
-    return sum(runs_indexer(l) for l in range(LAYERS))
+    return _layers(indexer=True)
 
 
 def cached_values_per_position() -> int:
-    """Latent (+ rotary key) values stored per position across the model."""
-    return sum(LATENT + (ROPE if is_rope_layer(l) else 0)
-               for l in range(LAYERS) if kv_source(l) == l)
+    """Latent (+ rotary key) values stored per position across the model:
+    one row per layer that owns its cache."""
+    return sum(_layers(rope=r, owns=True) * row_values(r) for r in (True, False))
 
 
 def values_saved_by_cache_sharing() -> int:
-    return sum(LATENT + (ROPE if is_rope_layer(l) else 0)
-               for l in range(LAYERS) if kv_source(l) != l)
+    """Values the layers that read another layer's cache would add."""
+    return sum(_layers(rope=r, owns=False) * row_values(r) for r in (True, False))
 
 
 def full_kv_values_per_position(head_k: int = 128, head_v: int = 128) -> int:
@@ -83,29 +109,34 @@ def latent_cache_bytes(positions: int, bytes_per_value: int = 2) -> int:
 
 
 def attend_macs_per_position() -> int:
-    """Model-wide multiply-adds per attended position (all 72 layers)."""
-    return sum(HEADS * (LATENT + (ROPE if is_rope_layer(l) else 0) + LATENT)
-               for l in range(LAYERS))
+    """Model-wide multiply-adds per attended position: in each layer every
+    head dots its query with the row (latent plus rotary key, if any) and
+    adds the 512-value latent to its output."""
+    return sum(_layers(rope=r) * HEADS * (row_values(r) + LATENT) for r in (True, False))
 
 
 def score_macs_per_position() -> int:
-    """Model-wide multiply-adds per scored position (indexer-running layers)."""
+    """Model-wide multiply-adds per scored position (indexer layers only)."""
     return indexer_layers() * INDEXER_HEADS * INDEXER_DIM
 
 
-def work(t: int):
-    """(dense MLA, sparse read) multiply-adds for one new token at context t."""
-    a, s = attend_macs_per_position(), score_macs_per_position()
-    return a * t, a * min(t, TOPK) + s * t
+def dense_macs(t: int) -> int:
+    """Dense MLA for one new token at context t: every position attended."""
+    return attend_macs_per_position() * t
+
+
+def sparse_macs(t: int) -> int:
+    """The sparse read: at most TOPK attended positions, all t scored."""
+    return attend_macs_per_position() * min(t, TOPK) + score_macs_per_position() * t
 
 
 def indexer_crossover_tokens() -> float:
-    return attend_macs_per_position() * TOPK / score_macs_per_position()
+    """Context at which scoring t positions costs as much as attending TOPK."""
+    return TOPK * attend_macs_per_position() / score_macs_per_position()
 
 
 def sparse_gain(t: int) -> float:
-    dense, sparse = work(t)
-    return dense / sparse
+    return dense_macs(t) / sparse_macs(t)
 
 
 def short_prompt_overhead() -> float:
@@ -114,7 +145,7 @@ def short_prompt_overhead() -> float:
 
 
 def selection_reuse_saving() -> float:
-    return (LAYERS - indexer_layers()) / LAYERS
+    return _layers(indexer=False) / LAYERS
 
 
 def fp8_indexer_key_bytes(positions: int) -> int:
@@ -122,8 +153,7 @@ def fp8_indexer_key_bytes(positions: int) -> int:
 
 
 def indexer_share(t: int) -> float:
-    a, s = attend_macs_per_position(), score_macs_per_position()
-    return s * t / (a * min(t, TOPK) + s * t)
+    return score_macs_per_position() * t / sparse_macs(t)
 
 
 def prefill_scoring_macs(t: int) -> float:

@@ -1,20 +1,23 @@
 // Rotary encoding and cache append on gfx950: the step just upstream of the
 // attention read (concept page "Mistral Large 4", sections "Positions" and
-// "Query scaling", and the YaRN wavelength function of its example).
+// "Query scaling").
 //
-// Frequencies: pair i < 32 of the 64-value rotary part turns at
-//   omega_i = 10000^(-2i/64); YaRN (window 512, factor 2,048) keeps the pairs
-//   that complete at least 32 turns within the window, divides by 2,048 those
-//   that complete less than one, and blends linearly in the pair index in
-//   between (from the rounded-down index of 32 turns to the rounded-up index
-//   of one turn); LeRoPE multiplies frequency i by e^{alpha_i}.
+// Frequencies (host, double precision): the 64-value rotary part is 32 pairs;
+// pair i turns at omega_i = 10000^(-i/32) radians per position.  Under YaRN
+// (original window 512, stretch 2,048) a pair whose wavelength 2 pi / omega_i
+// fits 32 times into the window is left alone, a pair whose wavelength is
+// longer than the window is slowed by the full stretch, and the pairs
+// between the longest unchanged and the shortest fully slowed wavelength
+// are slowed by a factor interpolated linearly in the pair index; LeRoPE
+// scales frequency i by the learned e^{alpha_i}.
 // Per new token at 0-based position t (pair i = values 2i, 2i+1 of the
 // rotary part, turned by the angle t * omega_i):
 //   cache row  = [latent (512) | rotated rotary key (64, rotary layers only)]
 //   query h    = m_h(t) * q[h], its rotary part rotated;  m_h(t) =
 //                s_h ln(t + 1) + b_h when per-head (s, b) are given (the
-//                page's query-scaling formula was lost; this affine function
-//                of ln(number of visible positions) is the reading taken).
+//                section's displayed formula was lost; its Scalable-Softmax
+//                argument gives the c ln(visible positions) form, and the
+//                learned offset b_h is a reading).
 // Angles are formed in double precision (t * omega reaches 10^6 radians at
 // the end of the 2^20-position range), then applied in float.
 #include <math.h>
@@ -102,16 +105,20 @@ __global__ __launch_bounds__(ROPE_THREADS) void rope_append_kernel(BatchDev b, i
 }
 
 void rope_frequencies(const float* alpha, double* out) {
-  const double theta = 10000.0, window = 512.0, factor = 2048.0, fast = 32.0, slow = 1.0;
-  const int pairs = DR / 2;
-  // fractional pair index that completes `turns` turns within the window
-  auto pair_at = [&](double turns) { return DR * log(window / (turns * 2.0 * M_PI)) / (2.0 * log(theta)); };
-  const double lo = floor(pair_at(fast)), hi = ceil(pair_at(slow));
+  constexpr int pairs = DR / 2;
+  const double window = 512.0, stretch = 2048.0, min_turns = 32.0;
+  double omega[pairs];
+  int longest_kept = -1, shortest_slowed = pairs;
   for (int i = 0; i < pairs; ++i) {
-    const double w = pow(theta, -2.0 * i / DR);
-    const double ramp = fmin(fmax((i - lo) / (hi - lo), 0.0), 1.0);
-    const double keep = 1.0 - ramp;
-    double f = w * keep + (w / factor) * (1.0 - keep);
+    omega[i] = exp(-log(10000.0) * (double)i / (double)pairs);
+    const double wavelength = 2.0 * M_PI / omega[i];
+    if (wavelength * min_turns <= window) longest_kept = i;                    // wavelengths grow with i
+    if (wavelength > window && shortest_slowed == pairs) shortest_slowed = i;
+  }
+  for (int i = 0; i < pairs; ++i) {
+    double ramp = (double)(i - longest_kept) / (double)(shortest_slowed - longest_kept);
+    ramp = ramp < 0.0 ? 0.0 : (ramp > 1.0 ? 1.0 : ramp);
+    double f = omega[i] * (1.0 - ramp * (1.0 - 1.0 / stretch));
     if (alpha) f *= exp((double)alpha[i]);
     out[i] = f;
   }
