@@ -6,18 +6,26 @@ the C ABI, with all inputs resident in HBM: the fused decode entry for decode
 batches, the three calls in turn for a prefill chunk.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 0..4] [--no-cpu]
-                  [--index-dtype fp8]
+                  [--no-extras] [--index-dtype fp8]
   python bench.py --model-layers 72 [--model-batch 64] [--model-context 32768]
       one decode step of every layer of the model's schedule (indexer layers,
       selection reuse, rotary-free layers, shared cache), inputs drawn on the
-      GPU from a seeded generator (the caches of 63 layers do not fit a
-      host-side draw in reasonable time); prints its own JSON line.
+      GPU from a seeded generator; prints its own JSON line.
 
-The default workload is the decode batch of 64 sequences at 32,768 positions
-(bf16).  `roofline` describes the dominant kernel (the indexer): algorithmic
-bytes (or FLOP) per launch over its average duration, timed with HIP events
-on the launch stream over a timed loop of that kernel alone.  `cpu_baseline` times the CPU
-oracle on a bounded sample of the same workload.
+The default workload is the largest one: 4 sequences at 2^20 positions
+(bf16).  Timing: W untimed warmup steps; then K steps, each after a read of
+a 512 MiB buffer that evicts the L2s and the 256 MB Infinity Cache, each
+timed alone with HIP events on the launch stream; `value` and `ms_per_step`
+are the median of the K.  A warm figure (K steps back to back) is reported
+beside it.  `roofline` describes the dominant kernel (the indexer):
+algorithmic bytes (or FLOP) per launch over its average duration in a timed
+loop of that kernel alone on the same stream.  `bars` holds, from the same
+run, the two workloads that carry targets -- the ragged 4-layer decode batch
+reaching 131,072 positions (whole-step HBM fraction, median of 50 flushed
+steps) and the 2,048-query prefill chunk (indexer MFMA fraction) -- and the
+single fp32 query (median of 50 flushed steps).  `cpu_baseline` times the CPU
+oracle on a bounded sample of the headline workload, and single-threaded on
+one query of the single-query, 64 x 32,768 and 2^20 shapes.
 """
 from __future__ import annotations
 
@@ -25,6 +33,7 @@ import argparse
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -36,21 +45,22 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
 FP8_MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 matrix, published
 FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector, published
+HEADLINE_CONFIG = 4
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=HEADLINE_CONFIG)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extras", action="store_true", help="skip the other workloads' bar figures")
     ap.add_argument("--index-dtype", choices=["bf16", "fp8"], default=None,
                     help="store the indexer's query and keys in this type (default: the workload's)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget")
-    ap.add_argument("--cold-reps", type=int, default=10,
-                    help="extra steps, each after reading a 512 MiB buffer that evicts L2 and the Infinity Cache "
-                         "(reported apart from the warm value)")
+    ap.add_argument("--cold-reps", type=int, default=50,
+                    help="flushed steps whose median the bar workloads report")
     ap.add_argument("--model-layers", type=int, default=0,
                     help="time a decode step over this many layers of the model's schedule instead")
     ap.add_argument("--model-batch", type=int, default=64)
@@ -68,15 +78,18 @@ def kernel_source_digest(kind: str) -> str:
     return hashlib.sha256(open(src, "rb").read()).hexdigest()
 
 
-def measured_traffic(kernel: str, workload: str):
+def measured_traffic(kernel: str, workload: str, algorithmic_bytes: int):
     """HBM bytes per launch of `kernel` on `workload` from the committed
     counter summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy of
-    known size), or None if absent or taken on a different kernel source."""
+    known size), or None if absent, taken on a different kernel source or on
+    other inputs (different algorithmic bytes)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path)).get(f"{kernel}/{workload}")
     if not rec or rec.get("source_sha256") != kernel_source_digest(kernel):
+        return None
+    if rec.get("algorithmic_bytes") != algorithmic_bytes:
         return None
     return rec["bytes_per_launch"]
 
@@ -94,6 +107,129 @@ def indexer_kernel(w) -> str:
     return f"idx_decode_{t}_bal" if w.nq <= 1024 else f"idx_decode_{t}"
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+class Runner:
+    """One workload resident on the GPU, its step and its stages."""
+
+    def __init__(self, w, dev):
+        import torch
+
+        from sparse_attention_12_amd import binding as B
+
+        self.w, self.B, self.dev = w, B, dev
+        self.t = t = w.to_torch(dev)
+        self.batch = B.Batch(t["q_seq"], t["q_pos"], t["seq_len"], t["seq_row0"], w.max_len)
+        k, L = w.k, w.n_layers
+        self.scores = torch.empty((w.nq, w.max_len), dtype=torch.float32, device=dev)
+        self.idx = torch.empty((w.nq, k), dtype=torch.int32, device=dev)
+        self.count = torch.empty((w.nq,), dtype=torch.int32, device=dev)
+        self.outs = [torch.empty((w.nq, 64, 512), dtype=torch.float32, device=dev) for _ in range(L)]
+        self.lses = [torch.empty((w.nq, 64), dtype=torch.float32, device=dev) for _ in range(L)]
+        n = B.dsa_topk_workspace_size(w.nq, w.max_len, k)
+        self.tk_ws = torch.empty(n, dtype=torch.uint8, device=dev) if n else None
+        self.mla_ws = torch.empty(max(B.mla_sparse_attend_workspace_size(w.nq, k, 1), 256), dtype=torch.uint8,
+                                  device=dev)
+        self.fused_ws = torch.empty(max(B.dsa_mla_decode_fused_workspace_size(w.nq, w.max_len, k, L), 256),
+                                    dtype=torch.uint8, device=dev)
+        self.stream = torch.cuda.current_stream()
+
+    def step(self):
+        w, t, B = self.w, self.t, self.B
+        if w.kind == "decode":
+            # the decode read as one call: indexer, top-k, every layer's MLA
+            B.dsa_mla_decode_fused(self.batch, t["qI"], t["w"], t["kI"], w.k, t["q"], t["kv"], self.outs, w.tau,
+                                   self.lses, self.idx, self.fused_ws)
+        else:
+            self.indexer()
+            self.topk()
+            for l in range(w.n_layers):
+                B.mla_sparse_attend(self.batch, t["q"][l], t["kv"][l], self.idx, w.k, w.tau, self.outs[l],
+                                    self.lses[l], self.mla_ws)
+
+    def indexer(self):
+        t = self.t
+        self.B.dsa_index_score(self.batch, t["qI"], t["w"], t["kI"], self.scores)
+
+    def topk(self):
+        self.B.dsa_topk(self.batch, self.scores, self.w.k, self.idx, self.count, self.tk_ws)
+
+    def mla(self):
+        w, t = self.w, self.t
+        self.B.mla_sparse_attend(self.batch, t["q"][0], t["kv"][0], self.idx, w.k, w.tau, self.outs[0],
+                                 self.lses[0], self.mla_ws)
+
+    def timed(self, fn, n):
+        """Average ms per call of fn over n calls back to back, HIP events on
+        the launch stream."""
+        import torch
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(self.stream)
+        for _ in range(n):
+            fn()
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    def flushed(self, fn, n, flush):
+        """ms of each of n calls of fn, each after `flush` (outside its events)."""
+        import torch
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        torch.cuda.synchronize()
+        for a, b in ev:
+            flush()
+            a.record(self.stream)
+            fn()
+            b.record(self.stream)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in ev]
+
+    def traffic(self):
+        from sparse_attention_12_amd import costmodel
+        w = self.w
+        return costmodel.path_traffic(w.seq_len, w.q_seq, w.q_pos, w.dtype, w.n_layers, w.k,
+                                      index_dtype=w.index_dtype)
+
+    def indexer_roofline(self, idx_ms):
+        w = self.w
+        tr = self.traffic()
+        kname = indexer_kernel(w)
+        if w.kind == "prefill" and w.index_dtype != "f32":
+            peak = FP8_MFMA_PEAK_TFLOPS if w.index_dtype == "fp8" else BF16_MFMA_PEAK_TFLOPS
+            achieved = tr["indexer"]["flop"] / (idx_ms / 1e3) / 1e12
+            roof = dict(bound="mfma", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
+                        frac=round(achieved / peak, 4), traffic=None,
+                        kernel=kname, per_launch=tr["indexer"]["flop"], per_launch_unit="FLOP")
+        elif w.index_dtype != "f32":
+            achieved = tr["indexer"]["bytes"] / (idx_ms / 1e3) / 1e9
+            roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
+                        frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=None,
+                        kernel=kname, per_launch=tr["indexer"]["bytes"], per_launch_unit="B")
+        else:
+            achieved = tr["indexer"]["flop"] / (idx_ms / 1e3) / 1e12
+            roof = dict(bound="alu", achieved=round(achieved, 3), peak=FP32_VALU_PEAK_TFLOPS, unit="TFLOP/s",
+                        frac=round(achieved / FP32_VALU_PEAK_TFLOPS, 4), traffic=None,
+                        kernel="idx_decode_f32", per_launch=tr["indexer"]["flop"], per_launch_unit="FLOP")
+        roof["traffic"] = measured_traffic(roof["kernel"], w.name, tr["indexer"]["bytes"])
+        return roof
+
+    def release(self):
+        import torch
+        del self.t, self.scores, self.outs, self.lses, self.fused_ws, self.mla_ws, self.tk_ws
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -101,121 +237,49 @@ def main():
               "(every workload runs on a single MI355X); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
-    from sparse_attention_12_amd import binding as B
-    from sparse_attention_12_amd import costmodel, workloads
+    from sparse_attention_12_amd import workloads
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.model_layers:
         model_step(args, dev)
         return
+    # before each flushed step: a read of 512 MiB (clean lines, so no
+    # write-back competes with the step) evicts the 4 MB L2s and the 256 MB
+    # Infinity Cache
+    flush_buf = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    flush = lambda: flush_buf.sum()
+
     t_gen = time.time()
     w = workloads.config(args.config, args.index_dtype)
     print(f"[bench] workload {w.name}: nq={w.nq} layers={w.n_layers} max_len={w.max_len} "
           f"(generated in {time.time() - t_gen:.1f}s)", file=sys.stderr, flush=True)
-    t = w.to_torch(dev)
-    batch = B.Batch(t["q_seq"], t["q_pos"], t["seq_len"], t["seq_row0"], w.max_len)
-    k, L = w.k, w.n_layers
-    scores = torch.empty((w.nq, w.max_len), dtype=torch.float32, device=dev)
-    idx = torch.empty((w.nq, k), dtype=torch.int32, device=dev)
-    count = torch.empty((w.nq,), dtype=torch.int32, device=dev)
-    outs = [torch.empty((w.nq, 64, 512), dtype=torch.float32, device=dev) for _ in range(L)]
-    lses = [torch.empty((w.nq, 64), dtype=torch.float32, device=dev) for _ in range(L)]
-    tk_ws_n = B.dsa_topk_workspace_size(w.nq, w.max_len, k)
-    tk_ws = torch.empty(max(tk_ws_n, 256), dtype=torch.uint8, device=dev)
-    mla_ws = torch.empty(max(B.mla_sparse_attend_workspace_size(w.nq, k, 1), 256), dtype=torch.uint8,
-                         device=dev)
-    stream = torch.cuda.current_stream()
-
-    fused_ws = torch.empty(max(B.dsa_mla_decode_fused_workspace_size(w.nq, w.max_len, k, L), 256),
-                           dtype=torch.uint8, device=dev)
-
-    def step():
-        if w.kind == "decode":
-            # the decode read as one call: indexer, top-k, every layer's MLA
-            B.dsa_mla_decode_fused(batch, t["qI"], t["w"], t["kI"], k, t["q"], t["kv"], outs, w.tau, lses, idx,
-                                   fused_ws)
-        else:
-            B.dsa_index_score(batch, t["qI"], t["w"], t["kI"], scores)
-            B.dsa_topk(batch, scores, k, idx, count, tk_ws if tk_ws_n else None)
-            for l in range(L):
-                B.mla_sparse_attend(batch, t["q"][l], t["kv"][l], idx, k, w.tau, outs[l], lses[l], mla_ws)
-
-    def timed(fn, n):
-        """Average ms per call of fn over n calls, HIP events on the launch stream."""
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(n):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n
+    R = Runner(w, dev)
 
     for _ in range(args.warmup):
-        step()
+        R.step()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    ms_per_step = timed(step, args.steps)
+    per_step = R.flushed(R.step, args.steps, flush)
     wall = time.perf_counter() - wall0
-
-    # cold steps: before each, a read of a 512 MiB buffer evicts the 4 MB
-    # L2s and the 256 MB Infinity Cache (with clean lines, so no write-back
-    # competes with the step), so every input comes from HBM; only the step
-    # is timed
-    cold_ms = None
-    if args.cold_reps > 0:
-        flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
-        tot = 0.0
-        for _ in range(args.cold_reps):
-            flush.sum()
-            c0 = torch.cuda.Event(enable_timing=True)
-            c1 = torch.cuda.Event(enable_timing=True)
-            c0.record(stream)
-            step()
-            c1.record(stream)
-            torch.cuda.synchronize()
-            tot += c0.elapsed_time(c1)
-        cold_ms = tot / args.cold_reps
-        del flush
+    ms_per_step = statistics.median(per_step)
+    warm_ms = R.timed(R.step, args.steps)
 
     # per-stage timings of the same kernels, same launch configurations
-    idx_fn = lambda: B.dsa_index_score(batch, t["qI"], t["w"], t["kI"], scores)
-    idx_fn()
-    idx_ms = timed(idx_fn, args.steps)
-    tk_fn = lambda: B.dsa_topk(batch, scores, k, idx, count, tk_ws if tk_ws_n else None)
-    tk_ms = timed(tk_fn, args.steps)
-    mla_fn = lambda: B.mla_sparse_attend(batch, t["q"][0], t["kv"][0], idx, k, w.tau, outs[0], lses[0], mla_ws)
-    mla_ms = timed(mla_fn, args.steps)
-    print(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step (wall {wall * 1e3 / args.steps:.4f}); "
-          f"indexer {idx_ms:.4f} ms, top-k {tk_ms:.4f} ms, one-layer MLA {mla_ms:.4f} ms",
-          file=sys.stderr, flush=True)
+    R.indexer()
+    idx_ms = R.timed(R.indexer, args.steps)
+    tk_ms = R.timed(R.topk, args.steps)
+    mla_ms = R.timed(R.mla, args.steps)
+    print(f"[bench] {args.steps} flushed steps: median {ms_per_step:.4f} ms (min {min(per_step):.4f}, "
+          f"max {max(per_step):.4f}; region {wall:.2f} s); warm {warm_ms:.4f} ms; indexer {idx_ms:.4f} ms, "
+          f"top-k {tk_ms:.4f} ms, one-layer MLA {mla_ms:.4f} ms", file=sys.stderr, flush=True)
 
-    tr = costmodel.path_traffic(w.seq_len, w.q_seq, w.q_pos, w.dtype, L, k, index_dtype=w.index_dtype)
+    tr = R.traffic()
     value = w.nq / (ms_per_step / 1e3)
-    kname = indexer_kernel(w)
-    if w.kind == "prefill" and w.index_dtype != "f32":
-        peak = FP8_MFMA_PEAK_TFLOPS if w.index_dtype == "fp8" else BF16_MFMA_PEAK_TFLOPS
-        achieved = tr["indexer"]["flop"] / (idx_ms / 1e3) / 1e12
-        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
-                    frac=round(achieved / peak, 4), traffic=None,
-                    kernel=kname, per_launch=tr["indexer"]["flop"], per_launch_unit="FLOP")
-    elif w.index_dtype != "f32":
-        achieved = tr["indexer"]["bytes"] / (idx_ms / 1e3) / 1e9
-        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=None,
-                    kernel=kname, per_launch=tr["indexer"]["bytes"], per_launch_unit="B")
-    else:
-        achieved = tr["indexer"]["flop"] / (idx_ms / 1e3) / 1e12
-        roof = dict(bound="alu", achieved=round(achieved, 3), peak=FP32_VALU_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(achieved / FP32_VALU_PEAK_TFLOPS, 4), traffic=None,
-                    kernel="idx_decode_f32", per_launch=tr["indexer"]["flop"], per_launch_unit="FLOP")
+    roof = R.indexer_roofline(idx_ms)
     path_gbps = tr["path_bytes"] / (ms_per_step / 1e3) / 1e9
-    roof["traffic"] = measured_traffic(roof["kernel"], w.name)
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
@@ -226,9 +290,15 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    headline = w
+    R.release()
+    del R
+    bars = None if args.no_extras else extras(args, dev, flush)
+    del flush_buf
+
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(w, args.cpu_seconds)
+        cpu = cpu_baseline(headline, args.cpu_seconds)
 
     rec = {
         "metric": "query-tokens/s for DSA index+top-2048+sparse MLA attn; % HBM/MFMA peak",
@@ -244,22 +314,89 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded; integer indexer inputs in [-3,3], weights in [1,4], N(0,1) queries and cache)",
         "config": {"workload": w.name, "queries": w.nq, "sequences": w.nseq, "max_context": w.max_len,
-                   "layers_sharing_selection": L, "topk": k, "kind": w.kind,
-                   "indexer_dtype": w.index_dtype},
+                   "layers_sharing_selection": w.n_layers, "topk": w.k, "kind": w.kind,
+                   "indexer_dtype": w.index_dtype,
+                   "timing": "median of the timed steps, each after a 512 MiB read that evicts L2 and the "
+                             "Infinity Cache"},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "cold": None if cold_ms is None else {
-            "reps": args.cold_reps, "ms_per_step": round(cold_ms, 5),
-            "value": round(w.nq / (cold_ms / 1e3), 1),
-            "note": "each step after a 512 MiB read that evicts L2 and the Infinity Cache"},
+        "warm": {"ms_per_step": round(warm_ms, 5), "value": round(w.nq / (warm_ms / 1e3), 1),
+                 "note": "the same steps back to back"},
         "path": {"algorithmic_bytes": tr["path_bytes"], "algorithmic_flop": tr["path_flop"],
                  "GBps": round(path_gbps, 1), "hbm_frac": round(path_gbps / HBM_PEAK_GBPS, 4),
                  "step_entry": "dsa_mla_decode_fused" if w.kind == "decode" else
                                "dsa_index_score + dsa_topk + mla_sparse_attend",
+                 "step_ms_min": round(min(per_step), 5), "step_ms_max": round(max(per_step), 5),
                  "indexer_ms": round(idx_ms, 5), "topk_ms": round(tk_ms, 5),
                  "mla_one_layer_ms": round(mla_ms, 5)},
+        "bars": bars,
     }
     print(json.dumps(rec))
+
+
+def extras(args, dev, flush):
+    """The workloads that carry targets, timed in the same run: the ragged
+    4-layer decode batch (whole step against HBM peak, median of flushed
+    steps), the prefill chunk (its indexer against the matrix peak) and the
+    single fp32 query (median of flushed steps)."""
+    from sparse_attention_12_amd import workloads
+    out = {}
+    reps = max(args.cold_reps, 1)
+    # ragged decode batch: whole-step HBM fraction (target 0.60)
+    w = workloads.config(2, args.index_dtype)
+    R = Runner(w, dev)
+    for _ in range(args.warmup):
+        R.step()
+    cold = R.flushed(R.step, reps, flush)
+    warm = R.timed(R.step, reps)
+    R.indexer()
+    idx_ms = R.timed(R.indexer, args.steps)
+    tk_ms = R.timed(R.topk, args.steps)
+    tr = R.traffic()
+    med = statistics.median(cold)
+    gbps = tr["path_bytes"] / (med / 1e3) / 1e9
+    out["ragged_decode_128K"] = {
+        "workload": w.name, "reps": reps, "ms_per_step": round(med, 5), "value": round(w.nq / (med / 1e3), 1),
+        "unit": "query-tokens/s", "warm_ms_per_step": round(warm, 5), "path_bytes": tr["path_bytes"],
+        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4), "warm_hbm_frac": round(tr["path_bytes"] / (warm / 1e3) / 1e9
+                                                                          / HBM_PEAK_GBPS, 4),
+        "target_hbm_frac": 0.60, "indexer_ms": round(idx_ms, 5), "topk_ms": round(tk_ms, 5),
+        "indexer_roofline": R.indexer_roofline(idx_ms)}
+    print(f"[bench] {w.name}: median of {reps} flushed steps {med:.4f} ms ({gbps / HBM_PEAK_GBPS:.3f} of HBM "
+          f"peak), warm {warm:.4f} ms", file=sys.stderr, flush=True)
+    R.release()
+    del R, w
+    # prefill chunk: indexer against the matrix peak (target 0.40 in bf16)
+    w = workloads.config(3, args.index_dtype)
+    R = Runner(w, dev)
+    for _ in range(max(2, args.warmup // 2)):
+        R.step()
+    R.indexer()
+    idx_ms = R.timed(R.indexer, args.steps)
+    cold = R.flushed(R.step, max(10, reps // 5), flush)
+    med = statistics.median(cold)
+    roof = R.indexer_roofline(idx_ms)
+    out["causal_prefill_2048q"] = {
+        "workload": w.name, "reps": len(cold), "ms_per_step": round(med, 5),
+        "value": round(w.nq / (med / 1e3), 1), "unit": "query-tokens/s", "indexer_ms": round(idx_ms, 5),
+        "indexer_mfma_frac": roof["frac"], "target_mfma_frac": 0.40, "indexer_roofline": roof}
+    print(f"[bench] {w.name}: indexer {idx_ms:.4f} ms ({roof['frac']:.3f} of the matrix peak), step "
+          f"{med:.4f} ms", file=sys.stderr, flush=True)
+    R.release()
+    del R, w
+    # single fp32 query
+    w = workloads.config(0)
+    R = Runner(w, dev)
+    for _ in range(args.warmup):
+        R.step()
+    cold = R.flushed(R.step, reps, flush)
+    med = statistics.median(cold)
+    out["decode_b1_L4096_f32"] = {"workload": w.name, "reps": reps, "ms_per_step": round(med, 5),
+                                  "value": round(w.nq / (med / 1e3), 1), "unit": "query-tokens/s",
+                                  "warm_ms_per_step": round(R.timed(R.step, reps), 5)}
+    print(f"[bench] {w.name}: median of {reps} flushed steps {med:.4f} ms", file=sys.stderr, flush=True)
+    R.release()
+    return out
 
 
 def model_step(args, dev):
@@ -337,7 +474,9 @@ def cpu_baseline(w, budget_s: float):
     until the time budget is spent (at least one query).  When one pass over
     the workload takes less than the budget, each query's oracle call is
     repeated so that the timed work lasts about the budget (the inputs of a
-    query are widened once, outside the timed calls)."""
+    query are widened once, outside the timed calls).  Then the oracle on one
+    thread, one query of each decode shape (single query at 4,096, one
+    sequence of 32,768 and of 2^20 positions)."""
     import math as _m
 
     import oracle
@@ -366,10 +505,37 @@ def cpu_baseline(w, budget_s: float):
             r += 1
             if qi == 0 and r == 2:   # size the repeats from the first two calls' time
                 reps = max(2, _m.ceil(budget_s / (el / 2 * w.nq)))
+    nq_done = min(w.nq, qi + 1)
+    del qIw, kI, qs, kvs
+    single = single_thread_oracle()
+    oracle.set_threads(threads)
     return {"value": round(done / el, 3), "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
-            "sample": (f"{done} oracle calls over the first {min(w.nq, qi + 1)} of {w.nq} queries of the same "
+            "cpu_model": cpu_model(),
+            "sample": (f"{done} oracle calls over the first {nq_done} of {w.nq} queries of the same "
                        f"workload (each run {reps}x; {el:.1f} s of oracle time; fp64 C "
-                       f"oracle, OpenMP over positions and heads)")}
+                       f"oracle, OpenMP over positions and heads)"),
+            "single_thread": single}
+
+
+def single_thread_oracle():
+    """Seconds of one oracle call on one thread, one query per decode shape
+    (inputs drawn like the workloads'; the oracle's time does not depend on
+    the values)."""
+    import oracle
+    from sparse_attention_12_amd import workloads as wl
+    oracle.set_threads(1)
+    out = {}
+    for name, L, dt in (("decode_b1_L4096_f32", 4096, "f32"), ("decode_b64_L32768_bf16", 32768, "bf16"),
+                        ("decode_b4_L1048576_bf16", 1 << 20, "bf16")):
+        w = wl.make_decode([L], dt, 1, seed=77, split_kv=(dt == "f32"))
+        args = (w.widen(w.qI)[0], w.w[0], w.widen(w.kI), [w.widen(w.q[0])[0]], [w.widen(w.kv[0])], L, w.k, w.tau)
+        t0 = time.perf_counter()
+        oracle.decode_query(*args)
+        sec = time.perf_counter() - t0
+        out[name] = {"seconds_per_query": round(sec, 3), "query_tokens_per_s": round(1.0 / sec, 4),
+                     "sample": f"one query at {L:,} positions on one thread"}
+        del w, args
+    return out
 
 
 if __name__ == "__main__":

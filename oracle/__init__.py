@@ -69,6 +69,8 @@ def _load():
         lib.oracle_dims.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
+        lib.oracle_set_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_threads.restype = None
         _lib = lib
     return _lib
 
@@ -92,6 +94,11 @@ def dims() -> tuple:
 
 def max_threads() -> int:
     return int(_load().oracle_max_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads of the following oracle calls (timing only)."""
+    _load().oracle_set_threads(int(n))
 
 
 def index_score(qI, w, kI) -> np.ndarray:

@@ -196,3 +196,13 @@ int oracle_max_threads(void) {
   return 1;
 #endif
 }
+
+/* Threads for the following calls (timing only; results do not depend on it). */
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+  extern void omp_set_num_threads(int);
+  omp_set_num_threads(n > 0 ? n : 1);
+#else
+  (void)n;
+#endif
+}

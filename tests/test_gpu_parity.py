@@ -106,6 +106,40 @@ def test_index_score_prefill_exact(B, cache, first, nq, idt):
 
 
 @pytest.mark.parametrize("idt", ["bf16", "fp8"])
+@pytest.mark.parametrize("cache", [16384, 20480, 40960])
+def test_index_score_prefill_key_chunks(B, cache, idt):
+    """2,048 queries at the end of a cache of `cache` positions.  The
+    prefill dispatch starts from 8,192-key chunks and halves them while the
+    grid has fewer than 512 workgroups (64 query blocks here): 16,384
+    positions give chunks of 2,048 (8 x 64 workgroups), 20,480 positions
+    chunks of 2,048 (10 x 64) and 40,960 positions chunks of 4,096 (10 x 64),
+    the lengths the FP8 kernel is instantiated for and the bf16 kernel takes
+    at run time.  One query per 32-query block, the causal edge's first and
+    last among them, has its whole score row compared bit for bit; columns
+    past its candidates stay untouched; its selection equals the oracle's."""
+    nq = 2048
+    w = wl.make_prefill(cache, cache - nq, nq, "bf16", seed=48, index_dtype=idt)
+    t = w.to_torch(DEV)
+    batch = _batch(B, w, t)
+    scores = torch.full((nq, cache), float("nan"), device=DEV)
+    B.dsa_index_score(batch, t["qI"], t["w"], t["kI"], scores)
+    idx = torch.empty((nq, 2048), dtype=torch.int32, device=DEV)
+    B.dsa_topk(batch, scores, 2048, idx)
+    sample = list(range(0, nq, 32)) + [nq - 1]
+    rows = scores[sample].cpu().numpy()
+    idx_h = idx[sample].cpu().numpy()
+    torch.cuda.synchronize()
+    for j, qi in enumerate(sample):
+        n = cache - nq + qi + 1
+        ref = _oracle_scores(w, qi)
+        assert ref.shape[0] == n
+        assert np.array_equal(rows[j, :n].astype(np.float64), ref), f"query {qi}: scores"
+        assert np.all(np.isnan(rows[j, n:])), f"query {qi}: a column past its candidates was written"
+        ref_idx, _ = oracle.topk(ref, 2048)
+        assert np.array_equal(idx_h[j], ref_idx), f"query {qi}: selection"
+
+
+@pytest.mark.parametrize("idt", ["bf16", "fp8"])
 @pytest.mark.parametrize("order", ["grouped", "interleaved"])
 def test_index_score_prefill_several_sequences(B, idt, order):
     """A prefill batch over three sequences (50, 100 and 40 queries at the
