@@ -215,6 +215,29 @@ int32_t dsa_mla_decode_fused(const dsa_batch_t* batch, int32_t index_dtype, cons
                              size_t ws_bytes, void* stream);
 
 /*
+ * Allocation-free fused decode read, for callers that cannot allocate device
+ * memory or pass a workspace (code under graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and errors as
+ * dsa_mla_decode_fused without ws and ws_bytes: its scratch is a library-
+ * owned array of DSA_NOALLOC_SCRATCH_BYTES (128 MiB) in device memory, one
+ * per GPU the library runs on, held until the process ends.  The first call
+ * on a device is its set-up: it looks the array's address up, and the HIP
+ * runtime materialises the array on that device then; later calls allocate
+ * and free nothing.  The call uses the array of the calling thread's current
+ * device, which must be the device of `stream`.  A batch whose dsa_mla_decode_fused_workspace_size exceeds
+ * DSA_NOALLOC_SCRATCH_BYTES is rejected with DSA_ERR_WORKSPACE before
+ * anything is enqueued.  The array keeps the last call's contents and every
+ * call clears what it relies on; calls that overlap on one GPU (different
+ * streams or threads without ordering) share the array and race.
+ */
+#define DSA_NOALLOC_SCRATCH_BYTES (128u << 20)
+int32_t dsa_mla_decode_fused_noalloc(const dsa_batch_t* batch, int32_t index_dtype, const void* q_idx,
+                                     const float* w_idx, const void* k_idx, int32_t k, int32_t n_layers,
+                                     int32_t dtype, int32_t rope_dim, const void* const* q_l,
+                                     const void* const* kv_l, void* const* out_l, float* const* lse_l,
+                                     int32_t out_dtype, float scale, int32_t* idx_out, void* stream);
+
+/*
  * Layer schedule (concept page, change list and layer map).  For each layer:
  *   runs_indexer  1: the layer scores and selects with its own indexer;
  *                 0: it reuses the selection of the most recent layer that

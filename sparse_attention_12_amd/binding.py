@@ -24,8 +24,9 @@ EXPORTS = [
     "dsa_topk_workspace_size", "dsa_topk", "mla_sparse_attend_workspace_size",
     "mla_sparse_attend", "dsa_mla_decode_fused_workspace_size", "dsa_mla_decode_fused",
     "dsa_ml4_layer_plan", "dsa_mla_decode_layers_workspace_size", "dsa_mla_decode_layers",
-    "dsa_rope_frequencies", "dsa_rope_append",
+    "dsa_rope_frequencies", "dsa_rope_append", "dsa_mla_decode_fused_noalloc",
 ]
+NOALLOC_SCRATCH_BYTES = 128 << 20
 ML4_LAYERS = 72
 
 
@@ -70,6 +71,9 @@ def _load() -> ctypes.CDLL:
     lib.dsa_mla_decode_fused.argtypes = [bp, i32, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, i32,
                                          ctypes.c_float, vp, vp, sz, vp]
     lib.dsa_mla_decode_fused.restype = i32
+    lib.dsa_mla_decode_fused_noalloc.argtypes = [bp, i32, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, i32,
+                                                 ctypes.c_float, vp, vp]
+    lib.dsa_mla_decode_fused_noalloc.restype = i32
     pp = ctypes.POINTER(LayerPlan)
     lib.dsa_ml4_layer_plan.argtypes = [i32, pp]
     lib.dsa_ml4_layer_plan.restype = i32
@@ -218,6 +222,25 @@ def dsa_mla_decode_fused(batch: Batch, q_idx, w_idx, k_idx, k: int, q_l: Sequenc
                                     _dt(q_l[0]), _rope(q_l[0], kv_l[0]), cv(qa), cv(kva), cv(oa), cv(la),
                                     _dt(out_l[0]), scale, _p(idx_out),
                                     _p(ws), wsb, _stream(stream)), "dsa_mla_decode_fused")
+    return out_l
+
+
+def dsa_mla_decode_fused_noalloc(batch: Batch, q_idx, w_idx, k_idx, k: int, q_l: Sequence, kv_l: Sequence,
+                                 out_l: Sequence, scale: float, lse_l: Optional[Sequence] = None, idx_out=None,
+                                 stream=None):
+    """The fused decode read in the library's own per-GPU scratch array (no
+    workspace, nothing allocated)."""
+    n = len(q_l)
+    arr = ctypes.c_void_p * n
+    qa = arr(*[t.data_ptr() for t in q_l])
+    kva = arr(*[t.data_ptr() for t in kv_l])
+    oa = arr(*[t.data_ptr() for t in out_l])
+    la = None if lse_l is None else arr(*[(0 if t is None else t.data_ptr()) for t in lse_l])
+    cv = lambda a: None if a is None else ctypes.cast(a, ctypes.c_void_p)
+    _check(lib.dsa_mla_decode_fused_noalloc(batch.ref, _dt(q_idx), _p(q_idx), _p(w_idx), _p(k_idx), k, n,
+                                            _dt(q_l[0]), _rope(q_l[0], kv_l[0]), cv(qa), cv(kva), cv(oa), cv(la),
+                                            _dt(out_l[0]), scale, _p(idx_out), _stream(stream)),
+           "dsa_mla_decode_fused_noalloc")
     return out_l
 
 

@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/dsa_mla.h"
 #include "dsa_common.h"
 #include "kernels.h"
@@ -254,49 +256,30 @@ static int run_selection(const dsa::BatchDev& b, int32_t index_dtype, const void
                     "top-k launch");
 }
 
+// The fused decode read; ws == nullptr with noalloc: run in this device's
+// copy of the allocation-free scratch array.
+static int fused_impl(const dsa_batch_t* batch, int32_t index_dtype, const void* q_idx, const float* w_idx,
+                      const void* k_idx, int32_t k, int32_t n_layers, int32_t dtype, int32_t rope_dim,
+                      const void* const* q_l, const void* const* kv_l, void* const* out_l, float* const* lse_l,
+                      int32_t out_dtype, float scale, int32_t* idx_out, void* ws, size_t ws_bytes, bool noalloc,
+                      void* stream);
+
 int32_t dsa_mla_decode_fused(const dsa_batch_t* batch, int32_t index_dtype, const void* q_idx,
                              const float* w_idx, const void* k_idx, int32_t k, int32_t n_layers,
                              int32_t dtype, int32_t rope_dim, const void* const* q_l, const void* const* kv_l,
                              void* const* out_l, float* const* lse_l, int32_t out_dtype, float scale,
                              int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
-  dsa::BatchDev b;
-  int st = check_batch(batch, &b);
-  if (st) return st;
-  if ((st = check_index_dtype(index_dtype, "index_dtype"))) return st;
-  if ((st = check_dtype(dtype, "dtype"))) return st;
-  if ((st = check_rope(rope_dim))) return st;
-  if ((st = check_dtype(out_dtype, "out_dtype"))) return st;
-  if ((st = check_k(k))) return st;
-  if (n_layers < 1) return fail(DSA_ERR_SHAPE, "n_layers = %d < 1", n_layers);
-  if (n_layers > DSA_MAX_LAYERS) return fail(DSA_ERR_UNSUPPORTED, "n_layers = %d > %d", n_layers, DSA_MAX_LAYERS);
-  if (b.nq == 0) return DSA_OK;
-  REQUIRE_PTR(q_idx);
-  REQUIRE_PTR(w_idx);
-  REQUIRE_PTR(k_idx);
-  if (!q_l || !kv_l || !out_l) return fail(DSA_ERR_NULL, "a per-layer pointer table is NULL");
-  dsa::MlaLayers L;
-  memset(&L, 0, sizeof(L));
-  for (int l = 0; l < n_layers; ++l) {
-    if ((st = check_mla_layer(q_l[l], kv_l[l], out_l[l]))) return st;
-    if (lse_l && lse_l[l] && !aligned(lse_l[l], 4)) return fail(DSA_ERR_ALIGN, "lse_l[%d] is not 4-byte aligned", l);
-    L.q[l] = q_l[l];
-    L.kv[l] = kv_l[l];
-    L.out[l] = out_l[l];
-    L.lse[l] = lse_l ? lse_l[l] : nullptr;
-  }
-  OPTIONAL_PTR4(idx_out);
-  size_t off_idx, off_topk, off_mla;
-  const size_t need = fused_parts(b.nq, b.max_len, k, n_layers, &off_idx, &off_topk, &off_mla);
-  if (ws == nullptr || ws_bytes < need)
-    return fail(DSA_ERR_WORKSPACE, "fused workspace: %zu bytes given, %zu needed", ws_bytes, need);
-  if (!aligned16(ws)) return fail(DSA_ERR_ALIGN, "ws is not 16-byte aligned");
-  char* base = (char*)ws;
-  int32_t* idx = idx_out ? idx_out : (int32_t*)(base + off_idx);
-  hipStream_t s = as_stream(stream);
-  if ((st = run_selection(b, index_dtype, q_idx, w_idx, k_idx, k, idx, base, off_topk, off_mla, s))) return st;
-  return hip_status(dsa::launch_mla(b, dtype, rope_dim, L, n_layers, idx, k, scale, out_dtype, base + off_mla,
-                                    need - off_mla, s),
-                    "fused: MLA launch");
+  return fused_impl(batch, index_dtype, q_idx, w_idx, k_idx, k, n_layers, dtype, rope_dim, q_l, kv_l, out_l, lse_l,
+                    out_dtype, scale, idx_out, ws, ws_bytes, false, stream);
+}
+
+int32_t dsa_mla_decode_fused_noalloc(const dsa_batch_t* batch, int32_t index_dtype, const void* q_idx,
+                                     const float* w_idx, const void* k_idx, int32_t k, int32_t n_layers,
+                                     int32_t dtype, int32_t rope_dim, const void* const* q_l,
+                                     const void* const* kv_l, void* const* out_l, float* const* lse_l,
+                                     int32_t out_dtype, float scale, int32_t* idx_out, void* stream) {
+  return fused_impl(batch, index_dtype, q_idx, w_idx, k_idx, k, n_layers, dtype, rope_dim, q_l, kv_l, out_l, lse_l,
+                    out_dtype, scale, idx_out, nullptr, 0, true, stream);
 }
 
 int32_t dsa_ml4_layer_plan(int32_t n_layers, dsa_layer_plan_t* plan) {
@@ -448,3 +431,91 @@ int32_t dsa_rope_append(const dsa_batch_t* batch, int32_t dtype, int32_t rope_di
 }
 
 }  // extern "C"
+
+// Allocation-free scratch: one copy of this array per GPU, created when the
+// library's code object is loaded on that GPU and held until the process
+// ends.  Host code never uses the array's name as an address: each device's
+// copy is found once with hipGetSymbolAddress (with that device current)
+// and its address kept in scratch_dev.
+static __device__ __align__(256) unsigned char scratch[DSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_dev[SCRATCH_MAX_DEVICES];
+
+// Address of the current device's scratch array (looked up on the first
+// call on that device).
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= SCRATCH_MAX_DEVICES)
+    return fail(DSA_ERR_UNSUPPORTED, "device %d: the allocation-free entry supports devices 0..%d", dev,
+                SCRATCH_MAX_DEVICES - 1);
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr || !aligned(p, 256)) return fail(DSA_ERR_HIP, "scratch array of device %d has no usable address", dev);
+    scratch_dev[dev] = p;
+  }
+  *out = scratch_dev[dev];
+  return DSA_OK;
+}
+}  // namespace
+
+static int fused_impl(const dsa_batch_t* batch, int32_t index_dtype, const void* q_idx, const float* w_idx,
+                      const void* k_idx, int32_t k, int32_t n_layers, int32_t dtype, int32_t rope_dim,
+                      const void* const* q_l, const void* const* kv_l, void* const* out_l, float* const* lse_l,
+                      int32_t out_dtype, float scale, int32_t* idx_out, void* ws, size_t ws_bytes, bool noalloc,
+                      void* stream) {
+  dsa::BatchDev b;
+  int st = check_batch(batch, &b);
+  if (st) return st;
+  if ((st = check_index_dtype(index_dtype, "index_dtype"))) return st;
+  if ((st = check_dtype(dtype, "dtype"))) return st;
+  if ((st = check_rope(rope_dim))) return st;
+  if ((st = check_dtype(out_dtype, "out_dtype"))) return st;
+  if ((st = check_k(k))) return st;
+  if (n_layers < 1) return fail(DSA_ERR_SHAPE, "n_layers = %d < 1", n_layers);
+  if (n_layers > DSA_MAX_LAYERS) return fail(DSA_ERR_UNSUPPORTED, "n_layers = %d > %d", n_layers, DSA_MAX_LAYERS);
+  if (b.nq == 0) return DSA_OK;
+  REQUIRE_PTR(q_idx);
+  REQUIRE_PTR(w_idx);
+  REQUIRE_PTR(k_idx);
+  if (!q_l || !kv_l || !out_l) return fail(DSA_ERR_NULL, "a per-layer pointer table is NULL");
+  dsa::MlaLayers L;
+  memset(&L, 0, sizeof(L));
+  for (int l = 0; l < n_layers; ++l) {
+    if ((st = check_mla_layer(q_l[l], kv_l[l], out_l[l]))) return st;
+    if (lse_l && lse_l[l] && !aligned(lse_l[l], 4)) return fail(DSA_ERR_ALIGN, "lse_l[%d] is not 4-byte aligned", l);
+    L.q[l] = q_l[l];
+    L.kv[l] = kv_l[l];
+    L.out[l] = out_l[l];
+    L.lse[l] = lse_l ? lse_l[l] : nullptr;
+  }
+  OPTIONAL_PTR4(idx_out);
+  size_t off_idx, off_topk, off_mla;
+  const size_t need = fused_parts(b.nq, b.max_len, k, n_layers, &off_idx, &off_topk, &off_mla);
+  if (noalloc) {
+    if (need > (size_t)DSA_NOALLOC_SCRATCH_BYTES)
+      return fail(DSA_ERR_WORKSPACE,
+                  "this batch needs %zu bytes of scratch; the allocation-free entry holds %zu (use "
+                  "dsa_mla_decode_fused with a workspace)",
+                  need, (size_t)DSA_NOALLOC_SCRATCH_BYTES);
+    if ((st = scratch_address(&ws))) return st;
+    ws_bytes = (size_t)DSA_NOALLOC_SCRATCH_BYTES;
+  }
+  if (ws == nullptr || ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "fused workspace: %zu bytes given, %zu needed", ws_bytes, need);
+  if (!aligned16(ws)) return fail(DSA_ERR_ALIGN, "ws is not 16-byte aligned");
+  char* base = (char*)ws;
+  int32_t* idx = idx_out ? idx_out : (int32_t*)(base + off_idx);
+  hipStream_t s = as_stream(stream);
+  if ((st = run_selection(b, index_dtype, q_idx, w_idx, k_idx, k, idx, base, off_topk, off_mla, s))) return st;
+  return hip_status(dsa::launch_mla(b, dtype, rope_dim, L, n_layers, idx, k, scale, out_dtype, base + off_mla,
+                                    need - off_mla, s),
+                    "fused: MLA launch");
+}

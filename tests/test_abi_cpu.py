@@ -35,6 +35,8 @@ def lib():
     l.mla_sparse_attend_workspace_size.restype = sz
     l.dsa_mla_decode_fused.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, i32,
                                        ctypes.c_float, vp, vp, sz, vp]
+    l.dsa_mla_decode_fused_noalloc.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, i32,
+                                               ctypes.c_float, vp, vp]
     l.dsa_mla_decode_fused_workspace_size.argtypes = [i32, i32, i32, i32]
     l.dsa_mla_decode_fused_workspace_size.restype = sz
     l.dsa_ml4_layer_plan.argtypes = [i32, vp]
@@ -66,7 +68,7 @@ def _batch(nq=2, nseq=2, max_len=100):
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -385,3 +387,27 @@ def test_alignment_contract_rope_append(lib):
         assert call(**{kw: A8}) == ALIGN, kw
     assert call(s=A8, bb=A) == ALIGN
     assert call(s=A, bb=A8) == ALIGN
+
+
+def test_noalloc_fused_validation(lib):
+    """The allocation-free fused entry validates like the fused one and
+    rejects, before anything is enqueued (no HIP call), a batch whose
+    workspace would exceed its 128 MiB scratch array."""
+    tab = lambda: ctypes.cast((ctypes.c_void_p * 2)(A, A), ctypes.c_void_p)
+
+    def call(b, n_layers=2, k=2048, idt=1, q=None):
+        return lib.dsa_mla_decode_fused_noalloc(ctypes.byref(b), idt, A, A, A, k, n_layers, 1, 64,
+                                                q if q is not None else tab(), tab(), tab(), None, 0, 0.07, None,
+                                                None)
+
+    assert call(_batch(), idt=7) == DTYPE
+    assert call(_batch(), n_layers=17) == UNSUPPORTED
+    assert call(_batch(), k=0) == SHAPE
+    mis = ctypes.cast((ctypes.c_void_p * 2)(A, MIS), ctypes.c_void_p)
+    assert call(_batch(), q=mis) == ALIGN
+    big = _batch(nq=64, nseq=64, max_len=1 << 20)
+    need = lib.dsa_mla_decode_fused_workspace_size(64, 1 << 20, 2048, 2)
+    assert need > 128 << 20
+    assert call(big) == WORKSPACE
+    assert b"allocation-free" in lib.dsa_last_error()
+    assert call(_batch(nq=0)) == OK
