@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdsa_mla.so")
-SOURCES = ["abi.hip", "indexer.hip", "topk.hip", "mla.hip", "rope.hip"]
+SOURCES = ["abi.hip", "noalloc.hip", "plan.cpp", "indexer.hip", "topk.hip", "mla.hip", "rope.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

@@ -5,9 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
-#include <mutex>
-
 #include "../../include/dsa_mla.h"
+#include "abi_internal.h"
 #include "dsa_common.h"
 #include "kernels.h"
 
@@ -15,10 +14,15 @@ namespace {
 
 thread_local char g_err[512] = "";
 
+int vfail(int status, const char* fmt, va_list ap) {
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  return status;
+}
+
 int fail(int status, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  vfail(status, fmt, ap);
   va_end(ap);
   return status;
 }
@@ -102,9 +106,18 @@ int check_k(int32_t k) {
 
 hipStream_t as_stream(void* s) { return (hipStream_t)s; }
 
-size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
-
 }  // namespace
+
+namespace dsa {
+int abi_fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vfail(status, fmt, ap);
+  va_end(ap);
+  return status;
+}
+int abi_hip_status(hipError_t e, const char* what) { return hip_status(e, what); }
+}  // namespace dsa
 
 extern "C" {
 
@@ -146,6 +159,7 @@ size_t dsa_topk_workspace_size(int32_t nq, int32_t max_len, int32_t k) {
   if (nq <= 0 || max_len <= 0 || k <= 0) return 0;
   return dsa::topk_workspace_bytes(nq, max_len, k);
 }
+
 
 int32_t dsa_topk(const dsa_batch_t* batch, const float* scores, int64_t ld, int32_t k, int32_t* idx,
                  int32_t* count, void* ws, size_t ws_bytes, void* stream) {
@@ -210,76 +224,39 @@ int32_t mla_sparse_attend(const dsa_batch_t* batch, int32_t dtype, int32_t rope_
                     "mla_sparse_attend launch");
 }
 
-static size_t fused_parts(int32_t nq, int32_t max_len, int32_t k, int32_t n_layers, size_t* off_idx,
-                          size_t* off_topk, size_t* off_mla) {
-  size_t off = 0;
-  // scores [nq][max_len] float32
-  off = align_up(off + (size_t)nq * (size_t)max_len * sizeof(float));
-  *off_idx = off;
-  off = align_up(off + (size_t)nq * (size_t)k * sizeof(int32_t));
-  *off_topk = off;
-  off = align_up(off + dsa::topk_workspace_bytes(nq, max_len, k));
-  *off_mla = off;
-  // a launch over fewer layers can take more splits: size for the largest
-  size_t m = 0;
-  for (int n = 1; n <= n_layers; ++n)
-    for (int dt = 0; dt < 2; ++dt) {
-      const size_t x = dsa::mla_workspace_bytes(dt, nq, k, n);
-      m = x > m ? x : m;
-    }
-  off = align_up(off + m);
-  return off;
-}
-
 size_t dsa_mla_decode_fused_workspace_size(int32_t nq, int32_t max_len, int32_t k, int32_t n_layers) {
   if (nq <= 0 || max_len <= 0 || k <= 0 || n_layers <= 0) return 0;
-  size_t a, c, d;
-  return fused_parts(nq, max_len, k, n_layers, &a, &c, &d);
+  return dsa::fused_layout(nq, max_len, k, n_layers).bytes;
 }
 
-// Indexer scores, then top-k into idx, using the scores and top-k parts of
-// a fused-layout workspace; the indexer launch also clears the top-k
-// histograms, so the workspace needs no clearing by the caller.
+// Indexer scores, then top-k into idx, in the scores, histogram and top-k
+// parts of a fused-layout workspace.  The indexer counts the top-k's
+// first-level histograms into the histogram part, which each call leaves
+// zero (the top-k checks it and clears it after use), so the workspace
+// needs no clearing by the caller.
 static int run_selection(const dsa::BatchDev& b, int32_t index_dtype, const void* q_idx, const float* w_idx,
-                         const void* k_idx, int32_t k, int32_t* idx, char* base, size_t off_topk, size_t off_mla,
+                         const void* k_idx, int32_t k, int32_t* idx, char* base, const dsa::FusedLayout& f,
                          hipStream_t s) {
   int st;
-  float* scores = (float*)base;
-  dsa::ZeroSpans z;
-  z.s[0] = dsa::topk_zero_span(base + off_topk, b.nq, b.max_len);
-  z.s[1] = dsa::ZeroSpan{nullptr, 0, 0};
-  if ((st = hip_status(dsa::launch_index_score(b, index_dtype, q_idx, w_idx, k_idx, scores, b.max_len, s, &z),
-                       "index score launch")))
+  float* scores = (float*)(base + f.scores);
+  uint32_t* hist = (uint32_t*)(base + f.hist);
+  bool counted = false;
+  if ((st = hip_status(
+           dsa::launch_index_score(b, index_dtype, q_idx, w_idx, k_idx, scores, b.max_len, s, hist, &counted),
+           "index score launch")))
     return st;
-  return hip_status(dsa::launch_topk(b, scores, b.max_len, k, idx, nullptr, base + off_topk, off_mla - off_topk, s,
-                                     true),
+  return hip_status(dsa::launch_topk(b, scores, b.max_len, k, idx, nullptr, base + f.topk, f.mla - f.topk, s,
+                                     counted ? hist : nullptr),
                     "top-k launch");
 }
-
-// The fused decode read; ws == nullptr with noalloc: run in this device's
-// copy of the allocation-free scratch array.
-static int fused_impl(const dsa_batch_t* batch, int32_t index_dtype, const void* q_idx, const float* w_idx,
-                      const void* k_idx, int32_t k, int32_t n_layers, int32_t dtype, int32_t rope_dim,
-                      const void* const* q_l, const void* const* kv_l, void* const* out_l, float* const* lse_l,
-                      int32_t out_dtype, float scale, int32_t* idx_out, void* ws, size_t ws_bytes, bool noalloc,
-                      void* stream);
 
 int32_t dsa_mla_decode_fused(const dsa_batch_t* batch, int32_t index_dtype, const void* q_idx,
                              const float* w_idx, const void* k_idx, int32_t k, int32_t n_layers,
                              int32_t dtype, int32_t rope_dim, const void* const* q_l, const void* const* kv_l,
                              void* const* out_l, float* const* lse_l, int32_t out_dtype, float scale,
                              int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
-  return fused_impl(batch, index_dtype, q_idx, w_idx, k_idx, k, n_layers, dtype, rope_dim, q_l, kv_l, out_l, lse_l,
-                    out_dtype, scale, idx_out, ws, ws_bytes, false, stream);
-}
-
-int32_t dsa_mla_decode_fused_noalloc(const dsa_batch_t* batch, int32_t index_dtype, const void* q_idx,
-                                     const float* w_idx, const void* k_idx, int32_t k, int32_t n_layers,
-                                     int32_t dtype, int32_t rope_dim, const void* const* q_l,
-                                     const void* const* kv_l, void* const* out_l, float* const* lse_l,
-                                     int32_t out_dtype, float scale, int32_t* idx_out, void* stream) {
-  return fused_impl(batch, index_dtype, q_idx, w_idx, k_idx, k, n_layers, dtype, rope_dim, q_l, kv_l, out_l, lse_l,
-                    out_dtype, scale, idx_out, nullptr, 0, true, stream);
+  return dsa::fused_read(batch, index_dtype, q_idx, w_idx, k_idx, k, n_layers, dtype, rope_dim, q_l, kv_l, out_l,
+                         lse_l, out_dtype, scale, idx_out, ws, ws_bytes, nullptr, stream);
 }
 
 int32_t dsa_ml4_layer_plan(int32_t n_layers, dsa_layer_plan_t* plan) {
@@ -327,8 +304,7 @@ size_t dsa_mla_decode_layers_workspace_size(int32_t nq, int32_t max_len, int32_t
                                             const dsa_layer_plan_t* plan) {
   int group = 0;
   if (nq <= 0 || max_len <= 0 || k <= 0 || check_plan(n_layers, plan, &group)) return 0;
-  size_t a, c, d;
-  return fused_parts(nq, max_len, k, group, &a, &c, &d);
+  return dsa::fused_layout(nq, max_len, k, group).bytes;
 }
 
 int32_t dsa_mla_decode_layers(const dsa_batch_t* batch, int32_t n_layers, const dsa_layer_plan_t* plan,
@@ -361,8 +337,8 @@ int32_t dsa_mla_decode_layers(const dsa_batch_t* batch, int32_t n_layers, const 
     if ((st = check_mla_layer(q_l[l], kv_l[plan[l].kv_source], out_l[l]))) return st;
     if (lse_l && lse_l[l] && !aligned(lse_l[l], 4)) return fail(DSA_ERR_ALIGN, "lse_l[%d] is not 4-byte aligned", l);
   }
-  size_t off_idx, off_topk, off_mla;
-  const size_t need = fused_parts(b.nq, b.max_len, k, max_group, &off_idx, &off_topk, &off_mla);
+  const dsa::FusedLayout f = dsa::fused_layout(b.nq, b.max_len, k, max_group);
+  const size_t need = f.bytes;
   if (ws == nullptr || ws_bytes < need)
     return fail(DSA_ERR_WORKSPACE, "layers workspace: %zu bytes given, %zu needed", ws_bytes, need);
   if (!aligned16(ws)) return fail(DSA_ERR_ALIGN, "ws is not 16-byte aligned");
@@ -371,10 +347,8 @@ int32_t dsa_mla_decode_layers(const dsa_batch_t* batch, int32_t n_layers, const 
   int32_t* idx = nullptr;
   for (int l = 0; l < n_layers;) {
     if (plan[l].runs_indexer) {
-      idx = (idx_l && idx_l[l]) ? idx_l[l] : (int32_t*)(base + off_idx);
-      if ((st = run_selection(b, index_dtype, q_idx_l[l], w_idx_l[l], k_idx_l[l], k, idx, base, off_topk, off_mla,
-                              s)))
-        return st;
+      idx = (idx_l && idx_l[l]) ? idx_l[l] : (int32_t*)(base + f.idx);
+      if ((st = run_selection(b, index_dtype, q_idx_l[l], w_idx_l[l], k_idx_l[l], k, idx, base, f, s))) return st;
     }
     // this layer and the following ones that reuse the same selection with
     // the same rotary width: one MLA launch
@@ -391,7 +365,7 @@ int32_t dsa_mla_decode_layers(const dsa_batch_t* batch, int32_t n_layers, const 
       L.lse[j] = lse_l ? lse_l[l + j] : nullptr;
     }
     if ((st = hip_status(dsa::launch_mla(b, dtype, plan[l].rope_dim, L, n, idx, k, scale, out_dtype,
-                                         base + off_mla, need - off_mla, s),
+                                         base + f.mla, need - f.mla, s),
                          "layers: MLA launch")))
       return st;
     l += n;
@@ -432,45 +406,13 @@ int32_t dsa_rope_append(const dsa_batch_t* batch, int32_t dtype, int32_t rope_di
 
 }  // extern "C"
 
-// Allocation-free scratch: one copy of this array per GPU, created when the
-// library's code object is loaded on that GPU and held until the process
-// ends.  Host code never uses the array's name as an address: each device's
-// copy is found once with hipGetSymbolAddress (with that device current)
-// and its address kept in scratch_dev.
-static __device__ __align__(256) unsigned char scratch[DSA_NOALLOC_SCRATCH_BYTES];
+namespace dsa {
 
-namespace {
-constexpr int SCRATCH_MAX_DEVICES = 64;
-std::mutex scratch_mu;
-void* scratch_dev[SCRATCH_MAX_DEVICES];
-
-// Address of the current device's scratch array (looked up on the first
-// call on that device).
-int scratch_address(void** out) {
-  int dev = -1;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
-  if (dev < 0 || dev >= SCRATCH_MAX_DEVICES)
-    return fail(DSA_ERR_UNSUPPORTED, "device %d: the allocation-free entry supports devices 0..%d", dev,
-                SCRATCH_MAX_DEVICES - 1);
-  std::lock_guard<std::mutex> lock(scratch_mu);
-  if (scratch_dev[dev] == nullptr) {
-    void* p = nullptr;
-    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
-    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
-    if (p == nullptr || !aligned(p, 256)) return fail(DSA_ERR_HIP, "scratch array of device %d has no usable address", dev);
-    scratch_dev[dev] = p;
-  }
-  *out = scratch_dev[dev];
-  return DSA_OK;
-}
-}  // namespace
-
-static int fused_impl(const dsa_batch_t* batch, int32_t index_dtype, const void* q_idx, const float* w_idx,
-                      const void* k_idx, int32_t k, int32_t n_layers, int32_t dtype, int32_t rope_dim,
-                      const void* const* q_l, const void* const* kv_l, void* const* out_l, float* const* lse_l,
-                      int32_t out_dtype, float scale, int32_t* idx_out, void* ws, size_t ws_bytes, bool noalloc,
-                      void* stream) {
+int fused_read(const dsa_batch_t* batch, int32_t index_dtype, const void* q_idx, const float* w_idx,
+               const void* k_idx, int32_t k, int32_t n_layers, int32_t dtype, int32_t rope_dim,
+               const void* const* q_l, const void* const* kv_l, void* const* out_l, float* const* lse_l,
+               int32_t out_dtype, float scale, int32_t* idx_out, void* ws, size_t ws_bytes, ScratchFn scratch,
+               void* stream) {
   dsa::BatchDev b;
   int st = check_batch(batch, &b);
   if (st) return st;
@@ -497,25 +439,19 @@ static int fused_impl(const dsa_batch_t* batch, int32_t index_dtype, const void*
     L.lse[l] = lse_l ? lse_l[l] : nullptr;
   }
   OPTIONAL_PTR4(idx_out);
-  size_t off_idx, off_topk, off_mla;
-  const size_t need = fused_parts(b.nq, b.max_len, k, n_layers, &off_idx, &off_topk, &off_mla);
-  if (noalloc) {
-    if (need > (size_t)DSA_NOALLOC_SCRATCH_BYTES)
-      return fail(DSA_ERR_WORKSPACE,
-                  "this batch needs %zu bytes of scratch; the allocation-free entry holds %zu (use "
-                  "dsa_mla_decode_fused with a workspace)",
-                  need, (size_t)DSA_NOALLOC_SCRATCH_BYTES);
-    if ((st = scratch_address(&ws))) return st;
-    ws_bytes = (size_t)DSA_NOALLOC_SCRATCH_BYTES;
-  }
+  const dsa::FusedLayout f = dsa::fused_layout(b.nq, b.max_len, k, n_layers);
+  const size_t need = f.bytes;
+  if (scratch != nullptr && (st = scratch(need, &ws, &ws_bytes))) return st;
   if (ws == nullptr || ws_bytes < need)
     return fail(DSA_ERR_WORKSPACE, "fused workspace: %zu bytes given, %zu needed", ws_bytes, need);
   if (!aligned16(ws)) return fail(DSA_ERR_ALIGN, "ws is not 16-byte aligned");
   char* base = (char*)ws;
-  int32_t* idx = idx_out ? idx_out : (int32_t*)(base + off_idx);
+  int32_t* idx = idx_out ? idx_out : (int32_t*)(base + f.idx);
   hipStream_t s = as_stream(stream);
-  if ((st = run_selection(b, index_dtype, q_idx, w_idx, k_idx, k, idx, base, off_topk, off_mla, s))) return st;
-  return hip_status(dsa::launch_mla(b, dtype, rope_dim, L, n_layers, idx, k, scale, out_dtype, base + off_mla,
-                                    need - off_mla, s),
+  if ((st = run_selection(b, index_dtype, q_idx, w_idx, k_idx, k, idx, base, f, s))) return st;
+  return hip_status(dsa::launch_mla(b, dtype, rope_dim, L, n_layers, idx, k, scale, out_dtype, base + f.mla,
+                                    need - f.mla, s),
                     "fused: MLA launch");
 }
+
+}  // namespace dsa

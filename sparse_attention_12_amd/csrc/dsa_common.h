@@ -5,15 +5,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-namespace dsa {
+#include "plan.h"
 
-constexpr int HI = 32;    // indexer heads
-constexpr int DI = 128;   // indexer head width
-constexpr int H = 64;     // attention heads
-constexpr int DC = 512;   // latent (= value) width
-constexpr int DR = 64;    // rotary key width
-constexpr int D = 576;    // cache row
-constexpr int KMAX = 2048;
+namespace dsa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));

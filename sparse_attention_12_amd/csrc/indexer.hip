@@ -8,7 +8,11 @@
 // Decode (one query per sequence) is a stream over the query's keys: heads
 // sit on the M axis of 16x16x32 MFMA tiles and keys on N, so each lane ends
 // with 8 of the 32 head dot products of one key; the ReLU and the weighted
-// head sum stay in registers and finish with two cross-lane adds.
+// head sum stay in registers and finish with two cross-lane adds.  Decode
+// batches of up to IDX_BAL_MAXQ queries can also count every score they
+// store into a per-query histogram of its top TK_BITS1 key bits: the
+// top-k's first radix level, built where the scores are made, so the
+// selection need not read them a first time to count them.
 //
 // Prefill (many queries per sequence) is a blocked product: a workgroup
 // keeps 32 queries' indexer rows in registers (4 per wave) and streams key
@@ -20,17 +24,21 @@
 namespace dsa {
 
 // Zeroes query q's words of every span (see ZeroSpans in kernels.h).
-__device__ inline void zero_query_spans(const ZeroSpans& z, int q, int tid, int nthreads) {
+__global__ __launch_bounds__(256) void zero_spans_kernel(ZeroSpans z) {
+  const int q = blockIdx.x;
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     if (z.s[s].base == nullptr) continue;
     uint32_t* p = z.s[s].base + (int64_t)q * z.s[s].stride;
-    for (int i = tid; i < z.s[s].count; i += nthreads) p[i] = 0u;
+    for (int i = threadIdx.x; i < z.s[s].count; i += 256) p[i] = 0u;
   }
 }
 
-__global__ __launch_bounds__(256) void zero_spans_kernel(ZeroSpans z) {
-  zero_query_spans(z, blockIdx.x, threadIdx.x, 256);
+// Adds a stored score to the workgroup's LDS histogram (bin: the score's
+// top TK_BITS1 order-preserving key bits, as the top-k reads them).
+template <bool HIST>
+__device__ __forceinline__ void count_score(uint32_t* lh, float x) {
+  if (HIST) atomicAdd(&lh[score_key(x) >> TK_SHIFT1], 1u);
 }
 
 // ---------------------------------------------------------------------------
@@ -52,11 +60,13 @@ struct KeyTile {
 
 // Scores of query q's keys [base, end): the four waves of the workgroup
 // take interleaved 32-key steps, each wave keeping four steps of loads in
-// flight.  Waves are independent (no LDS, no barriers).
+// flight.  Waves are independent (no barriers); with HIST every stored
+// score is also counted into the LDS histogram lh.
+template <bool HIST>
 __device__ __forceinline__ void idx_decode_range(const BatchDev& b, const uint16_t* __restrict__ qI,
                                                  const float* __restrict__ w, const uint16_t* __restrict__ kI,
                                                  float* __restrict__ scores, int64_t ld, int q, int64_t row0,
-                                                 int base, int end) {
+                                                 int base, int end, uint32_t* lh) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int c16 = lane & 15;  // A row (head within block) / B column (key within block)
@@ -112,7 +122,10 @@ __device__ __forceinline__ void idx_decode_range(const BatchDev& b, const uint16
       }
       part = rows4_sum(part);
       const int key = k + kb2 * 16 + c16;
-      if (g == 0 && key < end) out[key] = part;
+      if (g == 0 && key < end) {
+        out[key] = part;
+        count_score<HIST>(lh, part);
+      }
     }
   };
 
@@ -155,10 +168,11 @@ __device__ __forceinline__ i32x8 cat32(u32x4 lo, u32x4 hi) {
   return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+template <bool HIST>
 __device__ __forceinline__ void idx_decode_range_f8(const BatchDev& b, const uint8_t* __restrict__ qI,
                                                     const float* __restrict__ w, const uint8_t* __restrict__ kI,
                                                     float* __restrict__ scores, int64_t ld, int q, int64_t row0,
-                                                    int base, int end) {
+                                                    int base, int end, uint32_t* lh) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int c16 = lane & 15;
@@ -205,7 +219,10 @@ __device__ __forceinline__ void idx_decode_range_f8(const BatchDev& b, const uin
       }
       part = rows4_sum(part);
       const int key = k + kb4 * 16 + c16;
-      if (g == 0 && key < end) out[key] = part;
+      if (g == 0 && key < end) {
+        out[key] = part;
+        count_score<HIST>(lh, part);
+      }
     }
   };
 
@@ -231,13 +248,14 @@ __device__ __forceinline__ void idx_decode_range_f8(const BatchDev& b, const uin
 }
 
 // Scores of keys [base, end) of query q in the given storage.
-template <bool FP8>
+template <bool FP8, bool HIST>
 __device__ __forceinline__ void idx_decode_any(const BatchDev& b, const void* qI, const float* w, const void* kI,
-                                               float* scores, int64_t ld, int q, int64_t row0, int base, int end) {
+                                               float* scores, int64_t ld, int q, int64_t row0, int base, int end,
+                                               uint32_t* lh) {
   if (FP8)
-    idx_decode_range_f8(b, (const uint8_t*)qI, w, (const uint8_t*)kI, scores, ld, q, row0, base, end);
+    idx_decode_range_f8<HIST>(b, (const uint8_t*)qI, w, (const uint8_t*)kI, scores, ld, q, row0, base, end, lh);
   else
-    idx_decode_range(b, (const uint16_t*)qI, w, (const uint16_t*)kI, scores, ld, q, row0, base, end);
+    idx_decode_range<HIST>(b, (const uint16_t*)qI, w, (const uint16_t*)kI, scores, ld, q, row0, base, end, lh);
 }
 
 // Grid (chunks, queries): workgroup (c, q) scores keys [c*chunk, (c+1)*chunk)
@@ -245,32 +263,34 @@ __device__ __forceinline__ void idx_decode_any(const BatchDev& b, const void* qI
 template <bool FP8>
 __device__ __forceinline__ void idx_decode_chunked(BatchDev b, const void* __restrict__ qI, const float* __restrict__ w,
                                                    const void* __restrict__ kI, float* __restrict__ scores,
-                                                   int64_t ld, int chunk, ZeroSpans z) {
+                                                   int64_t ld, int chunk) {
   const int q = blockIdx.y;
-  if (blockIdx.x == 0) zero_query_spans(z, q, threadIdx.x, IDX_DEC_THREADS);
   const QueryRange r = query_range(b, q);
   const int base = blockIdx.x * chunk;
   if (base >= r.n) return;
-  idx_decode_any<FP8>(b, qI, w, kI, scores, ld, q, r.row0, base, min(base + chunk, r.n));
+  idx_decode_any<FP8, false>(b, qI, w, kI, scores, ld, q, r.row0, base, min(base + chunk, r.n), nullptr);
 }
 
 // Balanced decode: the batch's keys, laid end to end in query order, are
 // cut into gridDim.x equal ranges, one per workgroup, so ragged lengths
 // cost no imbalance and every workgroup streams a long range.  Each
 // workgroup first forms the prefix sums of the candidate counts itself.
-constexpr int IDX_BAL_MAXQ = 1024;
-constexpr int IDX_BAL_GRID = 512;
-
-template <bool FP8>
+// With HIST, a workgroup counts its scores of each query into an LDS
+// histogram and adds the non-zero bins to hist[q] when it moves past the
+// query (a handful of global atomics per query and workgroup: the scores
+// crowd into few bins).
+template <bool FP8, bool HIST>
 __device__ __forceinline__ void idx_decode_bal(BatchDev b, const void* __restrict__ qI, const float* __restrict__ w,
                                                const void* __restrict__ kI, float* __restrict__ scores, int64_t ld,
-                                               ZeroSpans z) {
+                                               uint32_t* __restrict__ hist) {
   __shared__ int64_t pre[IDX_BAL_MAXQ + 1];
   __shared__ int64_t wtot[IDX_DEC_WAVES];
+  __shared__ uint32_t lh[HIST ? TK_BINS1 : 1];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  for (int q = blockIdx.x; q < b.nq; q += gridDim.x) zero_query_spans(z, q, tid, IDX_DEC_THREADS);
+  if (HIST)
+    for (int i = tid; i < TK_BINS1; i += IDX_DEC_THREADS) lh[i] = 0u;
   // candidate counts -> exclusive prefix sums in pre[0..nq]
   constexpr int PER = IDX_BAL_MAXQ / IDX_DEC_THREADS;
   int64_t cnt[PER];
@@ -315,30 +335,44 @@ __device__ __forceinline__ void idx_decode_bal(BatchDev b, const void* __restric
     const int64_t s1 = min(hi, pre[q + 1]) - pre[q];
     if (s0 >= s1) continue;
     const int s = b.q_seq[q];
-    idx_decode_any<FP8>(b, qI, w, kI, scores, ld, q, b.seq_row0[s], (int)s0, (int)s1);
+    idx_decode_any<FP8, HIST>(b, qI, w, kI, scores, ld, q, b.seq_row0[s], (int)s0, (int)s1, lh);
+    if (HIST) {
+      __syncthreads();
+      uint32_t* gq = hist + (int64_t)q * TK_BINS1;
+      for (int i = tid; i < TK_BINS1; i += IDX_DEC_THREADS) {
+        const uint32_t v = lh[i];
+        if (v) {
+          atomicAdd(&gq[i], v);
+          lh[i] = 0u;
+        }
+      }
+      __syncthreads();
+    }
   }
 }
 
 // One kernel per storage type, so profiles name what ran.
+template <bool HIST>
 __global__ __launch_bounds__(IDX_DEC_THREADS) void idx_decode_bf16_bal(BatchDev b, const void* qI, const float* w,
                                                                        const void* kI, float* scores, int64_t ld,
-                                                                       ZeroSpans z) {
-  idx_decode_bal<false>(b, qI, w, kI, scores, ld, z);
+                                                                       uint32_t* hist) {
+  idx_decode_bal<false, HIST>(b, qI, w, kI, scores, ld, hist);
 }
+template <bool HIST>
 __global__ __launch_bounds__(IDX_DEC_THREADS) void idx_decode_fp8_bal(BatchDev b, const void* qI, const float* w,
                                                                       const void* kI, float* scores, int64_t ld,
-                                                                      ZeroSpans z) {
-  idx_decode_bal<true>(b, qI, w, kI, scores, ld, z);
+                                                                      uint32_t* hist) {
+  idx_decode_bal<true, HIST>(b, qI, w, kI, scores, ld, hist);
 }
 __global__ __launch_bounds__(IDX_DEC_THREADS) void idx_decode_bf16(BatchDev b, const void* qI, const float* w,
-                                                                   const void* kI, float* scores, int64_t ld, int chunk,
-                                                                   ZeroSpans z) {
-  idx_decode_chunked<false>(b, qI, w, kI, scores, ld, chunk, z);
+                                                                   const void* kI, float* scores, int64_t ld,
+                                                                   int chunk) {
+  idx_decode_chunked<false>(b, qI, w, kI, scores, ld, chunk);
 }
 __global__ __launch_bounds__(IDX_DEC_THREADS) void idx_decode_fp8(BatchDev b, const void* qI, const float* w,
-                                                                  const void* kI, float* scores, int64_t ld, int chunk,
-                                                                  ZeroSpans z) {
-  idx_decode_chunked<true>(b, qI, w, kI, scores, ld, chunk, z);
+                                                                  const void* kI, float* scores, int64_t ld,
+                                                                  int chunk) {
+  idx_decode_chunked<true>(b, qI, w, kI, scores, ld, chunk);
 }
 
 // ---------------------------------------------------------------------------
@@ -348,11 +382,10 @@ constexpr int IDX_F32_THREADS = 256;
 
 __global__ __launch_bounds__(IDX_F32_THREADS) void idx_decode_f32(
     BatchDev b, const float* __restrict__ qI, const float* __restrict__ w,
-    const float* __restrict__ kI, float* __restrict__ scores, int64_t ld, ZeroSpans z) {
+    const float* __restrict__ kI, float* __restrict__ scores, int64_t ld) {
   __shared__ float qs[HI * DI];
   __shared__ float wsh[HI];
   const int q = blockIdx.y;
-  if (blockIdx.x == 0) zero_query_spans(z, q, threadIdx.x, IDX_F32_THREADS);
   const QueryRange r = query_range(b, q);
   const int base = blockIdx.x * IDX_F32_THREADS;
   if (base >= r.n) return;
@@ -387,11 +420,8 @@ __global__ __launch_bounds__(IDX_F32_THREADS) void idx_decode_f32(
 constexpr int PF_THREADS = 512;
 constexpr int PF_WAVES = PF_THREADS / 64;
 constexpr int PF_QPW = 4;                    // queries per wave
-constexpr int PF_QB = PF_WAVES * PF_QPW;     // queries per workgroup
+static_assert(PF_QB == PF_WAVES * PF_QPW, "queries per workgroup");
 constexpr int PF_TK = 32;                    // keys per LDS tile
-constexpr int PF_KC = 8192;                  // keys per workgroup (at most)
-constexpr int PF_KC_MIN = 1024;              // shortest key chunk (a power of two below PF_KC)
-constexpr int PF_MIN_GRID = 512;             // workgroups the chunk length aims for
 
 // (key chunk, query block) of a prefill workgroup.  Workgroups go to the 8
 // XCDs round-robin in launch order (linear id L -> XCD L % 8), each XCD with
@@ -735,16 +765,6 @@ __global__ __launch_bounds__(PF_THREADS) void idx_prefill_fp8(
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
-// Keys per decode workgroup: the largest power of two in [512, 4096] that
-// still gives about 2,048 workgroups for the padded batch (nq x max_len), so
-// short or ragged batches keep every compute unit streaming.
-static int decode_chunk(int nq, int max_len) {
-  const int64_t keys = (int64_t)nq * max_len;
-  int chunk = 4096;
-  while (chunk > 512 && keys / chunk < 2048) chunk >>= 1;
-  return chunk;
-}
-
 hipError_t launch_zero(const ZeroSpans& z, int nq, hipStream_t st) {
   if (nq == 0 || (z.s[0].base == nullptr && z.s[1].base == nullptr)) return hipSuccess;
   hipLaunchKernelGGL(zero_spans_kernel, dim3(nq), dim3(256), 0, st, z);
@@ -752,61 +772,67 @@ hipError_t launch_zero(const ZeroSpans& z, int nq, hipStream_t st) {
 }
 
 hipError_t launch_index_score(const BatchDev& b, int dtype, const void* qI, const float* w,
-                              const void* kI, float* scores, int64_t ld, hipStream_t st, const ZeroSpans* zp) {
+                              const void* kI, float* scores, int64_t ld, hipStream_t st, uint32_t* hist,
+                              bool* hist_done) {
+  if (hist_done) *hist_done = false;
   if (b.nq == 0) return hipSuccess;
-  ZeroSpans z;
-  z.s[0] = ZeroSpan{nullptr, 0, 0};
-  z.s[1] = ZeroSpan{nullptr, 0, 0};
-  if (zp) z = *zp;
-  if (dtype == 0) {
-    dim3 grid((b.max_len + IDX_F32_THREADS - 1) / IDX_F32_THREADS, b.nq);
-    hipLaunchKernelGGL(idx_decode_f32, grid, dim3(IDX_F32_THREADS), 0, st, b, (const float*)qI, w,
-                       (const float*)kI, scores, ld, z);
-  } else if (b.nq >= PF_QB && (int64_t)b.nq >= (int64_t)PF_QB * b.nseq) {
-    // at least a block's worth of queries per sequence on average: a
-    // sequence's queries are best contiguous in the batch, so that blocks
-    // rarely straddle sequences
-    hipError_t e = launch_zero(z, b.nq, st);
-    if (e != hipSuccess) return e;
-    // key chunks of PF_KC, halved (to PF_KC_MIN at the shortest) while the
-    // grid has fewer than PF_MIN_GRID workgroups (few, short sequences)
-    const int nqb = (b.nq + PF_QB - 1) / PF_QB;
-    int kc = PF_KC;
-    while (kc > PF_KC_MIN && (int64_t)((b.max_len + kc - 1) / kc) * nqb < PF_MIN_GRID) kc >>= 1;
-    dim3 grid((b.max_len + kc - 1) / kc, nqb);
-    if (dtype == 2) {
-      const uint8_t* q8 = (const uint8_t*)qI;
-      const uint8_t* k8 = (const uint8_t*)kI;
-      if (kc == 8192)
-        hipLaunchKernelGGL(idx_prefill_fp8<8192>, grid, dim3(PF_THREADS), 0, st, b, q8, w, k8, scores, ld);
-      else if (kc == 4096)
-        hipLaunchKernelGGL(idx_prefill_fp8<4096>, grid, dim3(PF_THREADS), 0, st, b, q8, w, k8, scores, ld);
-      else if (kc == 2048)
-        hipLaunchKernelGGL(idx_prefill_fp8<2048>, grid, dim3(PF_THREADS), 0, st, b, q8, w, k8, scores, ld);
+  switch (index_kernel(dtype, b.nq, b.nseq)) {
+    case IndexKernel::F32: {
+      dim3 grid((b.max_len + IDX_F32_THREADS - 1) / IDX_F32_THREADS, b.nq);
+      hipLaunchKernelGGL(idx_decode_f32, grid, dim3(IDX_F32_THREADS), 0, st, b, (const float*)qI, w,
+                         (const float*)kI, scores, ld);
+      break;
+    }
+    case IndexKernel::Prefill: {
+      // a sequence's queries are best contiguous in the batch, so that
+      // blocks rarely straddle sequences
+      const int kc = prefill_key_chunk(b.nq, b.max_len);
+      dim3 grid((b.max_len + kc - 1) / kc, (b.nq + PF_QB - 1) / PF_QB);
+      if (dtype == 2) {
+        const uint8_t* q8 = (const uint8_t*)qI;
+        const uint8_t* k8 = (const uint8_t*)kI;
+        if (kc == 8192)
+          hipLaunchKernelGGL(idx_prefill_fp8<8192>, grid, dim3(PF_THREADS), 0, st, b, q8, w, k8, scores, ld);
+        else if (kc == 4096)
+          hipLaunchKernelGGL(idx_prefill_fp8<4096>, grid, dim3(PF_THREADS), 0, st, b, q8, w, k8, scores, ld);
+        else if (kc == 2048)
+          hipLaunchKernelGGL(idx_prefill_fp8<2048>, grid, dim3(PF_THREADS), 0, st, b, q8, w, k8, scores, ld);
+        else
+          hipLaunchKernelGGL(idx_prefill_fp8<1024>, grid, dim3(PF_THREADS), 0, st, b, q8, w, k8, scores, ld);
+      } else if (b.nseq == 1) {
+        hipLaunchKernelGGL(idx_prefill_bf16, grid, dim3(PF_THREADS), 0, st, b, (const uint16_t*)qI, w,
+                           (const uint16_t*)kI, scores, ld, kc);
+      } else {
+        hipLaunchKernelGGL(idx_prefill_bf16_multi, grid, dim3(PF_THREADS), 0, st, b, (const uint16_t*)qI, w,
+                           (const uint16_t*)kI, scores, ld, kc);
+      }
+      break;
+    }
+    case IndexKernel::Balanced: {
+      const dim3 grid(IDX_BAL_GRID), block(IDX_DEC_THREADS);
+      if (hist != nullptr) {
+        if (dtype == 2)
+          hipLaunchKernelGGL(idx_decode_fp8_bal<true>, grid, block, 0, st, b, qI, w, kI, scores, ld, hist);
+        else
+          hipLaunchKernelGGL(idx_decode_bf16_bal<true>, grid, block, 0, st, b, qI, w, kI, scores, ld, hist);
+        if (hist_done) *hist_done = true;
+      } else {
+        if (dtype == 2)
+          hipLaunchKernelGGL(idx_decode_fp8_bal<false>, grid, block, 0, st, b, qI, w, kI, scores, ld, hist);
+        else
+          hipLaunchKernelGGL(idx_decode_bf16_bal<false>, grid, block, 0, st, b, qI, w, kI, scores, ld, hist);
+      }
+      break;
+    }
+    case IndexKernel::Chunked: {
+      const int chunk = decode_key_chunk(b.nq, b.max_len);
+      dim3 grid((b.max_len + chunk - 1) / chunk, b.nq);
+      if (dtype == 2)
+        hipLaunchKernelGGL(idx_decode_fp8, grid, dim3(IDX_DEC_THREADS), 0, st, b, qI, w, kI, scores, ld, chunk);
       else
-        hipLaunchKernelGGL(idx_prefill_fp8<1024>, grid, dim3(PF_THREADS), 0, st, b, q8, w, k8, scores, ld);
-    } else if (b.nseq == 1)
-      hipLaunchKernelGGL(idx_prefill_bf16, grid, dim3(PF_THREADS), 0, st, b, (const uint16_t*)qI, w,
-                         (const uint16_t*)kI, scores, ld, kc);
-    else
-      hipLaunchKernelGGL(idx_prefill_bf16_multi, grid, dim3(PF_THREADS), 0, st, b, (const uint16_t*)qI, w,
-                         (const uint16_t*)kI, scores, ld, kc);
-  } else if (b.nq <= IDX_BAL_MAXQ) {
-    if (dtype == 2)
-      hipLaunchKernelGGL(idx_decode_fp8_bal, dim3(IDX_BAL_GRID), dim3(IDX_DEC_THREADS), 0, st, b, qI, w, kI,
-                         scores, ld, z);
-    else
-      hipLaunchKernelGGL(idx_decode_bf16_bal, dim3(IDX_BAL_GRID), dim3(IDX_DEC_THREADS), 0, st, b, qI, w, kI,
-                         scores, ld, z);
-  } else {
-    const int chunk = decode_chunk(b.nq, b.max_len);
-    dim3 grid((b.max_len + chunk - 1) / chunk, b.nq);
-    if (dtype == 2)
-      hipLaunchKernelGGL(idx_decode_fp8, grid, dim3(IDX_DEC_THREADS), 0, st, b, qI, w, kI, scores, ld,
-                         chunk, z);
-    else
-      hipLaunchKernelGGL(idx_decode_bf16, grid, dim3(IDX_DEC_THREADS), 0, st, b, qI, w, kI, scores, ld,
-                         chunk, z);
+        hipLaunchKernelGGL(idx_decode_bf16, grid, dim3(IDX_DEC_THREADS), 0, st, b, qI, w, kI, scores, ld, chunk);
+      break;
+    }
   }
   return hipGetLastError();
 }

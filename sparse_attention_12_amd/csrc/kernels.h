@@ -24,19 +24,25 @@ struct ZeroSpans {
 // Zeroes every span (one workgroup per query).
 hipError_t launch_zero(const ZeroSpans& z, int nq, hipStream_t st);
 
-// Indexer scores of every query over its candidates (indexer.hip).  The
-// first workgroup of each query also zeroes that query's words of `z`
-// (nobody else touches them during the launch).
+// Indexer scores of every query over its candidates (indexer.hip).  With
+// hist (HOST-chosen, may be NULL) and a decode batch of at most IDX_BAL_MAXQ
+// queries, the launch also adds each query's scores to hist[q][0, TK_BINS1)
+// by their top TK_BITS1 key bits (the top-k's first radix level), which
+// must be zero before the launch; *hist_done (may be NULL) says whether it
+// did.
 hipError_t launch_index_score(const BatchDev& b, int dtype, const void* qI, const float* w,
                               const void* kI, float* scores, int64_t ld, hipStream_t st,
-                              const ZeroSpans* z = nullptr);
+                              uint32_t* hist = nullptr, bool* hist_done = nullptr);
 
-// Top-k selection (topk.hip).  ws may be NULL when topk_workspace_bytes() == 0.
-// With ws_zeroed, the words topk_zero_span() describes are already zero.
-size_t topk_workspace_bytes(int nq, int max_len, int k);
+// Top-k selection (topk.hip).  ws may be NULL when topk_workspace_bytes() ==
+// 0.  hist_pre (may be NULL): the indexer's first-level histograms
+// [nq][TK_BINS1]; each query's is checked (its bins must sum to the query's
+// candidate count, which holds exactly when it started from zero), used in
+// place of a counting pass when it checks out, and cleared for the next call
+// either way.
 ZeroSpan topk_zero_span(void* ws, int nq, int max_len);
 hipError_t launch_topk(const BatchDev& b, const float* scores, int64_t ld, int k, int32_t* idx,
-                       int32_t* count, void* ws, size_t ws_bytes, hipStream_t st, bool ws_zeroed = false);
+                       int32_t* count, void* ws, size_t ws_bytes, hipStream_t st, uint32_t* hist_pre = nullptr);
 
 // Sparse MLA over a shared selection for n_layers layers (mla.hip).
 struct MlaLayers {
@@ -45,15 +51,12 @@ struct MlaLayers {
   void* out[MLA_MAX_LAYERS];
   float* lse[MLA_MAX_LAYERS];
 };
-int mla_num_splits(int dtype, int nq, int k, int n_layers);
-size_t mla_workspace_bytes(int dtype, int nq, int k, int n_layers);
 // rope: rotary width of every layer's rows (DR, or 0 without rotary encoding).
 hipError_t launch_mla(const BatchDev& b, int dtype, int rope, const MlaLayers& layers, int n_layers,
                       const int32_t* idx, int k, float scale, int out_dtype, void* ws,
                       size_t ws_bytes, hipStream_t st);
 
-// Rotary frequencies (host) and the rotary / cache-append step (rope.hip).
-void rope_frequencies(const float* alpha, double* out);
+// The rotary / cache-append step (rope.hip).
 hipError_t launch_rope_append(const BatchDev& b, int dtype, int rope, const double* freq, const float* latent,
                               const float* rope_key, void* kv, void* q, const float* ss, const float* sb,
                               hipStream_t st);

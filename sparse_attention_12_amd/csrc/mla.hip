@@ -70,7 +70,6 @@ __device__ inline void store_out4(const MlaParams& p, int layer, int64_t off, f3
 // buffers; the two wave halves issue alternate tiles, so two tiles are in
 // flight while one is consumed.
 constexpr int MLA_THREADS = 512;
-constexpr int MLA_TILE = 32;                    // positions per tile
 constexpr int MLA_SPLIT_MAX = KMAX;
 constexpr int MLA_VBLK = DC / 16 / 2;           // 16-column value blocks per wave (16)
 constexpr float MLA_RESCALE_SLACK = 8.0f;       // log2 units
@@ -447,7 +446,6 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_bf16_kernel(MlaParams p) {
 // fp32 split kernel (VALU; small fp32 workloads)
 // ---------------------------------------------------------------------------
 constexpr int MLA32_THREADS = 256;
-constexpr int MLA32_TILE = 8;
 
 template <int ROPE>
 __global__ __launch_bounds__(MLA32_THREADS) void mla_f32_kernel(MlaParams p) {
@@ -583,31 +581,6 @@ __global__ __launch_bounds__(CMB_THREADS) void mla_combine(MlaParams p) {
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-constexpr int MLA_TARGET_BLOCKS = 256;  // one workgroup per compute unit
-
-int mla_num_splits(int dtype, int nq, int k, int n_layers) {
-  const int tile = dtype == 0 ? MLA32_TILE : MLA_TILE;
-  const int max_split = (k + tile - 1) / tile;
-  const int base = nq * n_layers;
-  int ns = base > 0 ? (MLA_TARGET_BLOCKS + base - 1) / base : 1;
-  const int cap = dtype == 0 ? 64 : 16;
-  ns = min(ns, min(cap, max_split));
-  return max(ns, 1);
-}
-
-static int split_len_of(int dtype, int k, int ns) {
-  const int tile = dtype == 0 ? MLA32_TILE : MLA_TILE;
-  int len = (k + ns - 1) / ns;
-  return (len + tile - 1) / tile * tile;
-}
-
-size_t mla_workspace_bytes(int dtype, int nq, int k, int n_layers) {
-  const int ns = mla_num_splits(dtype, nq, k, n_layers);
-  if (ns <= 1) return 0;
-  const size_t slots = (size_t)ns * n_layers * nq * H;
-  return slots * DC * sizeof(float) + slots * 2 * sizeof(float);
-}
-
 hipError_t launch_mla(const BatchDev& b, int dtype, int rope, const MlaLayers& layers, int n_layers,
                       const int32_t* idx, int k, float scale, int out_dtype, void* ws,
                       size_t ws_bytes, hipStream_t st) {
@@ -618,7 +591,7 @@ hipError_t launch_mla(const BatchDev& b, int dtype, int rope, const MlaLayers& l
   p.k = k;
   p.n_layers = n_layers;
   p.nsplit = mla_num_splits(dtype, b.nq, k, n_layers);
-  p.split_len = split_len_of(dtype, k, p.nsplit);
+  p.split_len = mla_split_len(dtype, k, p.nsplit);
   p.nsplit = (k + p.split_len - 1) / p.split_len;
   p.out_bf16 = out_dtype == 1;
   p.scale_log2 = scale * 1.44269504088896340736f;

@@ -2,14 +2,9 @@
 // attention read (concept page "Mistral Large 4", sections "Positions" and
 // "Query scaling").
 //
-// Frequencies (host, double precision): the 64-value rotary part is 32 pairs;
-// pair i turns at omega_i = 10000^(-i/32) radians per position.  Under YaRN
-// (original window 512, stretch 2,048) a pair whose wavelength 2 pi / omega_i
-// fits 32 times into the window is left alone, a pair whose wavelength is
-// longer than the window is slowed by the full stretch, and the pairs
-// between the longest unchanged and the shortest fully slowed wavelength
-// are slowed by a factor interpolated linearly in the pair index; LeRoPE
-// scales frequency i by the learned e^{alpha_i}.
+// The frequencies (host, double precision) come from rope_frequencies in
+// plan.cpp: YaRN with an original window of 512 and a stretch of 2,048,
+// then LeRoPE's learned multipliers.
 // Per new token at 0-based position t (pair i = values 2i, 2i+1 of the
 // rotary part, turned by the angle t * omega_i):
 //   cache row  = [latent (512) | rotated rotary key (64, rotary layers only)]
@@ -101,26 +96,6 @@ __global__ __launch_bounds__(ROPE_THREADS) void rope_append_kernel(BatchDev b, i
       const int i = (c - DC) / 2;
       Elem<T>::put2(qq, h * W + c, x * cs[i] - y * sn[i], x * sn[i] + y * cs[i]);
     }
-  }
-}
-
-void rope_frequencies(const float* alpha, double* out) {
-  constexpr int pairs = DR / 2;
-  const double window = 512.0, stretch = 2048.0, min_turns = 32.0;
-  double omega[pairs];
-  int longest_kept = -1, shortest_slowed = pairs;
-  for (int i = 0; i < pairs; ++i) {
-    omega[i] = exp(-log(10000.0) * (double)i / (double)pairs);
-    const double wavelength = 2.0 * M_PI / omega[i];
-    if (wavelength * min_turns <= window) longest_kept = i;                    // wavelengths grow with i
-    if (wavelength > window && shortest_slowed == pairs) shortest_slowed = i;
-  }
-  for (int i = 0; i < pairs; ++i) {
-    double ramp = (double)(i - longest_kept) / (double)(shortest_slowed - longest_kept);
-    ramp = ramp < 0.0 ? 0.0 : (ramp > 1.0 ? 1.0 : ramp);
-    double f = omega[i] * (1.0 - ramp * (1.0 - 1.0 / stretch));
-    if (alpha) f *= exp((double)alpha[i]);
-    out[i] = f;
   }
 }
 

@@ -19,19 +19,18 @@
 // registers between steps 1 and 2.  If the candidate list would not fit in LDS (for
 // instance every score equal), a row-streaming fallback selects with
 // 64-bit (u, position) keys and compacts the row itself.
+// In the fused decode read, the indexer has already counted step 1's
+// histogram while making the scores; it is taken from there after a check
+// that its bins sum to the row's length (bins never go negative, so the sum
+// is right exactly when the histogram started from zero), and cleared for
+// the next call; a histogram that fails the check is recounted here.
 #include "dsa_common.h"
 #include "kernels.h"
 
 namespace dsa {
 
-constexpr int TK_THREADS = 1024;
 constexpr int TK_WAVES = TK_THREADS / 64;
-constexpr int TK_BITS1 = 12;
-constexpr int TK_BINS1 = 1 << TK_BITS1;
-constexpr int TK_SHIFT1 = 32 - TK_BITS1;
 constexpr int TK_FCAP = 12288;          // candidate entries held in LDS
-constexpr int TK_CHUNK = 8192;          // scores per workgroup in the split path
-constexpr int TK_ROWS_SPLIT_MAX = 255;  // batches with more rows use one workgroup per row
 constexpr int TK_LEVEL_BITS = 11;       // fallback levels over 64-bit keys
 // First-level histograms are kept in TK_HCOPIES interleaved copies (bin b,
 // copy c at word TK_HCOPIES*b + c; lane l adds to copy l % TK_HCOPIES), so
@@ -80,6 +79,7 @@ struct ScanShared {
   uint32_t total;
   int digit;
   uint32_t above;
+  uint64_t red[TK_WAVES];
 };
 
 // Bucket d of hist[0, nbins) with fewer than `need` entries above it and at
@@ -142,6 +142,39 @@ __device__ void hist_range(const float* row, int c0, int c1, uint32_t* hist) {
       }
     }
   }
+}
+
+// 64-bit sum over the workgroup (every thread calls; the result in every
+// thread).  red: TK_WAVES words of LDS.
+__device__ inline uint64_t block_sum64(uint64_t v, uint64_t* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint64_t t = 0;
+#pragma unroll
+  for (int w = 0; w < TK_WAVES; ++w) t += red[w];
+  __syncthreads();
+  return t;
+}
+
+// Takes the indexer's first-level histogram of a row: copies it to hist
+// (LDS), clears it in global memory for the next call, and returns whether
+// it is the row's histogram (its bins sum to n).  Thread t owns bins
+// [4t, 4t + 4).
+static_assert(TK_BINS1 == 4 * TK_THREADS, "one uint4 of bins per thread");
+__device__ inline bool take_precounted(uint32_t* gh, uint32_t* hist, int n, uint64_t* red) {
+  uint4* g4 = (uint4*)gh;
+  const uint4 v = g4[threadIdx.x];
+  g4[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+  *(uint4*)(hist + 4 * threadIdx.x) = v;
+  const uint64_t mine = (uint64_t)v.x + v.y + v.z + v.w;
+  return block_sum64(mine, red) == (uint64_t)n;
+}
+
+// Clears a row's precounted histogram in global memory.
+__device__ inline void clear_precounted(uint32_t* gh) {
+  ((uint4*)gh)[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 __device__ inline void hist_copies_zero(uint32_t* hc) {
@@ -341,10 +374,13 @@ __device__ inline void keep_all(int n, int k, int32_t* out) {
 // them there, so that part of the row crosses HBM once.  The rest of a
 // longer row (beyond what 128 registers per thread hold) is read twice,
 // as in the two-pass path.
+// With hist_pre, the row's first-level histogram comes precounted (and is
+// cleared for the next call).
 template <int NST>
 __global__ __launch_bounds__(TK_THREADS) void topk_row_reg_kernel(BatchDev b, const float* __restrict__ scores,
                                                                  int64_t ld, int k, int32_t* __restrict__ idx,
-                                                                 int32_t* __restrict__ count) {
+                                                                 int32_t* __restrict__ count,
+                                                                 uint32_t* __restrict__ hist_pre) {
   __shared__ __attribute__((aligned(16))) RowShared sm;
   const int q = blockIdx.x;
   const int tid = threadIdx.x;
@@ -352,12 +388,15 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_reg_kernel(BatchDev b, co
   const int n = r.n;
   int32_t* out = idx + (int64_t)q * k;
   const float* row = scores + (int64_t)q * ld;
+  uint32_t* gh = hist_pre ? hist_pre + (int64_t)q * TK_BINS1 : nullptr;
   if (n <= k) {
     keep_all(n, k, out);
+    if (gh) clear_precounted(gh);
   } else {
     constexpr int REG = NST * TK_STRETCH;
     uint32_t* hc = sm.list.hcopies;
-    hist_copies_zero(hc);
+    const bool counted = gh && take_precounted(gh, sm.hist1, n, sm.list.ss.red);
+    if (!counted) hist_copies_zero(hc);
     // keys of this thread's runs (positions at or past n are never counted)
     uint32_t u[NST][TK_RUN];
     const bool vec = (((uintptr_t)row) & 15) == 0;
@@ -378,19 +417,21 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_reg_kernel(BatchDev b, co
         for (int j = 0; j < TK_RUN; ++j) u[st][j] = s0 + j < n ? score_key(row[s0 + j]) : 0u;
       }
     }
-    __syncthreads();  // copies cleared
-    const uint32_t copy = (uint32_t)tid & (TK_HCOPIES - 1);
+    __syncthreads();  // copies cleared (or the precounted histogram in place)
+    if (!counted) {
+      const uint32_t copy = (uint32_t)tid & (TK_HCOPIES - 1);
 #pragma unroll
-    for (int st = 0; st < NST; ++st) {
-      const int s0 = st * TK_STRETCH + tid * TK_RUN;
+      for (int st = 0; st < NST; ++st) {
+        const int s0 = st * TK_STRETCH + tid * TK_RUN;
 #pragma unroll
-      for (int j = 0; j < TK_RUN; ++j)
-        if (s0 + j < n) atomicAdd(&hc[(u[st][j] >> TK_SHIFT1) * TK_HCOPIES + copy], 1u);
+        for (int j = 0; j < TK_RUN; ++j)
+          if (s0 + j < n) atomicAdd(&hc[(u[st][j] >> TK_SHIFT1) * TK_HCOPIES + copy], 1u);
+      }
+      if (n > REG) hist_range(row, REG, n, hc);
+      __syncthreads();
+      hist_copies_fold(hc, sm.hist1);
+      __syncthreads();
     }
-    if (n > REG) hist_range(row, REG, n, hc);
-    __syncthreads();
-    hist_copies_fold(hc, sm.hist1);
-    __syncthreads();
     int d1;
     uint32_t above;
     find_bucket(sm.hist1, TK_BINS1, (uint32_t)k, sm.list.ss, &d1, &above);
@@ -469,7 +510,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_hist_kernel(BatchDev b, const
 
 __global__ __launch_bounds__(TK_THREADS) void topk_gather_kernel(BatchDev b, const float* __restrict__ scores,
                                                                  int64_t ld, int k, SplitWs ws) {
-  __shared__ uint32_t hist[TK_BINS1];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[TK_BINS1];
   __shared__ ScanShared ss;
   const int q = blockIdx.y;
   const int c = blockIdx.x;
@@ -498,8 +539,17 @@ __global__ __launch_bounds__(TK_THREADS) void topk_gather_kernel(BatchDev b, con
 #pragma unroll
     for (int j = 0; j < GR; ++j) u[j] = s0 + j < c1 ? score_key(row[s0 + j]) : 0u;
   }
+  // the row's histogram (counted by the indexer or by topk_hist_kernel);
+  // one that does not sum to the row's length did not start from zero: the
+  // row is recounted here (only after a call that left it uncleared)
   const uint32_t* gh = ws.hist + (int64_t)q * TK_BINS1;
-  for (int i = tid; i < TK_BINS1; i += TK_THREADS) hist[i] = gh[i];
+  const uint4 hv = ((const uint4*)gh)[tid];
+  *(uint4*)(hist + 4 * tid) = hv;
+  if (block_sum64((uint64_t)hv.x + hv.y + hv.z + hv.w, ss.red) != (uint64_t)r.n) {
+    *(uint4*)(hist + 4 * tid) = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+    for (int i = tid; i < r.n; i += TK_THREADS) atomicAdd(&hist[score_key(row[i]) >> TK_SHIFT1], 1u);
+  }
   __syncthreads();
   int d1;
   uint32_t above;
@@ -543,6 +593,9 @@ __global__ __launch_bounds__(TK_THREADS) void topk_final_kernel(BatchDev b, cons
   const QueryRange r = query_range(b, q);
   const int n = r.n;
   int32_t* out = idx + (int64_t)q * k;
+  // every gather workgroup of this row is done with its histogram: clear
+  // it for the next call
+  clear_precounted(ws.hist + (int64_t)q * TK_BINS1);
   if (n <= k) {
     for (int j = tid; j < k; j += TK_THREADS) out[j] = j < n ? j : -1;
     if (tid == 0 && count) count[q] = n;
@@ -609,78 +662,53 @@ __global__ __launch_bounds__(TK_THREADS) void topk_final_kernel(BatchDev b, cons
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-// Few long rows take the split path (it needs one finalize thread per chunk
-// of the longest row); rows up to TK_ROW_MAX_LEN scores are faster with one
-// workgroup per row whatever the row count (measured on MI355X: 20 us
-// against 26 us for 64 rows of 32,768; the split path wins beyond ~50K).
-constexpr int TK_ROW_MAX_LEN = 49152;
-static bool use_split(int nq, int max_len) {
-  return nq <= TK_ROWS_SPLIT_MAX && max_len > TK_ROW_MAX_LEN &&
-         (int64_t)max_len <= (int64_t)TK_THREADS * TK_CHUNK;
-}
-
-static size_t split_bytes(int nq, int max_len, SplitWs* ws, char* base) {
-  const int nchunk = (max_len + TK_CHUNK - 1) / TK_CHUNK;
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    const size_t at = off;
-    off += (bytes + 255) & ~(size_t)255;
-    return at;
-  };
-  const size_t h = take((size_t)nq * TK_BINS1 * 4);
-  const size_t bk = take((size_t)nq * 4 * 4);
-  const size_t c = take((size_t)nq * nchunk * 4);
-  const size_t kk = take((size_t)nq * nchunk * TK_CHUNK * 4);
-  const size_t p = take((size_t)nq * nchunk * TK_CHUNK * 4);
-  if (ws) {
-    ws->hist = (uint32_t*)(base + h);
-    ws->bucket = (uint32_t*)(base + bk);
-    ws->cnt = (uint32_t*)(base + c);
-    ws->lkey = (uint32_t*)(base + kk);
-    ws->lpos = (int32_t*)(base + p);
-    ws->nchunk = nchunk;
-  }
-  return off;
-}
-
-size_t topk_workspace_bytes(int nq, int max_len, int k) {
-  (void)k;
-  if (nq <= 0 || max_len <= 0 || !use_split(nq, max_len)) return 0;
-  return split_bytes(nq, max_len, nullptr, nullptr);
+static SplitWs split_ws(int nq, int max_len, char* base) {
+  const TopkLayout t = topk_layout(nq, max_len);
+  SplitWs ws;
+  ws.hist = (uint32_t*)(base + t.hist);
+  ws.bucket = (uint32_t*)(base + t.bucket);
+  ws.cnt = (uint32_t*)(base + t.cnt);
+  ws.lkey = (uint32_t*)(base + t.lkey);
+  ws.lpos = (int32_t*)(base + t.lpos);
+  ws.nchunk = t.nchunk;
+  return ws;
 }
 
 ZeroSpan topk_zero_span(void* wsp, int nq, int max_len) {
-  if (wsp == nullptr || nq <= 0 || max_len <= 0 || !use_split(nq, max_len)) return ZeroSpan{nullptr, 0, 0};
-  SplitWs ws;
-  split_bytes(nq, max_len, &ws, (char*)wsp);
-  return ZeroSpan{ws.hist, TK_BINS1, TK_BINS1};
+  if (wsp == nullptr || nq <= 0 || max_len <= 0 || !topk_use_split(nq, max_len)) return ZeroSpan{nullptr, 0, 0};
+  return ZeroSpan{split_ws(nq, max_len, (char*)wsp).hist, TK_BINS1, TK_BINS1};
 }
 
 hipError_t launch_topk(const BatchDev& b, const float* scores, int64_t ld, int k, int32_t* idx,
-                       int32_t* count, void* wsp, size_t ws_bytes, hipStream_t st, bool ws_zeroed) {
+                       int32_t* count, void* wsp, size_t ws_bytes, hipStream_t st, uint32_t* hist_pre) {
   if (b.nq == 0) return hipSuccess;
-  if (!use_split(b.nq, b.max_len)) {
+  if (!topk_use_split(b.nq, b.max_len)) {
     // as many 16,384-score stretches in registers as the row needs, at most 3
     const int nst = (b.max_len + TK_STRETCH - 1) / TK_STRETCH;
     if (nst <= 1)
-      hipLaunchKernelGGL(topk_row_reg_kernel<1>, dim3(b.nq), dim3(TK_THREADS), 0, st, b, scores, ld, k, idx, count);
+      hipLaunchKernelGGL(topk_row_reg_kernel<1>, dim3(b.nq), dim3(TK_THREADS), 0, st, b, scores, ld, k, idx, count,
+                         hist_pre);
     else if (nst == 2)
-      hipLaunchKernelGGL(topk_row_reg_kernel<2>, dim3(b.nq), dim3(TK_THREADS), 0, st, b, scores, ld, k, idx, count);
+      hipLaunchKernelGGL(topk_row_reg_kernel<2>, dim3(b.nq), dim3(TK_THREADS), 0, st, b, scores, ld, k, idx, count,
+                         hist_pre);
     else
-      hipLaunchKernelGGL(topk_row_reg_kernel<3>, dim3(b.nq), dim3(TK_THREADS), 0, st, b, scores, ld, k, idx, count);
+      hipLaunchKernelGGL(topk_row_reg_kernel<3>, dim3(b.nq), dim3(TK_THREADS), 0, st, b, scores, ld, k, idx, count,
+                         hist_pre);
     return hipGetLastError();
   }
-  SplitWs ws;
-  if (wsp == nullptr || ws_bytes < split_bytes(b.nq, b.max_len, &ws, (char*)wsp)) return hipErrorInvalidValue;
-  if (!ws_zeroed) {
+  if (wsp == nullptr || ws_bytes < topk_layout(b.nq, b.max_len).bytes) return hipErrorInvalidValue;
+  SplitWs ws = split_ws(b.nq, b.max_len, (char*)wsp);
+  dim3 grid(ws.nchunk, b.nq);
+  if (hist_pre != nullptr) {
+    ws.hist = hist_pre;   // counted by the indexer
+  } else {
     ZeroSpans z;
-    z.s[0] = topk_zero_span(wsp, b.nq, b.max_len);
+    z.s[0] = ZeroSpan{ws.hist, TK_BINS1, TK_BINS1};
     z.s[1] = ZeroSpan{nullptr, 0, 0};
     hipError_t e = launch_zero(z, b.nq, st);
     if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(TK_THREADS), 0, st, b, scores, ld, k, ws);
   }
-  dim3 grid(ws.nchunk, b.nq);
-  hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(TK_THREADS), 0, st, b, scores, ld, k, ws);
   hipLaunchKernelGGL(topk_gather_kernel, grid, dim3(TK_THREADS), 0, st, b, scores, ld, k, ws);
   hipLaunchKernelGGL(topk_final_kernel, dim3(b.nq), dim3(TK_THREADS), 0, st, b, scores, ld, k, idx, count, ws);
   return hipGetLastError();
