@@ -8,13 +8,15 @@
 // without rotary encoding (every fourth layer, list of changes on the same
 // page).  64 x (512 + R + 512) multiply-adds per selected position.
 //
-// bf16 kernel: one workgroup (4 waves) per (split of the selection, query,
-// layer); wave w owns heads 16w..16w+15.  Per tile of 32 positions the
-// 576-wide bf16 rows are gathered into LDS, then
-//   S^T (32 positions x 16 heads) = K_tile . Q_w^T   (18 MFMA 16x16x32 per block)
+// bf16 kernel: one workgroup (8 waves) per (split of the selection, query,
+// layer); wave w owns heads 16(w%4)..16(w%4)+15 and half of the row width
+// for the logits, half of the latent columns for the values.  Per tile of
+// 32 positions the 576-wide bf16 rows are gathered into LDS, then
+//   S^T (32 positions x 16 heads) = K_tile . Q_w^T   (MFMA 16x16x32; the two
+//   halves of the contraction are summed through LDS)
 //   online softmax in the exp2 domain, rescaling the accumulator only when a
 //   head's running max grows by more than 2^8
-//   O_w^T (512 x 16) += V_tile^T . P^T               (32 MFMA 16x16x32)
+//   O_w^T (256 x 16) += V_tile^T . P^T               (MFMA 16x16x32)
 // The S^T accumulator layout puts, in each lane, one head and 8 positions --
 // exactly the B operand of the P.V product when the 32 positions of a tile
 // are taken in the order {4g..4g+3, 16+4g..16+4g+3} for lane group g, so P
@@ -37,7 +39,8 @@ struct MlaParams {
   int n_layers;
   int out_bf16;
   float scale_log2;  // scale * log2(e)
-  float* part_acc;   // [nsplit][n_layers][nq][64][512]
+  void* part_o;      // [nsplit][n_layers][nq][64][512] split outputs, each normalised by its
+                     // own sum: bf16 for the bf16 kernel, float32 for the fp32 one
   float* part_ml;    // [nsplit][n_layers][nq][64][2]  (max in log2 units, sum)
   MlaLayers L;
 };
@@ -431,10 +434,19 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_bf16_kernel(MlaParams p) {
     if (d == 0 && g == 0 && p.L.lse[layer])
       p.L.lse[layer][qh] = l_part > 0.0f ? (st.m_run + log2f(l_part)) * LN2 : -INFINITY;
   } else {
+    // the split's output normalised by its own sum, in bf16 (half the
+    // partial traffic of float32; the merge weighs it by that sum)
     const int64_t slot = ((int64_t)split * p.n_layers + layer) * p.b.nq * H + qh;
-    float* acc = p.part_acc + slot * DC + col0;
+    const float inv = l_part > 0.0f ? 1.0f / l_part : 0.0f;
+    uint16_t* po = (uint16_t*)p.part_o + slot * DC + col0;
 #pragma unroll
-    for (int vb = 0; vb < MLA_VBLK; ++vb) *(f32x4*)(acc + vb * 16 + 4 * g) = st.o[vb];
+    for (int vb = 0; vb < MLA_VBLK; ++vb) {
+      const f32x4 v = st.o[vb] * inv;
+      uint2 pk;
+      pk.x = pack_bf16x2(v[0], v[1]);
+      pk.y = pack_bf16x2(v[2], v[3]);
+      *(uint2*)(po + vb * 16 + 4 * g) = pk;
+    }
     if (d == 0 && g == 0) {
       p.part_ml[slot * 2 + 0] = l_part > 0.0f ? st.m_run : -INFINITY;
       p.part_ml[slot * 2 + 1] = l_part;
@@ -516,9 +528,11 @@ __global__ __launch_bounds__(MLA32_THREADS) void mla_f32_kernel(MlaParams p) {
       p.L.lse[layer][qh] = l_run > 0.0f ? (m_run + log2f(l_run)) * LN2 : -INFINITY;
   } else {
     const int64_t slot = ((int64_t)split * p.n_layers + layer) * p.b.nq * H + qh;
-    float* pa = p.part_acc + slot * DC + part * VS;
+    const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+    float* pa = (float*)p.part_o + slot * DC + part * VS;
 #pragma unroll
-    for (int i = 0; i < VS; i += 4) *(f32x4*)(pa + i) = f32x4{acc[i], acc[i + 1], acc[i + 2], acc[i + 3]};
+    for (int i = 0; i < VS; i += 4)
+      *(f32x4*)(pa + i) = f32x4{acc[i] * inv, acc[i + 1] * inv, acc[i + 2] * inv, acc[i + 3] * inv};
     if (part == 0) {
       p.part_ml[slot * 2 + 0] = l_run > 0.0f ? m_run : -INFINITY;
       p.part_ml[slot * 2 + 1] = l_run;
@@ -529,53 +543,86 @@ __global__ __launch_bounds__(MLA32_THREADS) void mla_f32_kernel(MlaParams p) {
 // ---------------------------------------------------------------------------
 // log-sum-exp merge of the splits of each (query, layer)
 // ---------------------------------------------------------------------------
-constexpr int CMB_THREADS = 256;
-constexpr int CMB_HEADS = 8;   // heads per workgroup: 32 threads x 16 values each
+// One wave per (head, query, layer): lane i < nsplit holds split i's
+// (max, sum), so the merge weights w_i = 2^(m_i - M) l_i come from two wave
+// reductions; then lane l adds up latent columns [8l, 8l + 8) of every
+// split's normalised output, four splits' loads in flight at a time.  An
+// empty split (max -inf) weighs 0.
+constexpr int CMB_THREADS = 256;   // four heads per workgroup
+constexpr int CMB_BATCH = 4;
 
+__device__ inline float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ inline float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// Eight latent values of a split output: bf16 (one 16-byte load) or
+// float32 (two).
+template <bool BF16>
+__device__ inline void load8(const void* base, int64_t off, float (&v)[8]) {
+  if (BF16) {
+    const u32x4 x = *(const u32x4*)((const uint16_t*)base + off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(x[i] << 16);
+      v[2 * i + 1] = __uint_as_float(x[i] & 0xFFFF0000u);
+    }
+  } else {
+    const f32x4 a = *(const f32x4*)((const float*)base + off);
+    const f32x4 c = *(const f32x4*)((const float*)base + off + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = a[i];
+      v[4 + i] = c[i];
+    }
+  }
+}
+
+template <bool BF16>
 __global__ __launch_bounds__(CMB_THREADS) void mla_combine(MlaParams p) {
-  const int q = blockIdx.x;
-  const int layer = blockIdx.y;
-  const int head = blockIdx.z * CMB_HEADS + (threadIdx.x >> 5);
-  const int part = threadIdx.x & 31;
-  constexpr int VS = DC / 32;   // 16 value dims per thread
+  const int head = blockIdx.x * (CMB_THREADS / 64) + (threadIdx.x >> 6);
+  const int q = blockIdx.y;
+  const int layer = blockIdx.z;
+  const int lane = threadIdx.x & 63;
   const int64_t qh = (int64_t)q * H + head;
   const int64_t stride = (int64_t)p.n_layers * p.b.nq * H;  // slots between splits
   const int64_t slot0 = (int64_t)layer * p.b.nq * H + qh;
-  float mx = -INFINITY;
-#pragma unroll 4
-  for (int i = 0; i < p.nsplit; ++i) mx = fmaxf(mx, p.part_ml[(slot0 + i * stride) * 2]);
-  f32x4 acc[VS / 4];
+  float mi = -INFINITY, li = 0.0f;
+  if (lane < p.nsplit) {
+    mi = p.part_ml[(slot0 + lane * stride) * 2];
+    li = p.part_ml[(slot0 + lane * stride) * 2 + 1];
+  }
+  const float mx = wave_max(mi);
+  const float wi = mi == -INFINITY ? 0.0f : exp2f(mi - mx) * li;
+  const float den = wave_sum(wi);
+  float acc[8];
 #pragma unroll
-  for (int v = 0; v < VS / 4; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float den = 0.0f;
-  // four splits at a time, every load of a batch issued before any is used;
-  // an empty split (max -inf) weighs 0
-  constexpr int CB = 4;
-  for (int i0 = 0; i0 < p.nsplit; i0 += CB) {
-    float wgt[CB], sum[CB];
-    f32x4 val[CB][VS / 4];
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+  for (int i0 = 0; i0 < p.nsplit; i0 += CMB_BATCH) {
+    float val[CMB_BATCH][8];
+    float w[CMB_BATCH];
 #pragma unroll
-    for (int c = 0; c < CB; ++c) {
-      const bool ok = i0 + c < p.nsplit;
-      const int64_t slot = slot0 + (int64_t)(ok ? i0 + c : 0) * stride;
-      const float mi = p.part_ml[slot * 2];
-      sum[c] = p.part_ml[slot * 2 + 1];
-      wgt[c] = (!ok || mi == -INFINITY) ? 0.0f : exp2f(mi - mx);
-      const f32x4* pa = (const f32x4*)(p.part_acc + slot * DC) + part;
-#pragma unroll
-      for (int v = 0; v < VS / 4; ++v) val[c][v] = pa[32 * v];
+    for (int c = 0; c < CMB_BATCH; ++c) {
+      const int i = min(i0 + c, p.nsplit - 1);
+      w[c] = i0 + c < p.nsplit ? __shfl(wi, i) : 0.0f;
+      load8<BF16>(p.part_o, (slot0 + i * stride) * DC + 8 * lane, val[c]);
     }
 #pragma unroll
-    for (int c = 0; c < CB; ++c) {
-      den += wgt[c] * sum[c];
+    for (int c = 0; c < CMB_BATCH; ++c)
 #pragma unroll
-      for (int v = 0; v < VS / 4; ++v) acc[v] += wgt[c] * val[c][v];
-    }
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(w[c], val[c][e], acc[e]);
   }
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-#pragma unroll
-  for (int v = 0; v < VS / 4; ++v) store_out4(p, layer, qh * DC + 4 * (part + 32 * v), acc[v] * inv);
-  if (part == 0 && p.L.lse[layer]) p.L.lse[layer][qh] = den > 0.0f ? (mx + log2f(den)) * LN2 : -INFINITY;
+  const int64_t off = qh * DC + 8 * lane;
+  store_out4(p, layer, off, f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv});
+  store_out4(p, layer, off + 4, f32x4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv});
+  if (lane == 0 && p.L.lse[layer]) p.L.lse[layer][qh] = den > 0.0f ? (mx + log2f(den)) * LN2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -596,13 +643,13 @@ hipError_t launch_mla(const BatchDev& b, int dtype, int rope, const MlaLayers& l
   p.out_bf16 = out_dtype == 1;
   p.scale_log2 = scale * 1.44269504088896340736f;
   p.L = layers;
-  p.part_acc = nullptr;
+  p.part_o = nullptr;
   p.part_ml = nullptr;
   if (p.nsplit > 1) {
     const size_t slots = (size_t)p.nsplit * n_layers * b.nq * H;
     if (ws == nullptr || ws_bytes < mla_workspace_bytes(dtype, b.nq, k, n_layers)) return hipErrorInvalidValue;
-    p.part_acc = (float*)ws;
-    p.part_ml = (float*)ws + slots * DC;
+    p.part_o = ws;
+    p.part_ml = (float*)((char*)ws + slots * DC * mla_partial_bytes(dtype));
   }
   dim3 grid(p.nsplit, b.nq, n_layers);
   if (dtype == 0) {
@@ -618,7 +665,11 @@ hipError_t launch_mla(const BatchDev& b, int dtype, int rope, const MlaLayers& l
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
-  hipLaunchKernelGGL(mla_combine, dim3(b.nq, n_layers, H / CMB_HEADS), dim3(CMB_THREADS), 0, st, p);
+  const dim3 cgrid(H / (CMB_THREADS / 64), b.nq, n_layers);
+  if (dtype == 0)
+    hipLaunchKernelGGL(mla_combine<false>, cgrid, dim3(CMB_THREADS), 0, st, p);
+  else
+    hipLaunchKernelGGL(mla_combine<true>, cgrid, dim3(CMB_THREADS), 0, st, p);
   return hipGetLastError();
 }
 

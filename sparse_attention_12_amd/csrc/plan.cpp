@@ -99,7 +99,7 @@ size_t mla_workspace_bytes(int dtype, int nq, int k, int n_layers) {
   const int ns = mla_num_splits(dtype, nq, k, n_layers);
   if (ns <= 1) return 0;
   const size_t slots = (size_t)ns * n_layers * nq * H;
-  return slots * DC * sizeof(float) + slots * 2 * sizeof(float);
+  return slots * DC * mla_partial_bytes(dtype) + slots * 2 * sizeof(float);
 }
 
 // ---------------------------------------------------------------------------

@@ -70,6 +70,9 @@ constexpr int MLA_TILE = 32;         // positions per bf16 tile
 constexpr int MLA32_TILE = 8;        // positions per fp32 tile
 int mla_num_splits(int dtype, int nq, int k, int n_layers);
 int mla_split_len(int dtype, int k, int nsplit);
+// Bytes per value of a split's output: bf16 for the bf16 kernel, float32
+// for the fp32 one.
+inline size_t mla_partial_bytes(int dtype) { return dtype == 0 ? 4 : 2; }
 size_t mla_workspace_bytes(int dtype, int nq, int k, int n_layers);
 
 // ---------------------------------------------------------------------------
