@@ -95,16 +95,23 @@ __device__ __forceinline__ void idx_decode_range(const BatchDev& b, const uint16
   constexpr int WSTEP = IDX_DEC_WAVES * IDX_DEC_STEP;
 
   // Keys past the range end re-read its last row (a cache hit), so every
-  // load is unconditional and four stages stay in flight.
+  // load is unconditional and four stages stay in flight.  Plain (temporal)
+  // loads: the non-temporal hint measured 3-12% slower on long and ragged
+  // batches.
   auto load = [&](KeyTile& kt, int k) {
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
       const uint16_t* p = kb + (int64_t)min(k + kb2 * 16 + c16, last) * DI;
 #pragma unroll
-      for (int st = 0; st < 4; ++st) kt.v[kb2 * 4 + st] = load16_nt(p + st * 32);
+      for (int st = 0; st < 4; ++st) kt.v[kb2 * 4 + st] = load16(p + st * 32);
     }
   };
+  // The two key blocks' sums end up in every lane group, so lane group kb
+  // stores block kb: one store instruction writes the step's 32 scores, a
+  // whole 128-byte line (two 64-byte half-line stores cost the decode batch
+  // of four 2^20-position sequences 14% of its time).
   auto score = [&](const KeyTile& kt, int k) {
+    float part[2];
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
       f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
@@ -114,18 +121,19 @@ __device__ __forceinline__ void idx_decode_range(const BatchDev& b, const uint16
         acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0][st], bk, acc0, 0, 0, 0);
         acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1][st], bk, acc1, 0, 0, 0);
       }
-      float part = 0.0f;
+      float x = 0.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        part = fmaf(wr[0][i], relu(acc0[i]), part);
-        part = fmaf(wr[1][i], relu(acc1[i]), part);
+        x = fmaf(wr[0][i], relu(acc0[i]), x);
+        x = fmaf(wr[1][i], relu(acc1[i]), x);
       }
-      part = rows4_sum(part);
-      const int key = k + kb2 * 16 + c16;
-      if (g == 0 && key < end) {
-        out[key] = part;
-        count_score<HIST>(lh, part);
-      }
+      part[kb2] = rows4_sum(x);
+    }
+    const int key = k + g * 16 + c16;
+    if (g < 2 && key < end) {
+      const float x = g == 0 ? part[0] : part[1];
+      out[key] = x;
+      count_score<HIST>(lh, x);
     }
   };
 
@@ -199,11 +207,14 @@ __device__ __forceinline__ void idx_decode_range_f8(const BatchDev& b, const uin
 #pragma unroll
     for (int kb4 = 0; kb4 < 4; ++kb4) {
       const uint8_t* p = kb + (int64_t)min(k + kb4 * 16 + c16, last) * DI;
-      kt.v[kb4 * 2 + 0] = load16_nt(p);
-      kt.v[kb4 * 2 + 1] = load16_nt(p + 64);
+      kt.v[kb4 * 2 + 0] = load16(p);
+      kt.v[kb4 * 2 + 1] = load16(p + 64);
     }
   };
+  // lane group kb stores key block kb: one store instruction writes the
+  // step's 64 scores (two whole 128-byte lines)
   auto score = [&](const KeyTile8& kt, int k) {
+    float part[4];
 #pragma unroll
     for (int kb4 = 0; kb4 < 4; ++kb4) {
       const i32x8 bk = cat32(kt.v[kb4 * 2], kt.v[kb4 * 2 + 1]);
@@ -211,18 +222,19 @@ __device__ __forceinline__ void idx_decode_range_f8(const BatchDev& b, const uin
       // format 0 = FP8 E4M3 for both operands, no block scaling
       const f32x4 acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[0], bk, zero, 0, 0, 0, 0, 0, 0);
       const f32x4 acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[1], bk, zero, 0, 0, 0, 0, 0, 0);
-      float part = 0.0f;
+      float x = 0.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        part = fmaf(wr[0][i], relu(acc0[i]), part);
-        part = fmaf(wr[1][i], relu(acc1[i]), part);
+        x = fmaf(wr[0][i], relu(acc0[i]), x);
+        x = fmaf(wr[1][i], relu(acc1[i]), x);
       }
-      part = rows4_sum(part);
-      const int key = k + kb4 * 16 + c16;
-      if (g == 0 && key < end) {
-        out[key] = part;
-        count_score<HIST>(lh, part);
-      }
+      part[kb4] = rows4_sum(x);
+    }
+    const int key = k + g * 16 + c16;
+    if (key < end) {
+      const float x = g == 0 ? part[0] : (g == 1 ? part[1] : (g == 2 ? part[2] : part[3]));
+      out[key] = x;
+      count_score<HIST>(lh, x);
     }
   };
 
