@@ -242,10 +242,10 @@ static int run_selection(const dsa::BatchDev& b, int32_t index_dtype, const void
   uint32_t* hist = (uint32_t*)(base + f.hist);
   bool counted = false;
   if ((st = hip_status(
-           dsa::launch_index_score(b, index_dtype, q_idx, w_idx, k_idx, scores, b.max_len, s, hist, &counted),
+           dsa::launch_index_score(b, index_dtype, q_idx, w_idx, k_idx, scores, f.score_ld, s, hist, &counted),
            "index score launch")))
     return st;
-  return hip_status(dsa::launch_topk(b, scores, b.max_len, k, idx, nullptr, base + f.topk, f.mla - f.topk, s,
+  return hip_status(dsa::launch_topk(b, scores, f.score_ld, k, idx, nullptr, base + f.topk, f.mla - f.topk, s,
                                      counted ? hist : nullptr),
                     "top-k launch");
 }

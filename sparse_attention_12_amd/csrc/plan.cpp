@@ -108,8 +108,9 @@ size_t mla_workspace_bytes(int dtype, int nq, int k, int n_layers) {
 FusedLayout fused_layout(int nq, int max_len, int k, int n_layers) {
   FusedLayout f;
   size_t off = 0;
+  f.score_ld = ((int64_t)max_len + 3) & ~(int64_t)3;
   f.scores = off;
-  off = round256(off + (size_t)nq * (size_t)max_len * sizeof(float));
+  off = round256(off + (size_t)nq * (size_t)f.score_ld * sizeof(float));
   f.idx = off;
   off = round256(off + (size_t)nq * (size_t)k * sizeof(int32_t));
   f.hist = off;

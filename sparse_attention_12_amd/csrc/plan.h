@@ -79,7 +79,8 @@ size_t mla_workspace_bytes(int dtype, int nq, int k, int n_layers);
 // fused decode workspace
 // ---------------------------------------------------------------------------
 struct FusedLayout {
-  size_t scores;   // [nq][max_len] float32
+  int64_t score_ld;  // row stride of the scores: max_len rounded up to a multiple of 4 (16-byte rows)
+  size_t scores;   // [nq][score_ld] float32
   size_t idx;      // [nq][k] int32 (when the caller passes no idx_out)
   size_t hist;     // [nq][TK_BINS1] uint32: the indexer's score histogram, zero between calls
   size_t topk;     // top-k workspace

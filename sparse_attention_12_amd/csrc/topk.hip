@@ -202,13 +202,23 @@ struct ListShared {
     uint32_t hcopies[TK_BINS1 * TK_HCOPIES];  // first-level histogram copies, before the list exists
   };
   uint32_t hist[1 << 10];
+  uint32_t lo_min[1 << 10];  // per bin of the first 10-bit level: least and greatest key bits below it
+  uint32_t lo_max[1 << 10];
   ScanShared ss;
 };
 static_assert(2 * TK_FCAP >= TK_BINS1 * TK_HCOPIES, "the histogram copies fit in the list area");
+static_assert(TK_FCAP < (1 << 16), "list counts fit the 16-bit fields of a packed scan");
 
 // The list holds, in ascending position order, every position whose top 12
 // key bits are >= d1 (`total` entries, `need` of bucket d1 still to take).
 // Writes the kept positions in order to out[0, k).
+// Two 10-bit levels fix the k-th key T.  The first also records each bin's
+// range of the 10 key bits below it: when the bin holding T has one key
+// value (tied scores, as integer or FP8 indexer inputs make), T is known
+// and the second level is skipped.  The kept entries are those above T and
+// the first `need` equal to T: one block scan of the packed per-thread
+// counts (above T, equal to T) gives each thread both its tie rank r and
+// its first output slot (entries above T before it, plus min(r, need)).
 __device__ void finalize_list(ListShared& sm, int total, uint32_t d1, uint32_t need, int32_t* out) {
   const int tid = threadIdx.x;
   uint32_t prefix = d1;
@@ -216,11 +226,26 @@ __device__ void finalize_list(ListShared& sm, int total, uint32_t d1, uint32_t n
   while (plen < 32) {
     const int bits = 10;
     const int shift = 32 - plen - bits;
-    for (int i = tid; i < (1 << bits); i += TK_THREADS) sm.hist[i] = 0;
+    const bool range = shift > 0;
+    const uint32_t low = (1u << shift) - 1u;
+    for (int i = tid; i < (1 << bits); i += TK_THREADS) {
+      sm.hist[i] = 0;
+      if (range) {
+        sm.lo_min[i] = 0xffffffffu;
+        sm.lo_max[i] = 0u;
+      }
+    }
     __syncthreads();
     for (int e = tid; e < total; e += TK_THREADS) {
       const uint32_t u = sm.ukey[e];
-      if ((u >> (32 - plen)) == prefix) atomicAdd(&sm.hist[(u >> shift) & ((1u << bits) - 1)], 1u);
+      if ((u >> (32 - plen)) == prefix) {
+        const uint32_t bin = (u >> shift) & ((1u << bits) - 1);
+        atomicAdd(&sm.hist[bin], 1u);
+        if (range) {
+          atomicMin(&sm.lo_min[bin], u & low);
+          atomicMax(&sm.lo_max[bin], u & low);
+        }
+      }
     }
     __syncthreads();
     int d;
@@ -230,6 +255,10 @@ __device__ void finalize_list(ListShared& sm, int total, uint32_t d1, uint32_t n
     const uint32_t cnt = sm.hist[d];
     prefix = (prefix << bits) | (uint32_t)d;
     plen += bits;
+    if (range && sm.lo_min[d] == sm.lo_max[d]) {
+      prefix = (prefix << shift) | sm.lo_min[d];
+      plen = 32;
+    }
     __syncthreads();
     if (cnt == need) break;
   }
@@ -238,19 +267,15 @@ __device__ void finalize_list(ListShared& sm, int total, uint32_t d1, uint32_t n
   const int per = (total + TK_THREADS - 1) / TK_THREADS;
   const int e0 = min(tid * per, total);
   const int e1 = min(e0 + per, total);
-  uint32_t ties = 0;
-  for (int e = e0; e < e1; ++e) ties += ((sm.ukey[e] >> s) == prefix) ? 1u : 0u;
-  uint32_t tie_rank = block_exclusive_scan(ties, sm.ss.wsum, &sm.ss.total);
-  uint32_t keeps = 0;
-  {
-    uint32_t tr = tie_rank;
-    for (int e = e0; e < e1; ++e) {
-      const uint32_t v = sm.ukey[e] >> s;
-      if (v > prefix) ++keeps;
-      else if (v == prefix) keeps += (tr++ < need) ? 1u : 0u;
-    }
+  uint32_t gt = 0, ties = 0;
+  for (int e = e0; e < e1; ++e) {
+    const uint32_t v = sm.ukey[e] >> s;
+    gt += v > prefix ? 1u : 0u;
+    ties += v == prefix ? 1u : 0u;
   }
-  uint32_t slot = block_exclusive_scan(keeps, sm.ss.wsum, &sm.ss.total);
+  const uint32_t pre = block_exclusive_scan(gt | (ties << 16), sm.ss.wsum, &sm.ss.total);
+  uint32_t tie_rank = pre >> 16;
+  uint32_t slot = (pre & 0xffffu) + min(tie_rank, need);
   for (int e = e0; e < e1; ++e) {
     const uint32_t v = sm.ukey[e] >> s;
     bool keep = v > prefix;
@@ -438,30 +463,47 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_reg_kernel(BatchDev b, co
     const uint32_t need = (uint32_t)k - above;
     const uint32_t total = above + sm.hist1[d1];
     if (total <= (uint32_t)TK_FCAP) {
-      // ordered compaction of the keys with top 12 bits >= d1, one block
-      // scan per stretch
+      // ordered compaction of the keys with top 12 bits >= d1: every
+      // stretch's per-thread count (at most 16; at most 16,384 per stretch)
+      // in a 16-bit field, two stretches to a word, so one block scan
+      // orders two stretches
+      constexpr int NW = (NST + 1) / 2;
+      uint32_t f[NST], cw[NW], pw[NW], tw[NW];
+#pragma unroll
+      for (int w = 0; w < NW; ++w) cw[w] = 0;
+#pragma unroll
+      for (int st = 0; st < NST; ++st) {
+        const int s0 = st * TK_STRETCH + tid * TK_RUN;
+        f[st] = 0;
+#pragma unroll
+        for (int j = 0; j < TK_RUN; ++j)
+          if (s0 + j < n && (u[st][j] >> TK_SHIFT1) >= (uint32_t)d1) f[st] |= 1u << j;
+        cw[st >> 1] |= (uint32_t)__builtin_popcount(f[st]) << (16 * (st & 1));
+      }
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        pw[w] = block_exclusive_scan(cw[w], sm.list.ss.wsum, &sm.list.ss.total);
+        tw[w] = sm.list.ss.total;
+      }
       uint32_t base = 0;
 #pragma unroll
       for (int st = 0; st < NST; ++st) {
         const int s0 = st * TK_STRETCH + tid * TK_RUN;
-        uint32_t f = 0;
-#pragma unroll
-        for (int j = 0; j < TK_RUN; ++j)
-          if (s0 + j < n && (u[st][j] >> TK_SHIFT1) >= (uint32_t)d1) f |= 1u << j;
-        uint32_t pslot = block_exclusive_scan(__builtin_popcount(f), sm.list.ss.wsum, &sm.list.ss.total);
+        const int sh = 16 * (st & 1);
+        uint32_t slot = base + ((pw[st >> 1] >> sh) & 0xffffu);
 #pragma unroll
         for (int j = 0; j < TK_RUN; ++j) {
-          if (f & (1u << j)) {
-            const uint32_t slot = base + pslot++;
+          if (f[st] & (1u << j)) {
             if (slot < (uint32_t)TK_FCAP) {
               sm.list.ukey[slot] = u[st][j];
               sm.list.pos[slot] = s0 + j;
             }
+            ++slot;
           }
         }
-        base += sm.list.ss.total;
-        __syncthreads();
+        base += (tw[st >> 1] >> sh) & 0xffffu;
       }
+      __syncthreads();
       if (n > REG) {
         compact_chunk(row, REG, n, (uint32_t)d1, sm.list.ukey + base, sm.list.pos + base, TK_FCAP - base, sm.list.ss);
         __syncthreads();

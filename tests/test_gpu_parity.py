@@ -300,6 +300,10 @@ def test_topk_engineered_rows(B, k, long_row):
         rng.integers(0, 3, 40000).astype(np.float32) * 1000.0,          # three huge tie groups
         rng.standard_normal(max(1, k - 3)).astype(np.float32),          # fewer candidates than k
         np.full(k, 5.0, np.float32),                                    # exactly k candidates
+        # three keys one ulp apart: one 22-bit bin holds them all, so the
+        # second 10-bit level must split them
+        (np.float32(3.0) + rng.integers(0, 3, 9000).astype(np.float32) * np.spacing(np.float32(3.0))
+         ).astype(np.float32),
     ]
     if long_row:
         rows.append(rng.integers(0, 9, 60000).astype(np.float32))
