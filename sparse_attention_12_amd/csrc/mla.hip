@@ -47,6 +47,19 @@ struct MlaParams {
 
 constexpr float LN2 = 0.69314718055994530942f;
 
+// Workgroups reach the eight XCDs round-robin in dispatch order: workgroup
+// L of a one-dimensional grid runs on XCD L % 8.  xcd_item gives XCD x one
+// contiguous range of the grid's N items (N/8 of them, one more for the
+// first N % 8 XCDs), so items that are numbered together share one L2.  The
+// attention and merge grids both number their items (layer, query)-major,
+// so the splits of one query's layer read its query rows into one L2 and
+// the merge finds their partials there.
+__device__ inline int xcd_item(int L, int N) {
+  const int x = L & 7;
+  const int q8 = N >> 3;
+  return x * q8 + min(x, N & 7) + (L >> 3);
+}
+
 __device__ inline void store_out4(const MlaParams& p, int layer, int64_t off, f32x4 v) {
   if (p.out_bf16) {
     uint16_t* o = (uint16_t*)p.L.out[layer] + off;
@@ -311,9 +324,10 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_bf16_kernel(MlaParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t scratch_blk[1024];  // target of the filler gathers
   __shared__ int sel_l[MLA_SPLIT_MAX];
   __shared__ __attribute__((aligned(16))) f32x4 xpart[8][64][2];  // partial logits per wave
-  const int split = blockIdx.x;
-  const int q = blockIdx.y;
-  const int layer = blockIdx.z;
+  const int item = xcd_item(blockIdx.x, p.nsplit * p.b.nq * p.n_layers);
+  const int split = item % p.nsplit;
+  const int q = (item / p.nsplit) % p.b.nq;
+  const int layer = item / (p.nsplit * p.b.nq);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -586,9 +600,11 @@ __device__ inline void load8(const void* base, int64_t off, float (&v)[8]) {
 
 template <bool BF16>
 __global__ __launch_bounds__(CMB_THREADS) void mla_combine(MlaParams p) {
-  const int head = blockIdx.x * (CMB_THREADS / 64) + (threadIdx.x >> 6);
-  const int q = blockIdx.y;
-  const int layer = blockIdx.z;
+  constexpr int HG = H / (CMB_THREADS / 64);  // head groups per (query, layer)
+  const int item = xcd_item(blockIdx.x, HG * p.b.nq * p.n_layers);
+  const int head = (item % HG) * (CMB_THREADS / 64) + (threadIdx.x >> 6);
+  const int q = (item / HG) % p.b.nq;
+  const int layer = item / (HG * p.b.nq);
   const int lane = threadIdx.x & 63;
   const int64_t qh = (int64_t)q * H + head;
   const int64_t stride = (int64_t)p.n_layers * p.b.nq * H;  // slots between splits
@@ -658,14 +674,15 @@ hipError_t launch_mla(const BatchDev& b, int dtype, int rope, const MlaLayers& l
     else
       hipLaunchKernelGGL(mla_f32_kernel<0>, grid, dim3(MLA32_THREADS), 0, st, p);
   } else {
+    const dim3 grid1(p.nsplit * b.nq * n_layers);
     if (rope)
-      hipLaunchKernelGGL(mla_bf16_kernel<DR>, grid, dim3(MLA_THREADS), 0, st, p);
+      hipLaunchKernelGGL(mla_bf16_kernel<DR>, grid1, dim3(MLA_THREADS), 0, st, p);
     else
-      hipLaunchKernelGGL(mla_bf16_kernel<0>, grid, dim3(MLA_THREADS), 0, st, p);
+      hipLaunchKernelGGL(mla_bf16_kernel<0>, grid1, dim3(MLA_THREADS), 0, st, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
-  const dim3 cgrid(H / (CMB_THREADS / 64), b.nq, n_layers);
+  const dim3 cgrid(H / (CMB_THREADS / 64) * b.nq * n_layers);
   if (dtype == 0)
     hipLaunchKernelGGL(mla_combine<false>, cgrid, dim3(CMB_THREADS), 0, st, p);
   else
