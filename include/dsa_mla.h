@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 3
+#define DSA_ABI_VERSION 4
 
 #define DSA_INDEX_HEADS 32  /* indexer heads                          */
 #define DSA_INDEX_DIM 128   /* indexer head width                     */
@@ -135,6 +135,35 @@ int32_t dsa_abi_version(void);
 const char* dsa_status_string(int32_t status);
 /* Detail of the last failing call on this thread ("" if none). */
 const char* dsa_last_error(void);
+
+/*
+ * Checks of a debug build (for callers chasing a wrong result, not a
+ * contract of the method).  A library built with -DDSA_DEBUG checks, inside
+ * its kernels, what the release build only guards or assumes, and records
+ * each failed check as a bit instead of trapping:
+ *   DSA_DEBUG_IDX_RANGE     an MLA selection entry outside [-1, n_cand)
+ *                           (skipped by both builds, flagged by this one)
+ *   DSA_DEBUG_TOPK_SLOT     a top-k output or candidate slot past its bound
+ *   DSA_DEBUG_LIST          the split top-k's chunk lists disagree with its
+ *                           histogram
+ *   DSA_DEBUG_SCORE_COL     an indexer score column at or past ld
+ *   DSA_DEBUG_HIST_RECOUNT  a workspace's precounted top-k histogram failed
+ *                           its check and was recounted (expected on a
+ *                           workspace's first use, not after)
+ *   DSA_DEBUG_GATHER_ROW    an MLA gather row below -1
+ * dsa_debug_flags waits for the device (hipDeviceSynchronize), stores the
+ * union of the bits set since the last reset in *flags and, with reset != 0,
+ * clears them.  flags: host pointer.  Release builds return
+ * DSA_ERR_UNSUPPORTED and leave *flags untouched; a NULL flags is
+ * DSA_ERR_NULL; a HIP failure is DSA_ERR_HIP.
+ */
+#define DSA_DEBUG_IDX_RANGE 1u
+#define DSA_DEBUG_TOPK_SLOT 2u
+#define DSA_DEBUG_LIST 4u
+#define DSA_DEBUG_SCORE_COL 8u
+#define DSA_DEBUG_HIST_RECOUNT 16u
+#define DSA_DEBUG_GATHER_ROW 32u
+int32_t dsa_debug_flags(uint32_t* flags, int32_t reset);
 
 /*
  * Indexer scores ("Where to look" / "Sparse attention"; formula above).

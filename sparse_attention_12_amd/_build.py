@@ -10,6 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdsa_mla.so")
+DEBUG_LIB = os.path.join(HERE, "libdsa_mla_debug.so")  # the same sources with -DDSA_DEBUG
 SOURCES = ["abi.hip", "noalloc.hip", "plan.cpp", "indexer.hip", "topk.hip", "mla.hip", "rope.hip"]
 ARCH = "gfx950"
 
@@ -22,28 +23,40 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, src + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(job) -> str:
+    src, debug = job
+    obj = os.path.join(BUILD, src + (".debug.o" if debug else ".o"))
+    cmd = [HIPCC, *FLAGS, *(["-DDSA_DEBUG"] if debug else []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
+        raise RuntimeError(f"hipcc failed on {src}{' (debug)' if debug else ''}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source for gfx950 and link libdsa_mla.so (always rebuilds)."""
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, debug: bool = True) -> str:
+    """Compile every HIP source for gfx950 and link libdsa_mla.so, and with
+    debug also libdsa_mla_debug.so (the kernels' checks compiled in); always
+    rebuilds."""
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = [(s, False) for s in SOURCES] + ([(s, True) for s in SOURCES] if debug else [])
+    with cf.ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 8)) as ex:
+        objs = list(ex.map(_compile, jobs))
+    _link(objs[:len(SOURCES)], LIB)
     if verbose:
         print(f"built {LIB}")
+    if debug:
+        _link(objs[len(SOURCES):], DEBUG_LIB)
+        if verbose:
+            print(f"built {DEBUG_LIB}")
     return LIB
 
 

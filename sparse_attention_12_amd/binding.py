@@ -24,8 +24,10 @@ EXPORTS = [
     "dsa_topk_workspace_size", "dsa_topk", "mla_sparse_attend_workspace_size",
     "mla_sparse_attend", "dsa_mla_decode_fused_workspace_size", "dsa_mla_decode_fused",
     "dsa_ml4_layer_plan", "dsa_mla_decode_layers_workspace_size", "dsa_mla_decode_layers",
-    "dsa_rope_frequencies", "dsa_rope_append", "dsa_mla_decode_fused_noalloc",
+    "dsa_rope_frequencies", "dsa_rope_append", "dsa_mla_decode_fused_noalloc", "dsa_debug_flags",
 ]
+DEBUG_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa_mla_debug.so")
+DEBUG_BITS = {"idx_range": 1, "topk_slot": 2, "list": 4, "score_col": 8, "hist_recount": 16, "gather_row": 32}
 NOALLOC_SCRATCH_BYTES = 128 << 20
 ML4_LAYERS = 72
 
@@ -45,11 +47,13 @@ class DsaBatch(ctypes.Structure):
     ]
 
 
-def _load() -> ctypes.CDLL:
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+def _load(path: str = None) -> ctypes.CDLL:
+    """The library at path (default: the release build), its prototypes set."""
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with __graft_entry__.build() "
                           "(hipcc --offload-arch=gfx950); there is no CPU fallback")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     bp = ctypes.POINTER(DsaBatch)
     lib.dsa_abi_version.restype = i32
@@ -86,10 +90,29 @@ def _load() -> ctypes.CDLL:
     lib.dsa_rope_frequencies.restype = i32
     lib.dsa_rope_append.argtypes = [bp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.dsa_rope_append.restype = i32
+    lib.dsa_debug_flags.argtypes = [ctypes.POINTER(ctypes.c_uint32), i32]
+    lib.dsa_debug_flags.restype = i32
     return lib
 
 
 lib = _load()
+
+
+def load_debug_library() -> ctypes.CDLL:
+    """The debug build (kernel checks compiled in), with the same prototypes.
+    Calls go to it while it is assigned to this module's `lib`."""
+    return _load(DEBUG_LIB_PATH)
+
+
+def debug_flags(reset: bool = True, library=None) -> int:
+    """Union of the debug checks' bits set since the last reset (DEBUG_BITS);
+    waits for the device.  Raises DsaError on a release build."""
+    L = library or lib
+    v = ctypes.c_uint32(0)
+    st = L.dsa_debug_flags(ctypes.byref(v), 1 if reset else 0)
+    if st != 0:
+        raise DsaError(st, "dsa_debug_flags")
+    return int(v.value)
 
 
 class DsaError(RuntimeError):

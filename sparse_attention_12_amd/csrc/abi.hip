@@ -1,6 +1,8 @@
 // C ABI of the library (declared in include/dsa_mla.h): host-side argument
 // validation, workspace accounting and kernel dispatch.  Nothing here
-// allocates, frees or synchronises; every launch goes to the caller's stream.
+// allocates, frees or synchronises (except the debug build's
+// dsa_debug_flags, which waits for the device); every launch goes to the
+// caller's stream.
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -122,6 +124,30 @@ int abi_hip_status(hipError_t e, const char* what) { return hip_status(e, what);
 extern "C" {
 
 int32_t dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+int32_t dsa_debug_flags(uint32_t* flags, int32_t reset) {
+  if (flags == nullptr) return fail(DSA_ERR_NULL, "flags is NULL");
+#ifdef DSA_DEBUG
+  static_assert(DSA_DEBUG_IDX_RANGE == dsa::DBG_IDX_RANGE && DSA_DEBUG_TOPK_SLOT == dsa::DBG_TOPK_SLOT &&
+                    DSA_DEBUG_LIST == dsa::DBG_LIST && DSA_DEBUG_SCORE_COL == dsa::DBG_SCORE_COL &&
+                    DSA_DEBUG_HIST_RECOUNT == dsa::DBG_HIST_RECOUNT && DSA_DEBUG_GATHER_ROW == dsa::DBG_GATHER_ROW,
+                "header bits match the kernels' bits");
+  int st;
+  if ((st = hip_status(hipDeviceSynchronize(), "device synchronize"))) return st;
+  const uint32_t parts[3] = {dsa::debug_flags_indexer(reset != 0), dsa::debug_flags_topk(reset != 0),
+                             dsa::debug_flags_mla(reset != 0)};
+  uint32_t v = 0;
+  for (uint32_t x : parts) {
+    if (x == 0xffffffffu) return fail(DSA_ERR_HIP, "reading the debug flags failed");
+    v |= x;
+  }
+  *flags = v;
+  return DSA_OK;
+#else
+  (void)reset;
+  return fail(DSA_ERR_UNSUPPORTED, "a release build has no debug checks (build with DSA_DEBUG)");
+#endif
+}
 
 const char* dsa_status_string(int32_t st) {
   switch (st) {

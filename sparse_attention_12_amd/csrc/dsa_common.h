@@ -30,6 +30,41 @@ struct QueryRange {
   int64_t row0; // first row of the query's sequence in the caches
 };
 
+// Checks of a debug build (-DDSA_DEBUG): a failed check sets its bit in the
+// translation unit's flag word, read and cleared from the host through
+// dsa_debug_flags; nothing traps.  Release builds compile the checks away.
+constexpr uint32_t DBG_IDX_RANGE = 1u;     // an MLA selection entry outside [-1, n) (skipped)
+constexpr uint32_t DBG_TOPK_SLOT = 2u;     // a top-k output or candidate slot past its bound
+constexpr uint32_t DBG_LIST = 4u;          // the split path's chunk lists disagree with the histogram
+constexpr uint32_t DBG_SCORE_COL = 8u;     // an indexer score column at or past the row stride
+constexpr uint32_t DBG_HIST_RECOUNT = 16u; // a precounted histogram failed its check and was recounted
+constexpr uint32_t DBG_GATHER_ROW = 32u;   // an MLA gather row past its sequence
+#ifdef DSA_DEBUG
+static __device__ uint32_t dbg_flags;
+#define DSA_CHECK(cond, bit)                 \
+  do {                                       \
+    if (!(cond)) atomicOr(&dbg_flags, (bit)); \
+  } while (0)
+// Reads (and, with reset, clears) this translation unit's flag word
+// (synchronous; defined once per unit by DSA_DEBUG_READER).
+#define DSA_DEBUG_READER(fn)                                                          \
+  uint32_t fn(bool reset) {                                                           \
+    uint32_t v = 0;                                                                   \
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(dbg_flags), sizeof(v), 0, hipMemcpyDeviceToHost) != hipSuccess) \
+      return 0xffffffffu;                                                             \
+    if (reset) {                                                                      \
+      const uint32_t z = 0;                                                           \
+      if (hipMemcpyToSymbol(HIP_SYMBOL(dbg_flags), &z, sizeof(z), 0, hipMemcpyHostToDevice) != hipSuccess) \
+        return 0xffffffffu;                                                           \
+    }                                                                                 \
+    return v;                                                                         \
+  }
+#else
+#define DSA_CHECK(cond, bit) \
+  do {                       \
+  } while (0)
+#endif
+
 // Candidates of query q: its own position and every earlier one, clamped to
 // the sequence length and to max_len (so no access leaves the sequence).
 __device__ inline QueryRange query_range(const BatchDev& b, int q) {

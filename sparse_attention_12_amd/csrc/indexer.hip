@@ -132,6 +132,7 @@ __device__ __forceinline__ void idx_decode_range(const BatchDev& b, const uint16
     const int key = k + g * 16 + c16;
     if (g < 2 && key < end) {
       const float x = g == 0 ? part[0] : part[1];
+      DSA_CHECK(key < ld, DBG_SCORE_COL);
       out[key] = x;
       count_score<HIST>(lh, x);
     }
@@ -233,6 +234,7 @@ __device__ __forceinline__ void idx_decode_range_f8(const BatchDev& b, const uin
     const int key = k + g * 16 + c16;
     if (key < end) {
       const float x = g == 0 ? part[0] : (g == 1 ? part[1] : (g == 2 ? part[2] : part[3]));
+      DSA_CHECK(key < ld, DBG_SCORE_COL);
       out[key] = x;
       count_score<HIST>(lh, x);
     }
@@ -777,6 +779,10 @@ __global__ __launch_bounds__(PF_THREADS) void idx_prefill_fp8(
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
+#ifdef DSA_DEBUG
+DSA_DEBUG_READER(debug_flags_indexer)
+#endif
+
 hipError_t launch_zero(const ZeroSpans& z, int nq, hipStream_t st) {
   if (nq == 0 || (z.s[0].base == nullptr && z.s[1].base == nullptr)) return hipSuccess;
   hipLaunchKernelGGL(zero_spans_kernel, dim3(nq), dim3(256), 0, st, z);

@@ -44,6 +44,14 @@ ZeroSpan topk_zero_span(void* ws, int nq, int max_len);
 hipError_t launch_topk(const BatchDev& b, const float* scores, int64_t ld, int k, int32_t* idx,
                        int32_t* count, void* ws, size_t ws_bytes, hipStream_t st, uint32_t* hist_pre = nullptr);
 
+#ifdef DSA_DEBUG
+// Flag words of the debug checks, one per kernel source (DBG_* bits in
+// dsa_common.h); each read is synchronous, reset clears the word.
+uint32_t debug_flags_indexer(bool reset);
+uint32_t debug_flags_topk(bool reset);
+uint32_t debug_flags_mla(bool reset);
+#endif
+
 // Sparse MLA over a shared selection for n_layers layers (mla.hip).
 struct MlaLayers {
   const void* q[MLA_MAX_LAYERS];

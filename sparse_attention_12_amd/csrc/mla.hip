@@ -159,6 +159,7 @@ __device__ __forceinline__ void mla_issue(uint8_t* buf, uint8_t* dummy, __amdgpu
     const int gi = blk >> 2;
     const int oc = blk & 3;
     const int row = oc * 8 + (lane >> 3);
+    DSA_CHECK(pos[jj] >= -1, DBG_GATHER_ROW);
     const uint32_t off = (uint32_t)max(pos[jj], 0) * (uint32_t)G::ROWB + (uint32_t)(gi * 8 + ((lane & 7) ^ (row & 7))) * 16u;
     uint8_t* dst = id < G::BLOCKS ? buf + gi * MLA_GROUPB + oc * 1024 : dummy;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(kv, (lds_void*)dst, 16, off, 0, 0, 0);
@@ -368,6 +369,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_bf16_kernel(MlaParams p) {
   for (int i = 0; i < SEL_PER; ++i) {
     const int j = tid + i * MLA_THREADS;
     if (j < max(ntiles, 2) * MLA_TILE) sel_l[j] = (selv[i] >= 0 && selv[i] < r.n) ? selv[i] : -1;
+    DSA_CHECK(j >= nent || (selv[i] >= -1 && selv[i] < r.n), DBG_IDX_RANGE);
   }
   // buffer resource over exactly this sequence's rows (raw addressing): a
   // gather outside them reads zeros and touches no memory
@@ -509,6 +511,7 @@ __global__ __launch_bounds__(MLA32_THREADS) void mla_f32_kernel(MlaParams p) {
       const int j = j0 + rr;
       const int pos = j < j_end ? sel[j] : -1;
       const bool ok = pos >= 0 && pos < r.n;
+      DSA_CHECK(ch != 0 || (pos >= -1 && pos < r.n), DBG_IDX_RANGE);
       ((float4*)tile[rr])[ch] = ((const float4*)(kv + (int64_t)(ok ? pos : 0) * D))[ch];
       if (ch == 0) vflag[rr] = ok;
     }
@@ -644,6 +647,10 @@ __global__ __launch_bounds__(CMB_THREADS) void mla_combine(MlaParams p) {
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
+#ifdef DSA_DEBUG
+DSA_DEBUG_READER(debug_flags_mla)
+#endif
+
 hipError_t launch_mla(const BatchDev& b, int dtype, int rope, const MlaLayers& layers, int n_layers,
                       const int32_t* idx, int k, float scale, int out_dtype, void* ws,
                       size_t ws_bytes, hipStream_t st) {

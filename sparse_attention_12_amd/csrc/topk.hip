@@ -219,7 +219,7 @@ static_assert(TK_FCAP < (1 << 16), "list counts fit the 16-bit fields of a packe
 // the first `need` equal to T: one block scan of the packed per-thread
 // counts (above T, equal to T) gives each thread both its tie rank r and
 // its first output slot (entries above T before it, plus min(r, need)).
-__device__ void finalize_list(ListShared& sm, int total, uint32_t d1, uint32_t need, int32_t* out) {
+__device__ void finalize_list(ListShared& sm, int total, uint32_t d1, uint32_t need, int k, int32_t* out) {
   const int tid = threadIdx.x;
   uint32_t prefix = d1;
   int plen = TK_BITS1;
@@ -281,7 +281,8 @@ __device__ void finalize_list(ListShared& sm, int total, uint32_t d1, uint32_t n
     bool keep = v > prefix;
     if (v == prefix) keep = tie_rank++ < need;
     if (keep) {
-      if (slot < (uint32_t)KMAX) out[slot] = sm.pos[e];
+      DSA_CHECK(slot < (uint32_t)k, DBG_TOPK_SLOT);
+      if (slot < (uint32_t)k) out[slot] = sm.pos[e];
       ++slot;
     }
   }
@@ -324,6 +325,7 @@ __device__ void select_row_streaming(const float* row, int n, int k, uint32_t d1
     const int s = t0 + tid;
     const uint32_t f = (s < n && row_key(row, s) >= thresh) ? 1u : 0u;
     const uint32_t p = block_exclusive_scan(f, ss.wsum, &ss.total);
+    DSA_CHECK(!f || base + p < (uint32_t)k, DBG_TOPK_SLOT);
     if (f && base + p < (uint32_t)k) out[base + p] = s;
     base += ss.total;
     __syncthreads();
@@ -421,6 +423,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_reg_kernel(BatchDev b, co
     constexpr int REG = NST * TK_STRETCH;
     uint32_t* hc = sm.list.hcopies;
     const bool counted = gh && take_precounted(gh, sm.hist1, n, sm.list.ss.red);
+    DSA_CHECK(!gh || counted, DBG_HIST_RECOUNT);
     if (!counted) hist_copies_zero(hc);
     // keys of this thread's runs (positions at or past n are never counted)
     uint32_t u[NST][TK_RUN];
@@ -494,6 +497,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_reg_kernel(BatchDev b, co
 #pragma unroll
         for (int j = 0; j < TK_RUN; ++j) {
           if (f[st] & (1u << j)) {
+            DSA_CHECK(slot < (uint32_t)TK_FCAP, DBG_TOPK_SLOT);
             if (slot < (uint32_t)TK_FCAP) {
               sm.list.ukey[slot] = u[st][j];
               sm.list.pos[slot] = s0 + j;
@@ -508,7 +512,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_reg_kernel(BatchDev b, co
         compact_chunk(row, REG, n, (uint32_t)d1, sm.list.ukey + base, sm.list.pos + base, TK_FCAP - base, sm.list.ss);
         __syncthreads();
       }
-      finalize_list(sm.list, (int)total, (uint32_t)d1, need, out);
+      finalize_list(sm.list, (int)total, (uint32_t)d1, need, k, out);
     } else {
       select_row_streaming(row, n, k, (uint32_t)d1, need, sm.hist1, sm.list.ss, out);
     }
@@ -588,6 +592,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_gather_kernel(BatchDev b, con
   const uint4 hv = ((const uint4*)gh)[tid];
   *(uint4*)(hist + 4 * tid) = hv;
   if (block_sum64((uint64_t)hv.x + hv.y + hv.z + hv.w, ss.red) != (uint64_t)r.n) {
+    DSA_CHECK(false, DBG_HIST_RECOUNT);
     *(uint4*)(hist + 4 * tid) = make_uint4(0u, 0u, 0u, 0u);
     __syncthreads();
     for (int i = tid; i < r.n; i += TK_THREADS) atomicAdd(&hist[score_key(row[i]) >> TK_SHIFT1], 1u);
@@ -612,6 +617,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_gather_kernel(BatchDev b, con
 #pragma unroll
   for (int j = 0; j < GR; ++j) {
     if (f & (1u << j)) {
+      DSA_CHECK(slot < (uint32_t)TK_CHUNK, DBG_LIST);
       ws.lkey[lbase + slot] = u[j];
       ws.lpos[lbase + slot] = s0 + j;
       ++slot;
@@ -656,6 +662,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_final_kernel(BatchDev b, cons
     // by a block scan, then every entry copied in one parallel pass with all
     // of a thread's reads in flight together
     const uint32_t o = block_exclusive_scan(mine, sm.list.ss.wsum, &sm.list.ss.total);
+    DSA_CHECK(sm.list.ss.total == total, DBG_LIST);
     if (tid < nch) sm.off[tid] = o;
     __syncthreads();
     const int64_t lq = (int64_t)q * ws.nchunk * TK_CHUNK;
@@ -694,7 +701,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_final_kernel(BatchDev b, cons
       }
     }
     __syncthreads();
-    finalize_list(sm.list, (int)total, (uint32_t)d1, need, out);
+    finalize_list(sm.list, (int)total, (uint32_t)d1, need, k, out);
   } else {
     select_row_streaming(scores + (int64_t)q * ld, n, k, (uint32_t)d1, need, sm.hist1, sm.list.ss, out);
   }
@@ -704,6 +711,10 @@ __global__ __launch_bounds__(TK_THREADS) void topk_final_kernel(BatchDev b, cons
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
+#ifdef DSA_DEBUG
+DSA_DEBUG_READER(debug_flags_topk)
+#endif
+
 static SplitWs split_ws(int nq, int max_len, char* base) {
   const TopkLayout t = topk_layout(nq, max_len);
   SplitWs ws;

@@ -68,13 +68,41 @@ def _batch(nq=2, nseq=2, max_len=100):
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(lib, n), n
 
 
+DEBUG_LIB = os.path.join(ROOT, "sparse_attention_12_amd", "libdsa_mla_debug.so")
+
+
+def test_debug_library_exports_every_declared_symbol():
+    """The debug build (kernel checks compiled in) has the same interface."""
+    if not os.path.exists(DEBUG_LIB):
+        from sparse_attention_12_amd import _build
+        _build.build()
+    dl = ctypes.CDLL(DEBUG_LIB)
+    for n in _declared():
+        assert hasattr(dl, n), n
+
+
+def test_debug_flags_in_a_release_build(lib):
+    """A release build has no checks to report: DSA_ERR_UNSUPPORTED, and the
+    caller's word is left as it was; a NULL word is DSA_ERR_NULL in either
+    build (checked before anything touches the device)."""
+    lib.dsa_debug_flags.argtypes = [ctypes.c_void_p, ctypes.c_int32]
+    v = ctypes.c_uint32(0xABCD)
+    assert lib.dsa_debug_flags(ctypes.byref(v), 1) == UNSUPPORTED
+    assert v.value == 0xABCD
+    assert b"DSA_DEBUG" in lib.dsa_last_error()
+    assert lib.dsa_debug_flags(None, 0) == NULL
+    dl = ctypes.CDLL(DEBUG_LIB)
+    dl.dsa_debug_flags.argtypes = [ctypes.c_void_p, ctypes.c_int32]
+    assert dl.dsa_debug_flags(None, 1) == NULL
+
+
 def test_version_and_status_strings(lib):
-    assert lib.dsa_abi_version() == 3
+    assert lib.dsa_abi_version() == 4
     for st in (OK, NULL, SHAPE, DTYPE, ALIGN, WORKSPACE, UNSUPPORTED, -7):
         assert lib.dsa_status_string(st)
     assert b"unknown" in lib.dsa_status_string(42)
