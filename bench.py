@@ -181,54 +181,16 @@ class Runner:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
-    def stage(self, fn, n):
-        """ms per call of one stage (fn launches its kernels and nothing
-        else), without the per-call host cost of the Python binding (which
-        exceeds the kernels' own time for the short stages): n and 2n calls
-        captured in two HIP graphs, each replayed three times and timed with
-        HIP events; per call = (best 2n replay - best n replay) / n, which
-        also cancels the graph's start-up (the runtime submits a replay's
-        first nodes with gaps of tens of microseconds).  Falls back to
-        back-to-back eager calls if capture fails."""
-        import torch
-
-        def capture(m):
-            g = torch.cuda.CUDAGraph()
-            side = torch.cuda.Stream()
-            side.wait_stream(self.stream)
-            with torch.cuda.stream(side):
-                with torch.cuda.graph(g, stream=side):
-                    for _ in range(m):
-                        fn()
-            self.stream.wait_stream(side)
-            torch.cuda.synchronize()
-            return g
-
-        def best(g):
-            g.replay()
-            torch.cuda.synchronize()
-            ts = []
-            for _ in range(3):
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(self.stream)
-                g.replay()
-                e1.record(self.stream)
-                torch.cuda.synchronize()
-                ts.append(e0.elapsed_time(e1))
-            return min(ts)
-
-        try:
-            fn()
-            torch.cuda.synchronize()
-            ga, gb = capture(n), capture(2 * n)
-            ta, tb = best(ga), best(gb)
-            del ga, gb
-            return (tb - ta) / n
-        except RuntimeError as e:
-            print(f"[bench] graph capture failed ({e}); timing eager calls", file=sys.stderr, flush=True)
-            torch.cuda.synchronize()
-            return self.timed(fn, n)
+    def stage(self, fn, n, flush):
+        """ms of one stage (fn launches its kernels and nothing else), timed
+        like the step: the median of n calls, each alone after the
+        cache-evicting read (so the 190 MB of keys of the ragged batch are not
+        served from the 256 MB Infinity Cache by the previous call), HIP
+        events on the launch stream around the call; while the flush runs the
+        host has already queued the call, so no per-call host cost is
+        timed."""
+        fn()
+        return statistics.median(self.flushed(fn, n, flush))
 
     def flushed(self, fn, n, flush):
         """ms of each of n calls of fn, each after `flush` (outside its events)."""
@@ -318,9 +280,9 @@ def main():
 
     # per-stage timings of the same kernels, same launch configurations
     R.indexer()
-    idx_ms = R.stage(R.indexer, args.steps)
-    tk_ms = R.stage(R.topk, args.steps)
-    mla_ms = R.stage(R.mla, args.steps)
+    idx_ms = R.stage(R.indexer, args.steps, flush)
+    tk_ms = R.stage(R.topk, args.steps, flush)
+    mla_ms = R.stage(R.mla, args.steps, flush)
     print(f"[bench] {args.steps} flushed steps: median {ms_per_step:.4f} ms (min {min(per_step):.4f}, "
           f"max {max(per_step):.4f}; region {wall:.2f} s); warm {warm_ms:.4f} ms; indexer {idx_ms:.4f} ms, "
           f"top-k {tk_ms:.4f} ms, one-layer MLA {mla_ms:.4f} ms", file=sys.stderr, flush=True)
@@ -379,8 +341,8 @@ def main():
                  "indexer_ms": round(idx_ms, 5), "topk_ms": round(tk_ms, 5),
                  "mla_one_layer_ms": round(mla_ms, 5),
                  "stage_timing": "each stage through its own entry point (dsa_index_score, dsa_topk without the "
-                                 "indexer's histogram, mla_sparse_attend): HIP graphs of K and 2K calls, best of "
-                                 "three replays each, (2K - K) / K"},
+                                 "indexer's histogram, mla_sparse_attend), median of K calls, each after the same "
+                                 "cache-evicting read as the steps"},
         "bars": bars,
     }
     print(json.dumps(rec))
@@ -402,8 +364,8 @@ def extras(args, dev, flush):
     cold = R.flushed(R.step, reps, flush)
     warm = R.timed(R.step, reps)
     R.indexer()
-    idx_ms = R.stage(R.indexer, args.steps)
-    tk_ms = R.stage(R.topk, args.steps)
+    idx_ms = R.stage(R.indexer, args.steps, flush)
+    tk_ms = R.stage(R.topk, args.steps, flush)
     tr = R.traffic()
     med = statistics.median(cold)
     gbps = tr["path_bytes"] / (med / 1e3) / 1e9
@@ -424,7 +386,7 @@ def extras(args, dev, flush):
     for _ in range(max(2, args.warmup // 2)):
         R.step()
     R.indexer()
-    idx_ms = R.stage(R.indexer, args.steps)
+    idx_ms = R.stage(R.indexer, args.steps, flush)
     cold = R.flushed(R.step, max(10, reps // 5), flush)
     med = statistics.median(cold)
     roof = R.indexer_roofline(idx_ms)
