@@ -473,86 +473,170 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_bf16_kernel(MlaParams p) {
 // ---------------------------------------------------------------------------
 // fp32 split kernel (VALU; small fp32 workloads)
 // ---------------------------------------------------------------------------
+// Thread t = (head group hg = t / 16, part = t % 16) owns heads 4hg..4hg+3
+// and a sixteenth of the row: contraction values [part*W/16, +W/16) and value
+// columns [32 part, 32 part + 32).  Each row value read from the LDS tile
+// serves four heads; the four partial logits are summed over the 16 parts
+// (lanes of one DPP row) with lane moves.  The next tile's rows are loaded
+// into registers while the current one is consumed.
 constexpr int MLA32_THREADS = 256;
+constexpr int MLA32_HPT = 4;   // heads per thread
+constexpr int MLA32_PARTS = 16;
+
+// Sum over the 16 lanes of a DPP row; every lane of the row gets the sum.
+__device__ inline float row16_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));  // row_half_mirror
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));  // row_mirror
+  return x;
+}
 
 template <int ROPE>
 __global__ __launch_bounds__(MLA32_THREADS) void mla_f32_kernel(MlaParams p) {
-  constexpr int D = DC + ROPE;  // row width
+  constexpr int D = DC + ROPE;              // row width
+  constexpr int QS = D / MLA32_PARTS;       // 36 (or 32) contraction values per thread
+  constexpr int VS = DC / MLA32_PARTS;      // 32 value columns per thread
+  static_assert(QS % 4 == 0 && VS % 4 == 0, "whole float4 runs");
   __shared__ __attribute__((aligned(16))) float tile[MLA32_TILE][D];
   __shared__ int vflag[MLA32_TILE];
   const int split = blockIdx.x;
   const int q = blockIdx.y;
   const int layer = blockIdx.z;
   const int tid = threadIdx.x;
-  const int head = tid >> 2;   // 4 threads per head
-  const int part = tid & 3;    // quarter of the contraction / of the value dims
+  const int part = tid & (MLA32_PARTS - 1);
+  const int head0 = (tid / MLA32_PARTS) * MLA32_HPT;
   const QueryRange r = query_range(p.b, q);
   const int j_begin = split * p.split_len;
   const int j_end = min(j_begin + p.split_len, p.k);
   const float* kv = (const float*)p.L.kv[layer] + r.row0 * D;
   const int32_t* sel = p.idx + (int64_t)q * p.k;
-  constexpr int QS = D / 4;   // 144 (or 128) contraction dims per thread
-  constexpr int VS = DC / 4;  // 128 value dims per thread
-  float qr[QS];
-  {
-    const float* qp = (const float*)p.L.q[layer] + ((int64_t)q * H + head) * D + part * QS;
+  float qr[MLA32_HPT][QS];
 #pragma unroll
-    for (int i = 0; i < QS; ++i) qr[i] = qp[i];
+  for (int h = 0; h < MLA32_HPT; ++h) {
+    const float4* qp = (const float4*)((const float*)p.L.q[layer] + ((int64_t)q * H + head0 + h) * D + part * QS);
+#pragma unroll
+    for (int i = 0; i < QS / 4; ++i) {
+      const float4 v = qp[i];
+      qr[h][4 * i] = v.x;
+      qr[h][4 * i + 1] = v.y;
+      qr[h][4 * i + 2] = v.z;
+      qr[h][4 * i + 3] = v.w;
+    }
   }
-  float acc[VS];
+  float acc[MLA32_HPT][VS];
+  float m_run[MLA32_HPT], l_run[MLA32_HPT];
 #pragma unroll
-  for (int i = 0; i < VS; ++i) acc[i] = 0.0f;
-  float m_run = -INFINITY, l_run = 0.0f;
-  for (int j0 = j_begin; j0 < j_end && r.n > 0; j0 += MLA32_TILE) {
-    __syncthreads();
-    for (int c = tid; c < MLA32_TILE * D / 4; c += MLA32_THREADS) {
+  for (int h = 0; h < MLA32_HPT; ++h) {
+    m_run[h] = -INFINITY;
+    l_run[h] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < VS; ++i) acc[h][i] = 0.0f;
+  }
+  constexpr int NV = MLA32_TILE * D / 4;  // float4s per tile
+  constexpr int PER = (NV + MLA32_THREADS - 1) / MLA32_THREADS;
+  float4 nxt[PER];
+  bool nok[PER];
+  auto fetch = [&](int j0) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int c = tid + u * MLA32_THREADS;
       const int rr = c / (D / 4);
       const int ch = c - rr * (D / 4);
       const int j = j0 + rr;
-      const int pos = j < j_end ? sel[j] : -1;
-      const bool ok = pos >= 0 && pos < r.n;
-      DSA_CHECK(ch != 0 || (pos >= -1 && pos < r.n), DBG_IDX_RANGE);
-      ((float4*)tile[rr])[ch] = ((const float4*)(kv + (int64_t)(ok ? pos : 0) * D))[ch];
-      if (ch == 0) vflag[rr] = ok;
+      const int pos = (c < NV && j < j_end) ? sel[j] : -1;
+      nok[u] = pos >= 0 && pos < r.n;
+      DSA_CHECK(c >= NV || ch != 0 || (pos >= -1 && pos < r.n), DBG_IDX_RANGE);
+      nxt[u] = c < NV ? ((const float4*)(kv + (int64_t)(nok[u] ? pos : 0) * D))[ch] : float4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  if (j_begin < j_end && r.n > 0) fetch(j_begin);
+  for (int j0 = j_begin; j0 < j_end && r.n > 0; j0 += MLA32_TILE) {
+    __syncthreads();  // the previous tile is consumed
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int c = tid + u * MLA32_THREADS;
+      if (c < NV) {
+        const int rr = c / (D / 4);
+        const int ch = c - rr * (D / 4);
+        ((float4*)tile[rr])[ch] = nxt[u];
+        if (ch == 0) vflag[rr] = nok[u];
+      }
     }
     __syncthreads();
+    if (j0 + MLA32_TILE < j_end) fetch(j0 + MLA32_TILE);
     for (int rr = 0; rr < MLA32_TILE; ++rr) {
       if (!vflag[rr]) continue;
-      const float* row = tile[rr];
-      float dot = 0.0f;
+      const float4* krow = (const float4*)(tile[rr] + part * QS);
+      float dot[MLA32_HPT] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < QS; ++i) dot = fmaf(qr[i], row[part * QS + i], dot);
-      dot += __shfl_xor(dot, 1);
-      dot += __shfl_xor(dot, 2);
-      const float x = dot * p.scale_log2;
-      const float m_new = fmaxf(m_run, x);
-      const float alpha = exp2f(m_run - m_new);
-      const float pw = exp2f(x - m_new);
-      l_run = l_run * alpha + pw;
+      for (int i = 0; i < QS / 4; ++i) {
+        const float4 v = krow[i];
 #pragma unroll
-      for (int i = 0; i < VS; ++i) acc[i] = fmaf(acc[i], alpha, pw * row[part * VS + i]);
-      m_run = m_new;
+        for (int h = 0; h < MLA32_HPT; ++h) {
+          dot[h] = fmaf(qr[h][4 * i], v.x, dot[h]);
+          dot[h] = fmaf(qr[h][4 * i + 1], v.y, dot[h]);
+          dot[h] = fmaf(qr[h][4 * i + 2], v.z, dot[h]);
+          dot[h] = fmaf(qr[h][4 * i + 3], v.w, dot[h]);
+        }
+      }
+      // lazy rescaling: the running max (log2 units) moves only when a logit
+      // exceeds it by more than MLA_RESCALE_SLACK, so weights stay <= 2^8
+      // and the value update is one multiply-add
+      float pw[MLA32_HPT];
+      bool resc_any = false;
+      float alpha[MLA32_HPT];
+#pragma unroll
+      for (int h = 0; h < MLA32_HPT; ++h) {
+        const float x = row16_sum(dot[h]) * p.scale_log2;
+        const bool resc = x > m_run[h] + MLA_RESCALE_SLACK;
+        alpha[h] = resc ? exp2f(m_run[h] - x) : 1.0f;
+        if (resc) m_run[h] = x;
+        resc_any |= resc;
+        pw[h] = exp2f(x - m_run[h]);
+        l_run[h] = l_run[h] * alpha[h] + pw[h];
+      }
+      if (__any(resc_any)) {
+#pragma unroll
+        for (int h = 0; h < MLA32_HPT; ++h)
+#pragma unroll
+          for (int i = 0; i < VS; ++i) acc[h][i] *= alpha[h];
+      }
+      const float4* vrow = (const float4*)(tile[rr] + part * VS);
+#pragma unroll
+      for (int i = 0; i < VS / 4; ++i) {
+        const float4 v = vrow[i];
+#pragma unroll
+        for (int h = 0; h < MLA32_HPT; ++h) {
+          acc[h][4 * i] = fmaf(pw[h], v.x, acc[h][4 * i]);
+          acc[h][4 * i + 1] = fmaf(pw[h], v.y, acc[h][4 * i + 1]);
+          acc[h][4 * i + 2] = fmaf(pw[h], v.z, acc[h][4 * i + 2]);
+          acc[h][4 * i + 3] = fmaf(pw[h], v.w, acc[h][4 * i + 3]);
+        }
+      }
     }
   }
-  const int64_t qh = (int64_t)q * H + head;
-  if (p.nsplit == 1) {
-    const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
 #pragma unroll
-    for (int i = 0; i < VS; i += 4)
-      store_out4(p, layer, qh * DC + part * VS + i,
-                 f32x4{acc[i] * inv, acc[i + 1] * inv, acc[i + 2] * inv, acc[i + 3] * inv});
-    if (part == 0 && p.L.lse[layer])
-      p.L.lse[layer][qh] = l_run > 0.0f ? (m_run + log2f(l_run)) * LN2 : -INFINITY;
-  } else {
-    const int64_t slot = ((int64_t)split * p.n_layers + layer) * p.b.nq * H + qh;
-    const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
-    float* pa = (float*)p.part_o + slot * DC + part * VS;
+  for (int h = 0; h < MLA32_HPT; ++h) {
+    const int64_t qh = (int64_t)q * H + head0 + h;
+    const float inv = l_run[h] > 0.0f ? 1.0f / l_run[h] : 0.0f;
+    if (p.nsplit == 1) {
 #pragma unroll
-    for (int i = 0; i < VS; i += 4)
-      *(f32x4*)(pa + i) = f32x4{acc[i] * inv, acc[i + 1] * inv, acc[i + 2] * inv, acc[i + 3] * inv};
-    if (part == 0) {
-      p.part_ml[slot * 2 + 0] = l_run > 0.0f ? m_run : -INFINITY;
-      p.part_ml[slot * 2 + 1] = l_run;
+      for (int i = 0; i < VS; i += 4)
+        store_out4(p, layer, qh * DC + part * VS + i,
+                   f32x4{acc[h][i] * inv, acc[h][i + 1] * inv, acc[h][i + 2] * inv, acc[h][i + 3] * inv});
+      if (part == 0 && p.L.lse[layer])
+        p.L.lse[layer][qh] = l_run[h] > 0.0f ? (m_run[h] + log2f(l_run[h])) * LN2 : -INFINITY;
+    } else {
+      const int64_t slot = ((int64_t)split * p.n_layers + layer) * p.b.nq * H + qh;
+      float* pa = (float*)p.part_o + slot * DC + part * VS;
+#pragma unroll
+      for (int i = 0; i < VS; i += 4)
+        *(f32x4*)(pa + i) = f32x4{acc[h][i] * inv, acc[h][i + 1] * inv, acc[h][i + 2] * inv, acc[h][i + 3] * inv};
+      if (part == 0) {
+        p.part_ml[slot * 2 + 0] = l_run[h] > 0.0f ? m_run[h] : -INFINITY;
+        p.part_ml[slot * 2 + 1] = l_run[h];
+      }
     }
   }
 }
