@@ -393,39 +393,59 @@ __global__ __launch_bounds__(IDX_DEC_THREADS) void idx_decode_fp8(BatchDev b, co
 // decode, fp32 (VALU; small fp32 workloads)
 // ---------------------------------------------------------------------------
 constexpr int IDX_F32_THREADS = 256;
+constexpr int IDX_F32_HG = 4;                               // threads per key, 8 heads each
+constexpr int IDX_F32_KEYS = IDX_F32_THREADS / IDX_F32_HG;  // keys per workgroup
 
+// Thread (key, head group hg) computes sum over heads 8hg..8hg+7 of
+// w * ReLU(q_h . k), its eight dot products as independent chains over the
+// key row held in registers; the four head groups of a key (adjacent lanes)
+// add their sums with DPP lane moves.
 __global__ __launch_bounds__(IDX_F32_THREADS) void idx_decode_f32(
     BatchDev b, const float* __restrict__ qI, const float* __restrict__ w,
     const float* __restrict__ kI, float* __restrict__ scores, int64_t ld) {
-  __shared__ float qs[HI * DI];
+  constexpr int HPG = HI / IDX_F32_HG;
+  __shared__ __attribute__((aligned(16))) float qs[HI * DI];
   __shared__ float wsh[HI];
   const int q = blockIdx.y;
   const QueryRange r = query_range(b, q);
-  const int base = blockIdx.x * IDX_F32_THREADS;
+  const int base = blockIdx.x * IDX_F32_KEYS;
   if (base >= r.n) return;
-  for (int i = threadIdx.x; i < HI * DI; i += IDX_F32_THREADS) qs[i] = qI[(int64_t)q * HI * DI + i];
+  for (int i = threadIdx.x; i < HI * DI / 4; i += IDX_F32_THREADS)
+    ((float4*)qs)[i] = ((const float4*)(qI + (int64_t)q * HI * DI))[i];
   if (threadIdx.x < HI) wsh[threadIdx.x] = w[(int64_t)q * HI + threadIdx.x];
   __syncthreads();
-  const int key = base + threadIdx.x;
-  if (key >= r.n) return;
-  const float4* kp = (const float4*)(kI + (r.row0 + key) * DI);
+  const int hg = threadIdx.x & (IDX_F32_HG - 1);
+  const int key = base + threadIdx.x / IDX_F32_HG;
+  // keys past the end compute on the last row (every lane takes part in the
+  // lane moves) and store nothing
+  const float4* kp = (const float4*)(kI + (r.row0 + min(key, r.n - 1)) * DI);
   float4 kr[DI / 4];
 #pragma unroll
   for (int i = 0; i < DI / 4; ++i) kr[i] = kp[i];
-  float total = 0.0f;
-  for (int h = 0; h < HI; ++h) {
-    const float* qh = qs + h * DI;
-    float dot = 0.0f;
+  const float4* q4 = (const float4*)qs + hg * HPG * (DI / 4);
+  float dot[HPG];
 #pragma unroll
-    for (int i = 0; i < DI / 4; ++i) {
-      dot = fmaf(qh[4 * i + 0], kr[i].x, dot);
-      dot = fmaf(qh[4 * i + 1], kr[i].y, dot);
-      dot = fmaf(qh[4 * i + 2], kr[i].z, dot);
-      dot = fmaf(qh[4 * i + 3], kr[i].w, dot);
+  for (int h = 0; h < HPG; ++h) dot[h] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < DI / 4; ++i) {
+#pragma unroll
+    for (int h = 0; h < HPG; ++h) {
+      const float4 qv = q4[h * (DI / 4) + i];
+      dot[h] = fmaf(qv.x, kr[i].x, dot[h]);
+      dot[h] = fmaf(qv.y, kr[i].y, dot[h]);
+      dot[h] = fmaf(qv.z, kr[i].z, dot[h]);
+      dot[h] = fmaf(qv.w, kr[i].w, dot[h]);
     }
-    total = fmaf(wsh[h], relu(dot), total);
   }
-  scores[(int64_t)q * ld + key] = total;
+  float total = 0.0f;
+#pragma unroll
+  for (int h = 0; h < HPG; ++h) total = fmaf(wsh[hg * HPG + h], relu(dot[h]), total);
+  total += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(total), 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+  total += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(total), 0x4E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
+  if (hg == 0 && key < r.n) {
+    DSA_CHECK(key < ld, DBG_SCORE_COL);
+    scores[(int64_t)q * ld + key] = total;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -796,7 +816,7 @@ hipError_t launch_index_score(const BatchDev& b, int dtype, const void* qI, cons
   if (b.nq == 0) return hipSuccess;
   switch (index_kernel(dtype, b.nq, b.nseq)) {
     case IndexKernel::F32: {
-      dim3 grid((b.max_len + IDX_F32_THREADS - 1) / IDX_F32_THREADS, b.nq);
+      dim3 grid((b.max_len + IDX_F32_KEYS - 1) / IDX_F32_KEYS, b.nq);
       hipLaunchKernelGGL(idx_decode_f32, grid, dim3(IDX_F32_THREADS), 0, st, b, (const float*)qI, w,
                          (const float*)kI, scores, ld);
       break;
