@@ -136,6 +136,23 @@ def test_config4_decode_1m(B):
     _check_all(4, w, idx, outs, lses)
 
 
+DSA_MAX_LEN = 3728270   # include/dsa_mla.h: the longest sequence the library takes
+
+
+def test_decode_at_the_longest_sequence(B):
+    """One query over DSA_MAX_LEN positions, two layers: the MLA gathers
+    address a sequence's bf16 rows with 32-bit byte offsets, and this length
+    puts the last row's end 256 bytes below the 2^32 limit (3,728,270 x
+    1,152 B = 4,294,967,040 B).  With 2,048 of 3.7 million positions kept,
+    the selection reaches rows near the end.  Selection bit-exact, outputs and
+    log-sum-exp to the bf16 bar."""
+    w = wl.make_decode([DSA_MAX_LEN], "bf16", n_layers=2, seed=77, name="decode_b1_longest")
+    assert DSA_MAX_LEN * 1152 < (1 << 32) <= (DSA_MAX_LEN + 1) * 1152
+    idx, outs, lses, _ = _run(B, w)
+    _check_query("longest", w, 0, idx, outs, lses)
+    assert int(idx[0].max()) > DSA_MAX_LEN - 100000, "the selection should reach rows near the end"
+
+
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4])
 def test_config_fp8_indexer(B, cfg):
     """The same workloads with the indexer's query and keys stored in FP8
