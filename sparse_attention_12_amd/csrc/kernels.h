@@ -25,11 +25,12 @@ struct ZeroSpans {
 hipError_t launch_zero(const ZeroSpans& z, int nq, hipStream_t st);
 
 // Indexer scores of every query over its candidates (indexer.hip).  With
-// hist (HOST-chosen, may be NULL) and a decode batch of at most IDX_BAL_MAXQ
-// queries, the launch also adds each query's scores to hist[q][0, TK_BINS1)
-// by their top TK_BITS1 key bits (the top-k's first radix level), which
-// must be zero before the launch; *hist_done (may be NULL) says whether it
-// did.
+// hist (may be NULL) and a decode batch of at most IDX_BAL_MAXQ queries, the
+// launch also adds each query's scores to hist[q][0, TK_BINS1) by their top
+// TK_BITS1 key bits (the top-k's first radix level).  The top-k uses such a
+// histogram only if its bins sum to the row's length (true exactly when it
+// started from zero) and clears it after use; *hist_done (may be NULL) says
+// whether the launch counted.
 hipError_t launch_index_score(const BatchDev& b, int dtype, const void* qI, const float* w,
                               const void* kI, float* scores, int64_t ld, hipStream_t st,
                               uint32_t* hist = nullptr, bool* hist_done = nullptr);
@@ -40,7 +41,6 @@ hipError_t launch_index_score(const BatchDev& b, int dtype, const void* qI, cons
 // candidate count, which holds exactly when it started from zero), used in
 // place of a counting pass when it checks out, and cleared for the next call
 // either way.
-ZeroSpan topk_zero_span(void* ws, int nq, int max_len);
 hipError_t launch_topk(const BatchDev& b, const float* scores, int64_t ld, int k, int32_t* idx,
                        int32_t* count, void* ws, size_t ws_bytes, hipStream_t st, uint32_t* hist_pre = nullptr);
 

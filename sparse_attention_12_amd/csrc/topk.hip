@@ -727,11 +727,6 @@ static SplitWs split_ws(int nq, int max_len, char* base) {
   return ws;
 }
 
-ZeroSpan topk_zero_span(void* wsp, int nq, int max_len) {
-  if (wsp == nullptr || nq <= 0 || max_len <= 0 || !topk_use_split(nq, max_len)) return ZeroSpan{nullptr, 0, 0};
-  return ZeroSpan{split_ws(nq, max_len, (char*)wsp).hist, TK_BINS1, TK_BINS1};
-}
-
 hipError_t launch_topk(const BatchDev& b, const float* scores, int64_t ld, int k, int32_t* idx,
                        int32_t* count, void* wsp, size_t ws_bytes, hipStream_t st, uint32_t* hist_pre) {
   if (b.nq == 0) return hipSuccess;
