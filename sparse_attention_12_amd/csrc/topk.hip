@@ -666,36 +666,54 @@ __global__ __launch_bounds__(TK_THREADS) void topk_final_kernel(BatchDev b, cons
     if (tid < nch) sm.off[tid] = o;
     __syncthreads();
     const int64_t lq = (int64_t)q * ws.nchunk * TK_CHUNK;
-    // thread t copies the run of entries [t*R, t*R + R): one search for the
-    // chunk of its first entry, then a forward walk over the offsets
+    // entry e = tid + i * TK_THREADS: the lanes of a wave copy consecutive
+    // entries, so each of its loads reads one or two cache lines, and every
+    // load of a thread is issued before the first is waited for.  An entry's
+    // chunk (the last chunk whose offset is <= e) comes from a binary search
+    // over the offsets; a thread's searches step together, and the lanes of a
+    // wave, holding neighbouring entries, mostly read the same offsets.
+    // Entries past the total load entry 0 of chunk 0 and are not stored.
     constexpr int PER = (TK_FCAP + TK_THREADS - 1) / TK_THREADS;
-    const uint32_t R = (total + TK_THREADS - 1) / TK_THREADS;
-    const uint32_t e0 = (uint32_t)tid * R;
-    int c = 0;
-    {
-      int hi = nch - 1;  // last chunk whose offset is <= e0
-      while (c < hi) {
-        const int mid = (c + hi + 1) >> 1;
-        if (sm.off[mid] <= e0) c = mid;
-        else hi = mid - 1;
+    int lo[PER], hi[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      lo[i] = 0;
+      hi[i] = nch - 1;
+    }
+    // (branch-free: with lo == hi the step reads off[lo] <= e and keeps lo,
+    // so every search takes ceil(log2(nch)) steps and each step's reads go
+    // out together)
+    for (int it = 0; (1 << it) < nch; ++it) {
+      uint32_t v[PER];
+      int mid[PER];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        mid[i] = (lo[i] + hi[i] + 1) >> 1;
+        v[i] = sm.off[mid[i]];
+      }
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const bool le = v[i] <= (uint32_t)(tid + i * TK_THREADS);
+        lo[i] = le ? mid[i] : lo[i];
+        hi[i] = le ? hi[i] : mid[i] - 1;
       }
     }
+    uint32_t oc[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) oc[i] = sm.off[lo[i]];
     uint32_t kv[PER];
     int32_t pv[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const uint32_t e = e0 + i;
-      if ((uint32_t)i < R && e < total) {
-        while (c + 1 < nch && sm.off[c + 1] <= e) ++c;
-        const int64_t src = lq + (int64_t)c * TK_CHUNK + (e - sm.off[c]);
-        kv[i] = ws.lkey[src];
-        pv[i] = ws.lpos[src];
-      }
+      const uint32_t e = (uint32_t)(tid + i * TK_THREADS);
+      const int64_t src = e < total ? lq + (int64_t)lo[i] * TK_CHUNK + (e - oc[i]) : lq;
+      kv[i] = ws.lkey[src];
+      pv[i] = ws.lpos[src];
     }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const uint32_t e = e0 + i;
-      if ((uint32_t)i < R && e < total) {
+      const uint32_t e = (uint32_t)(tid + i * TK_THREADS);
+      if (e < total) {
         sm.list.ukey[e] = kv[i];
         sm.list.pos[e] = pv[i];
       }
