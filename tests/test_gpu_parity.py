@@ -314,6 +314,28 @@ def test_topk_engineered_rows(B, k, long_row):
         assert np.array_equal(idx[i], ref), f"row {i}: selection differs"
 
 
+def test_topk_split_list_capacity(B):
+    """Rows longer than 49,152 scores take the split path, whose final
+    workgroup copies the threshold bin's candidates into LDS when they number
+    at most 12,288 (the copy's largest case: 12 entries per thread, consecutive
+    lanes on consecutive entries) and streams the row otherwise.  Threshold
+    bins of exactly 12,287, 12,288 and 12,289 tied keys, spread over every
+    chunk of a 70,000-score row, sit on either side of that capacity; the
+    other scores lie below them."""
+    rng = np.random.default_rng(57)
+    n = 70000
+    rows = []
+    for j, tied in enumerate((12287, 12288, 12289)):
+        row = rng.random(n).astype(np.float32)  # [0, 1): other first-level bins
+        row[rng.choice(n, tied, replace=False)] = np.float32(2.0 + j)
+        rows.append(row)
+    idx, cnt = _topk_gpu(B, rows, 2048)
+    for i, r in enumerate(rows):
+        ref, m = oracle.topk(r.astype(np.float64), 2048)
+        assert cnt[i] == m, f"row {i}"
+        assert np.array_equal(idx[i], ref), f"row {i}: selection differs"
+
+
 def test_topk_many_rows(B):
     """Batches of many rows take the one-workgroup-per-row path."""
     rng = np.random.default_rng(31)
