@@ -632,6 +632,68 @@ struct FinalShared {
   ListShared list;
 };
 
+// Copies the concatenated chunk lists (offsets in off[0..nch), total
+// entries) into the LDS list.  Entry e = tid + i * TK_THREADS for i < PER,
+// so PER * TK_THREADS must cover total; the caller takes an instance with
+// half the rounds when it does, so short lists issue fewer loads and
+// searches without a branch per round.
+template <int PER>
+__device__ __forceinline__ void copy_lists(ListShared& lst, const uint32_t* off, int nch, uint32_t total,
+                                           const SplitWs& ws, int64_t lq) {
+  const int tid = threadIdx.x;
+  // entry e = tid + i * TK_THREADS: the lanes of a wave copy consecutive
+  // entries, so each of its loads reads one or two cache lines, and every
+  // load of a thread is issued before the first is waited for.  An entry's
+  // chunk (the last chunk whose offset is <= e) comes from a binary search
+  // over the offsets; a thread's searches step together, and the lanes of a
+  // wave, holding neighbouring entries, mostly read the same offsets.
+  // Entries past the total load entry 0 of chunk 0 and are not stored.
+  int lo[PER], hi[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    lo[i] = 0;
+    hi[i] = nch - 1;
+  }
+  // (branch-free: with lo == hi the step reads off[lo] <= e and keeps lo,
+  // so every search takes ceil(log2(nch)) steps and each step's reads go
+  // out together)
+  for (int it = 0; (1 << it) < nch; ++it) {
+    uint32_t v[PER];
+    int mid[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      mid[i] = (lo[i] + hi[i] + 1) >> 1;
+      v[i] = off[mid[i]];
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const bool le = v[i] <= (uint32_t)(tid + i * TK_THREADS);
+      lo[i] = le ? mid[i] : lo[i];
+      hi[i] = le ? hi[i] : mid[i] - 1;
+    }
+  }
+  uint32_t oc[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) oc[i] = off[lo[i]];
+  uint32_t kv[PER];
+  int32_t pv[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const uint32_t e = (uint32_t)(tid + i * TK_THREADS);
+    const int64_t src = e < total ? lq + (int64_t)lo[i] * TK_CHUNK + (e - oc[i]) : lq;
+    kv[i] = ws.lkey[src];
+    pv[i] = ws.lpos[src];
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const uint32_t e = (uint32_t)(tid + i * TK_THREADS);
+    if (e < total) {
+      lst.ukey[e] = kv[i];
+      lst.pos[e] = pv[i];
+    }
+  }
+}
+
 __global__ __launch_bounds__(TK_THREADS) void topk_final_kernel(BatchDev b, const float* __restrict__ scores,
                                                                 int64_t ld, int k, int32_t* __restrict__ idx,
                                                                 int32_t* __restrict__ count, SplitWs ws) {
@@ -666,58 +728,11 @@ __global__ __launch_bounds__(TK_THREADS) void topk_final_kernel(BatchDev b, cons
     if (tid < nch) sm.off[tid] = o;
     __syncthreads();
     const int64_t lq = (int64_t)q * ws.nchunk * TK_CHUNK;
-    // entry e = tid + i * TK_THREADS: the lanes of a wave copy consecutive
-    // entries, so each of its loads reads one or two cache lines, and every
-    // load of a thread is issued before the first is waited for.  An entry's
-    // chunk (the last chunk whose offset is <= e) comes from a binary search
-    // over the offsets; a thread's searches step together, and the lanes of a
-    // wave, holding neighbouring entries, mostly read the same offsets.
-    // Entries past the total load entry 0 of chunk 0 and are not stored.
-    constexpr int PER = (TK_FCAP + TK_THREADS - 1) / TK_THREADS;
-    int lo[PER], hi[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      lo[i] = 0;
-      hi[i] = nch - 1;
-    }
-    // (branch-free: with lo == hi the step reads off[lo] <= e and keeps lo,
-    // so every search takes ceil(log2(nch)) steps and each step's reads go
-    // out together)
-    for (int it = 0; (1 << it) < nch; ++it) {
-      uint32_t v[PER];
-      int mid[PER];
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        mid[i] = (lo[i] + hi[i] + 1) >> 1;
-        v[i] = sm.off[mid[i]];
-      }
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const bool le = v[i] <= (uint32_t)(tid + i * TK_THREADS);
-        lo[i] = le ? mid[i] : lo[i];
-        hi[i] = le ? hi[i] : mid[i] - 1;
-      }
-    }
-    uint32_t oc[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) oc[i] = sm.off[lo[i]];
-    uint32_t kv[PER];
-    int32_t pv[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const uint32_t e = (uint32_t)(tid + i * TK_THREADS);
-      const int64_t src = e < total ? lq + (int64_t)lo[i] * TK_CHUNK + (e - oc[i]) : lq;
-      kv[i] = ws.lkey[src];
-      pv[i] = ws.lpos[src];
-    }
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const uint32_t e = (uint32_t)(tid + i * TK_THREADS);
-      if (e < total) {
-        sm.list.ukey[e] = kv[i];
-        sm.list.pos[e] = pv[i];
-      }
-    }
+    constexpr int PER_MAX = (TK_FCAP + TK_THREADS - 1) / TK_THREADS;
+    if (total <= (uint32_t)(PER_MAX / 2 * TK_THREADS))
+      copy_lists<PER_MAX / 2>(sm.list, sm.off, nch, total, ws, lq);
+    else
+      copy_lists<PER_MAX>(sm.list, sm.off, nch, total, ws, lq);
     __syncthreads();
     finalize_list(sm.list, (int)total, (uint32_t)d1, need, k, out);
   } else {
